@@ -1,1 +1,213 @@
-"""MI355X-native W4A16 group-quantized GEMM/GEMV (binding package)."""
+"""MI355X-native W4A16 group-quantized GEMM/GEMV.
+
+Thin torch binding over the C ABI of ``libw4a16.so`` (include/w4a16.h):
+argument marshalling only; every step runs in the library's HIP kernels on
+the caller's current torch stream.  There is no CPU fallback: calling an op
+without the built library or without a GPU raises.
+
+    pw = repack(qweight, scales, zeros, K, N, group)   # one time, on the GPU
+    y = gemm(A, pw)                                     # fp16 [M][N]
+    y = gemm(A, pw, epilogue="bias_relu", bias=b)
+    y = gemm(A, pw, gamma=g, eps=1e-6)                  # RMSNorm prologue
+    y = gemm_gate_up(A, pw_gate, pw_up)                 # silu(A.Wg) * (A.Wu)
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from . import _lib
+
+__all__ = [
+    "PackedWeight", "repack", "gemm", "gemm_gate_up", "packed_bytes",
+    "workspace_bytes", "layout_version", "add_bias", "relu", "rmsnorm",
+    "probe_read", "probe_copy", "Workspace",
+]
+
+
+def _stream():
+    return ctypes_stream(torch.cuda.current_stream())
+
+
+def ctypes_stream(s: torch.cuda.Stream):
+    return s.cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _need_gpu(t: torch.Tensor, name: str, dtype=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+@dataclass
+class PackedWeight:
+    """A repacked int4 weight (layout version 1) and its shape."""
+    data: torch.Tensor  # uint8, w4a16_packed_bytes long
+    K: int
+    N: int
+    group: int
+    scale_dtype: int    # _lib.SCALE_F16 / SCALE_F32
+    has_zp: bool
+
+
+def layout_version() -> int:
+    return _lib.lib().w4a16_layout_version()
+
+
+def packed_bytes(K: int, N: int, group: int, scale_dtype: int, has_zp: bool) -> int:
+    return _lib.lib().w4a16_packed_bytes(K, N, group, scale_dtype, int(has_zp))
+
+
+def workspace_bytes(M: int, K: int, N: int, group: int, gate_up: bool = False) -> int:
+    return _lib.lib().w4a16_workspace_bytes(M, K, N, group, int(gate_up))
+
+
+class Workspace:
+    """Zero-filled device workspace reused across calls on one device.
+
+    The library leaves its arrival counters at zero after every call, so the
+    buffer is zero-filled only when it is (re)allocated.  Calls that share a
+    workspace must be ordered on one stream.
+    """
+
+    def __init__(self):
+        self._buf = {}
+
+    def get(self, nbytes: int, device) -> Optional[torch.Tensor]:
+        if nbytes == 0:
+            return None
+        key = torch.device(device)
+        buf = self._buf.get(key)
+        if buf is None or buf.numel() < nbytes:
+            buf = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=key)
+            self._buf[key] = buf
+        return buf
+
+
+_default_ws = Workspace()
+
+
+def repack(qweight: torch.Tensor, scales: torch.Tensor, zeros: Optional[torch.Tensor],
+           K: int, N: int, group: int) -> PackedWeight:
+    """Repack canonical weights (u8 [N][K/2], fp16/fp32 scales [N][G],
+    u8 zeros [N][ceil(G/2)] or None) into the packed layout, on the GPU."""
+    _need_gpu(qweight, "qweight", torch.uint8)
+    _need_gpu(scales, "scales")
+    if scales.dtype == torch.float16:
+        sdt = _lib.SCALE_F16
+    elif scales.dtype == torch.float32:
+        sdt = _lib.SCALE_F32
+    else:
+        raise ValueError("scales must be float16 or float32")
+    if zeros is not None:
+        _need_gpu(zeros, "zeros", torch.uint8)
+    nbytes = packed_bytes(K, N, group, sdt, zeros is not None)
+    if nbytes == 0:
+        _lib.check(_lib.ERR_SHAPE, "w4a16_packed_bytes")
+    out = torch.empty(nbytes, dtype=torch.uint8, device=qweight.device)
+    st = _lib.lib().w4a16_repack(_ptr(qweight), _ptr(scales), _ptr(zeros), K, N, group,
+                                 sdt, _ptr(out), _stream())
+    _lib.check(st, "w4a16_repack")
+    return PackedWeight(out, K, N, group, sdt, zeros is not None)
+
+
+def gemm(A: torch.Tensor, w: PackedWeight, *, epilogue: str = "none",
+         bias: Optional[torch.Tensor] = None, gamma: Optional[torch.Tensor] = None,
+         eps: float = 1e-6, out: Optional[torch.Tensor] = None,
+         workspace: Optional[Workspace] = None) -> torch.Tensor:
+    """fp16 [M][N] = epilogue(X . dequant(W)), X = A or RMSNorm(A; gamma, eps)."""
+    _need_gpu(A, "A", torch.float16)
+    M, K = A.shape
+    if K != w.K:
+        raise ValueError(f"A has K={K}, weight has K={w.K}")
+    for t, n in ((bias, "bias"), (gamma, "gamma")):
+        if t is not None:
+            _need_gpu(t, n, torch.float16)
+    if out is None:
+        out = torch.empty((M, w.N), dtype=torch.float16, device=A.device)
+    _need_gpu(out, "out", torch.float16)
+    ws_n = workspace_bytes(M, K, w.N, w.group, False)
+    ws = (workspace or _default_ws).get(ws_n, A.device)
+    st = _lib.lib().w4a16_gemm(_ptr(A), M, K, w.N, w.group, w.scale_dtype, int(w.has_zp),
+                               _ptr(w.data), _lib.EPI[epilogue], _ptr(bias), _ptr(gamma),
+                               float(eps), _ptr(out), _ptr(ws), ws_n, _stream())
+    _lib.check(st, "w4a16_gemm")
+    return out
+
+
+def gemm_gate_up(A: torch.Tensor, w_gate: PackedWeight, w_up: PackedWeight, *,
+                 gamma: Optional[torch.Tensor] = None, eps: float = 1e-6,
+                 out: Optional[torch.Tensor] = None,
+                 workspace: Optional[Workspace] = None) -> torch.Tensor:
+    """fp16 [M][N] = silu(X . Wg) * (X . Wu)."""
+    _need_gpu(A, "A", torch.float16)
+    M, K = A.shape
+    for w in (w_gate, w_up):
+        if (w.K, w.N, w.group, w.scale_dtype, w.has_zp) != (
+                w_gate.K, w_gate.N, w_gate.group, w_gate.scale_dtype, w_gate.has_zp):
+            raise ValueError("gate and up weights must share K, N, group, scale dtype, zp")
+    if K != w_gate.K:
+        raise ValueError(f"A has K={K}, weights have K={w_gate.K}")
+    if gamma is not None:
+        _need_gpu(gamma, "gamma", torch.float16)
+    if out is None:
+        out = torch.empty((M, w_gate.N), dtype=torch.float16, device=A.device)
+    _need_gpu(out, "out", torch.float16)
+    ws_n = workspace_bytes(M, K, w_gate.N, w_gate.group, True)
+    ws = (workspace or _default_ws).get(ws_n, A.device)
+    st = _lib.lib().w4a16_gemm_gate_up(
+        _ptr(A), M, K, w_gate.N, w_gate.group, w_gate.scale_dtype, int(w_gate.has_zp),
+        _ptr(w_gate.data), _ptr(w_up.data), _ptr(gamma), float(eps), _ptr(out),
+        _ptr(ws), ws_n, _stream())
+    _lib.check(st, "w4a16_gemm_gate_up")
+    return out
+
+
+def add_bias(x: torch.Tensor, bias: torch.Tensor, out: Optional[torch.Tensor] = None):
+    """Unfused-chain pass: fp16(x + bias)."""
+    _need_gpu(x, "x", torch.float16)
+    M, N = x.shape
+    out = torch.empty_like(x) if out is None else out
+    _lib.check(_lib.lib().w4a16_add_bias(_ptr(x), _ptr(bias), M, N, _ptr(out), _stream()),
+               "w4a16_add_bias")
+    return out
+
+
+def relu(x: torch.Tensor, out: Optional[torch.Tensor] = None):
+    """Unfused-chain pass: max(x, 0)."""
+    _need_gpu(x, "x", torch.float16)
+    M, N = x.shape
+    out = torch.empty_like(x) if out is None else out
+    _lib.check(_lib.lib().w4a16_relu(_ptr(x), M, N, _ptr(out), _stream()), "w4a16_relu")
+    return out
+
+
+def rmsnorm(A: torch.Tensor, gamma: torch.Tensor, eps: float = 1e-6,
+            out: Optional[torch.Tensor] = None):
+    """Unfused-chain pass: fp16(A * gamma / sqrt(mean(A^2) + eps))."""
+    _need_gpu(A, "A", torch.float16)
+    M, K = A.shape
+    out = torch.empty_like(A) if out is None else out
+    _lib.check(_lib.lib().w4a16_rmsnorm(_ptr(A), _ptr(gamma), float(eps), M, K, _ptr(out),
+                                        _stream()), "w4a16_rmsnorm")
+    return out
+
+
+def probe_read(buf: torch.Tensor, sink: torch.Tensor) -> None:
+    _lib.check(_lib.lib().w4a16_probe_read(_ptr(buf), buf.numel() * buf.element_size(),
+                                           _ptr(sink), _stream()), "w4a16_probe_read")
+
+
+def probe_copy(src: torch.Tensor, dst: torch.Tensor) -> None:
+    _lib.check(_lib.lib().w4a16_probe_copy(_ptr(src), _ptr(dst),
+                                           src.numel() * src.element_size(), _stream()),
+               "w4a16_probe_copy")

@@ -1,0 +1,233 @@
+// C ABI of libw4a16.so (declared in include/w4a16.h): host-side argument
+// validation, launch planning and the kernel launches.  Validation always
+// runs before any HIP call, so every error status can be produced without a
+// GPU.
+#include "../../include/w4a16.h"
+#include "common.h"
+
+using namespace w4a16;
+
+namespace {
+
+constexpr int kMaxDim = 1 << 24;  // keeps every index product inside size_t math
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool group_ok(int g) { return g == 16 || g == 32 || g == 64 || g == 128; }
+
+int scale_bytes_of(int dtype) {
+  return dtype == W4A16_SCALE_F16 ? 2 : (dtype == W4A16_SCALE_F32 ? 4 : 0);
+}
+
+int check_kn(int K, int N, int group) {
+  if (K <= 0 || N <= 0 || K % kTileK != 0 || N % kTileN != 0 || K > kMaxDim ||
+      N > kMaxDim)
+    return W4A16_ERR_SHAPE;
+  if (!group_ok(group)) return W4A16_ERR_GROUP;
+  return W4A16_OK;
+}
+
+int check_gemm(const void *A, int M, int K, int N, int group, int scale_dtype,
+               const void *const *packed, int npacked, const void *out) {
+  if (A == nullptr || out == nullptr) return W4A16_ERR_NULL;
+  for (int i = 0; i < npacked; ++i)
+    if (packed[i] == nullptr) return W4A16_ERR_NULL;
+  if (M < 1 || M > kMaxDim) return W4A16_ERR_SHAPE;
+  const int st = check_kn(K, N, group);
+  if (st != W4A16_OK) return st;
+  if (scale_bytes_of(scale_dtype) == 0) return W4A16_ERR_DTYPE;
+  if (!aligned16(A) || !aligned16(out)) return W4A16_ERR_ALIGN;
+  for (int i = 0; i < npacked; ++i)
+    if (!aligned16(packed[i])) return W4A16_ERR_ALIGN;
+  return W4A16_OK;
+}
+
+int check_workspace(const Plan &pl, const void *ws, size_t ws_bytes) {
+  if (pl.ws_total == 0) return W4A16_OK;
+  if (ws == nullptr) return W4A16_ERR_WORKSPACE;
+  if (ws_bytes < pl.ws_total) return W4A16_ERR_WORKSPACE;
+  if (!aligned16(ws)) return W4A16_ERR_ALIGN;
+  return W4A16_OK;
+}
+
+void fill_packed(GemmArgs &a, int slot, const void *packed, int K, int N,
+                 int group, int sbytes, bool has_zp) {
+  const PackedOffsets off = packed_offsets(K, N, group, sbytes, has_zp);
+  const uint8_t *base = static_cast<const uint8_t *>(packed);
+  a.w[slot] = base;
+  a.scales[slot] = base + off.scales;
+  a.zeros[slot] = has_zp ? base + off.zeros : nullptr;
+}
+
+void fill_workspace(GemmArgs &a, const Plan &pl, void *ws) {
+  uint8_t *b = static_cast<uint8_t *>(ws);
+  a.split = pl.split;
+  a.cps = pl.cps;
+  a.ws_part = pl.ws_total ? reinterpret_cast<float *>(b + pl.ws_part_off) : nullptr;
+  a.ws_rms = pl.ws_total ? reinterpret_cast<float *>(b + pl.ws_rms_off) : nullptr;
+  a.ws_cnt = pl.ws_total ? reinterpret_cast<uint32_t *>(b + pl.ws_cnt_off) : nullptr;
+}
+
+int launched(hipError_t e) { return e == hipSuccess ? W4A16_OK : W4A16_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+size_t w4a16_packed_bytes(int K, int N, int group, int scale_dtype, int has_zp) {
+  if (check_kn(K, N, group) != W4A16_OK) return 0;
+  const int sb = scale_bytes_of(scale_dtype);
+  if (sb == 0) return 0;
+  return packed_offsets(K, N, group, sb, has_zp != 0).total;
+}
+
+int w4a16_repack(const uint8_t *qweight, const void *scales,
+                 const uint8_t *zeros, int K, int N, int group,
+                 int scale_dtype, void *packed, w4a16_stream stream) {
+  if (qweight == nullptr || scales == nullptr || packed == nullptr)
+    return W4A16_ERR_NULL;
+  const int st = check_kn(K, N, group);
+  if (st != W4A16_OK) return st;
+  const int sb = scale_bytes_of(scale_dtype);
+  if (sb == 0) return W4A16_ERR_DTYPE;
+  if (!aligned16(qweight) || !aligned16(scales) || !aligned16(packed) ||
+      (zeros != nullptr && !aligned16(zeros)))
+    return W4A16_ERR_ALIGN;
+  return launched(launch_repack(qweight, scales, zeros, K, N, group, sb,
+                                static_cast<uint8_t *>(packed),
+                                static_cast<hipStream_t>(stream)));
+}
+
+size_t w4a16_workspace_bytes(int M, int K, int N, int group, int gate_up) {
+  if (M < 1 || M > kMaxDim || check_kn(K, N, group) != W4A16_OK) return 0;
+  return make_plan(M, K, N, group, gate_up != 0).ws_total;
+}
+
+int w4a16_gemm(const void *A, int M, int K, int N, int group, int scale_dtype,
+               int has_zp, const void *packed, int epilogue, const void *bias,
+               const void *rms_gamma, float rms_eps, void *out,
+               void *workspace, size_t workspace_bytes, w4a16_stream stream) {
+  const void *pk[1] = {packed};
+  int st = check_gemm(A, M, K, N, group, scale_dtype, pk, 1, out);
+  if (st != W4A16_OK) return st;
+  if (epilogue != W4A16_EPI_NONE && epilogue != W4A16_EPI_BIAS &&
+      epilogue != W4A16_EPI_BIAS_RELU)
+    return W4A16_ERR_EPILOGUE;
+  if (epilogue != W4A16_EPI_NONE && bias == nullptr) return W4A16_ERR_EPILOGUE;
+  if ((bias != nullptr && !aligned16(bias)) ||
+      (rms_gamma != nullptr && !aligned16(rms_gamma)))
+    return W4A16_ERR_ALIGN;
+  const Plan pl = make_plan(M, K, N, group, false);
+  st = check_workspace(pl, workspace, workspace_bytes);
+  if (st != W4A16_OK) return st;
+
+  const int sb = scale_bytes_of(scale_dtype);
+  GemmArgs a{};
+  a.A = static_cast<const f16 *>(A);
+  a.M = M;
+  a.K = K;
+  a.N = N;
+  fill_packed(a, 0, packed, K, N, group, sb, has_zp != 0);
+  a.has_zp = has_zp != 0;
+  a.epilogue = epilogue;
+  a.bias = static_cast<const f16 *>(bias);
+  a.gamma = static_cast<const f16 *>(rms_gamma);
+  a.eps = rms_eps;
+  a.out = static_cast<f16 *>(out);
+  fill_workspace(a, pl, workspace);
+  return launched(launch_gemm(a, pl, group, sb == 4, false,
+                              static_cast<hipStream_t>(stream)));
+}
+
+int w4a16_gemm_gate_up(const void *A, int M, int K, int N, int group,
+                       int scale_dtype, int has_zp, const void *packed_gate,
+                       const void *packed_up, const void *rms_gamma,
+                       float rms_eps, void *out, void *workspace,
+                       size_t workspace_bytes, w4a16_stream stream) {
+  const void *pk[2] = {packed_gate, packed_up};
+  int st = check_gemm(A, M, K, N, group, scale_dtype, pk, 2, out);
+  if (st != W4A16_OK) return st;
+  if (rms_gamma != nullptr && !aligned16(rms_gamma)) return W4A16_ERR_ALIGN;
+  const Plan pl = make_plan(M, K, N, group, true);
+  st = check_workspace(pl, workspace, workspace_bytes);
+  if (st != W4A16_OK) return st;
+
+  const int sb = scale_bytes_of(scale_dtype);
+  GemmArgs a{};
+  a.A = static_cast<const f16 *>(A);
+  a.M = M;
+  a.K = K;
+  a.N = N;
+  fill_packed(a, 0, packed_gate, K, N, group, sb, has_zp != 0);
+  fill_packed(a, 1, packed_up, K, N, group, sb, has_zp != 0);
+  a.has_zp = has_zp != 0;
+  a.epilogue = W4A16_EPI_NONE;
+  a.gamma = static_cast<const f16 *>(rms_gamma);
+  a.eps = rms_eps;
+  a.out = static_cast<f16 *>(out);
+  fill_workspace(a, pl, workspace);
+  return launched(launch_gemm(a, pl, group, sb == 4, true,
+                              static_cast<hipStream_t>(stream)));
+}
+
+const char *w4a16_status_string(int status) {
+  switch (status) {
+    case W4A16_OK: return "ok";
+    case W4A16_ERR_NULL: return "a required pointer is NULL";
+    case W4A16_ERR_SHAPE: return "bad shape (need M >= 1, K % 128 == 0, N % 16 == 0)";
+    case W4A16_ERR_GROUP: return "group must be 16, 32, 64 or 128";
+    case W4A16_ERR_DTYPE: return "unknown scale dtype";
+    case W4A16_ERR_EPILOGUE: return "unknown epilogue, or bias missing for a bias epilogue";
+    case W4A16_ERR_WORKSPACE: return "workspace missing or too small";
+    case W4A16_ERR_ALIGN: return "device pointer not 16-byte aligned";
+    case W4A16_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int w4a16_layout_version(void) { return W4A16_LAYOUT_VERSION; }
+
+int w4a16_add_bias(const void *in, const void *bias, int M, int N, void *out,
+                   w4a16_stream stream) {
+  if (in == nullptr || bias == nullptr || out == nullptr) return W4A16_ERR_NULL;
+  if (M < 1 || N < 1 || N % 16 != 0 || M > kMaxDim || N > kMaxDim) return W4A16_ERR_SHAPE;
+  if (!aligned16(in) || !aligned16(bias) || !aligned16(out)) return W4A16_ERR_ALIGN;
+  return launched(launch_add_bias(static_cast<const f16 *>(in), static_cast<const f16 *>(bias),
+                                  M, N, static_cast<f16 *>(out),
+                                  static_cast<hipStream_t>(stream)));
+}
+
+int w4a16_relu(const void *in, int M, int N, void *out, w4a16_stream stream) {
+  if (in == nullptr || out == nullptr) return W4A16_ERR_NULL;
+  if (M < 1 || N < 1 || N % 16 != 0 || M > kMaxDim || N > kMaxDim) return W4A16_ERR_SHAPE;
+  if (!aligned16(in) || !aligned16(out)) return W4A16_ERR_ALIGN;
+  return launched(launch_relu(static_cast<const f16 *>(in), M, N, static_cast<f16 *>(out),
+                              static_cast<hipStream_t>(stream)));
+}
+
+int w4a16_rmsnorm(const void *A, const void *gamma, float eps, int M, int K,
+                  void *out, w4a16_stream stream) {
+  if (A == nullptr || gamma == nullptr || out == nullptr) return W4A16_ERR_NULL;
+  if (M < 1 || K < 1 || K % 128 != 0 || M > kMaxDim || K > kMaxDim) return W4A16_ERR_SHAPE;
+  if (!aligned16(A) || !aligned16(gamma) || !aligned16(out)) return W4A16_ERR_ALIGN;
+  return launched(launch_rmsnorm(static_cast<const f16 *>(A), static_cast<const f16 *>(gamma),
+                                 eps, M, K, static_cast<f16 *>(out),
+                                 static_cast<hipStream_t>(stream)));
+}
+
+int w4a16_probe_read(const void *buf, size_t bytes, void *sink, w4a16_stream stream) {
+  if (buf == nullptr || sink == nullptr) return W4A16_ERR_NULL;
+  if (bytes == 0 || bytes % 16 != 0) return W4A16_ERR_SHAPE;
+  if (!aligned16(buf) || !aligned16(sink)) return W4A16_ERR_ALIGN;
+  return launched(launch_probe_read(buf, bytes, static_cast<uint32_t *>(sink),
+                                    static_cast<hipStream_t>(stream)));
+}
+
+int w4a16_probe_copy(const void *src, void *dst, size_t bytes, w4a16_stream stream) {
+  if (src == nullptr || dst == nullptr) return W4A16_ERR_NULL;
+  if (bytes == 0 || bytes % 16 != 0) return W4A16_ERR_SHAPE;
+  if (!aligned16(src) || !aligned16(dst)) return W4A16_ERR_ALIGN;
+  return launched(launch_probe_copy(src, dst, bytes, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

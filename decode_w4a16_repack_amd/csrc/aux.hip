@@ -1,0 +1,160 @@
+// Measurement aids: the separate passes of the unfused chain, and streaming
+// probes for the achievable HBM rate.
+//
+// The "Fusion benchmark" page measures a fused kernel against the unfused
+// chain at the same shape: matmul, then a bias pass, then a ReLU pass, each
+// reading and writing memory.  These kernels are those passes (and the
+// RMSNorm pass that stages a normalized activation before a plain GEMM).  They
+// are deliberately plain one-pass kernels: vectorized 16-byte accesses, one
+// read and one write per element.
+#include "common.h"
+
+namespace w4a16 {
+
+namespace {
+
+__global__ void __launch_bounds__(256)
+add_bias_kernel(const f16 *__restrict__ in, const f16 *__restrict__ bias,
+                int N, size_t vecs, f16 *__restrict__ out) {
+  for (size_t v = (size_t)blockIdx.x * blockDim.x + threadIdx.x; v < vecs;
+       v += (size_t)gridDim.x * blockDim.x) {
+    const size_t e = v * 8;
+    const int n = (int)(e % (size_t)N);
+    const f16x8 x = *reinterpret_cast<const f16x8 *>(in + e);
+    const f16x8 b = *reinterpret_cast<const f16x8 *>(bias + n);
+    f16x8 y;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] = (f16)((float)x[i] + (float)b[i]);
+    *reinterpret_cast<f16x8 *>(out + e) = y;
+  }
+}
+
+__global__ void __launch_bounds__(256)
+relu_kernel(const f16 *__restrict__ in, size_t vecs, f16 *__restrict__ out) {
+  for (size_t v = (size_t)blockIdx.x * blockDim.x + threadIdx.x; v < vecs;
+       v += (size_t)gridDim.x * blockDim.x) {
+    const f16x8 x = *reinterpret_cast<const f16x8 *>(in + v * 8);
+    f16x8 y;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] = x[i] > (f16)0.0f ? x[i] : (f16)0.0f;
+    *reinterpret_cast<f16x8 *>(out + v * 8) = y;
+  }
+}
+
+// One workgroup per row: sum of squares with a fixed-order tree, then
+// out = fp16(a * gamma / sqrt(mean + eps)).
+__global__ void __launch_bounds__(256)
+rmsnorm_kernel(const f16 *__restrict__ A, const f16 *__restrict__ gamma,
+               float eps, int K, f16 *__restrict__ out) {
+  __shared__ float part[256];
+  const int m = blockIdx.x;
+  const f16 *a = A + (size_t)m * K;
+  float ss = 0.f;
+  for (int k = threadIdx.x * 8; k < K; k += 256 * 8) {
+    const f16x8 x = *reinterpret_cast<const f16x8 *>(a + k);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ss += (float)x[i] * (float)x[i];
+  }
+  part[threadIdx.x] = ss;
+  __syncthreads();
+  for (int w = 128; w >= 1; w >>= 1) {
+    if ((int)threadIdx.x < w) part[threadIdx.x] += part[threadIdx.x + w];
+    __syncthreads();
+  }
+  const float r = 1.0f / sqrtf(part[0] / (float)K + eps);
+  for (int k = threadIdx.x * 8; k < K; k += 256 * 8) {
+    const f16x8 x = *reinterpret_cast<const f16x8 *>(a + k);
+    const f16x8 g = *reinterpret_cast<const f16x8 *>(gamma + k);
+    f16x8 y;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] = (f16)((float)x[i] * (float)g[i] * r);
+    *reinterpret_cast<f16x8 *>(out + (size_t)m * K + k) = y;
+  }
+}
+
+// Streaming read: four independent 16-byte loads per thread per iteration,
+// folded with xor so the loads cannot be removed; one word per workgroup.
+__global__ void __launch_bounds__(256)
+probe_read_kernel(const u32x4 *__restrict__ buf, size_t vecs,
+                  uint32_t *__restrict__ sink) {
+  __shared__ uint32_t red[256];
+  uint32_t acc = 0;
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  size_t v = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; v + 3 * stride < vecs; v += 4 * stride) {
+    const u32x4 a = buf[v], b = buf[v + stride], c = buf[v + 2 * stride],
+                d = buf[v + 3 * stride];
+    acc ^= a[0] ^ a[1] ^ a[2] ^ a[3] ^ b[0] ^ b[1] ^ b[2] ^ b[3] ^ c[0] ^
+           c[1] ^ c[2] ^ c[3] ^ d[0] ^ d[1] ^ d[2] ^ d[3];
+  }
+  for (; v < vecs; v += stride) {
+    const u32x4 a = buf[v];
+    acc ^= a[0] ^ a[1] ^ a[2] ^ a[3];
+  }
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int w = 128; w >= 1; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] ^= red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) sink[blockIdx.x] = red[0];
+}
+
+__global__ void __launch_bounds__(256)
+probe_copy_kernel(const u32x4 *__restrict__ src, u32x4 *__restrict__ dst,
+                  size_t vecs) {
+  for (size_t v = (size_t)blockIdx.x * blockDim.x + threadIdx.x; v < vecs;
+       v += (size_t)gridDim.x * blockDim.x)
+    dst[v] = src[v];
+}
+
+unsigned grid_for(size_t vecs, unsigned cap) {
+  size_t b = (vecs + 255) / 256;
+  if (b > cap) b = cap;
+  if (b < 1) b = 1;
+  return (unsigned)b;
+}
+
+}  // namespace
+
+hipError_t launch_add_bias(const f16 *in, const f16 *bias, int M, int N,
+                           f16 *out, hipStream_t stream) {
+  const size_t vecs = (size_t)M * N / 8;
+  hipLaunchKernelGGL(add_bias_kernel, dim3(grid_for(vecs, 8192)), dim3(256), 0,
+                     stream, in, bias, N, vecs, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_relu(const f16 *in, int M, int N, f16 *out,
+                       hipStream_t stream) {
+  const size_t vecs = (size_t)M * N / 8;
+  hipLaunchKernelGGL(relu_kernel, dim3(grid_for(vecs, 8192)), dim3(256), 0,
+                     stream, in, vecs, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm(const f16 *A, const f16 *gamma, float eps, int M,
+                          int K, f16 *out, hipStream_t stream) {
+  hipLaunchKernelGGL(rmsnorm_kernel, dim3(M), dim3(256), 0, stream, A, gamma,
+                     eps, K, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_probe_read(const void *buf, size_t bytes, uint32_t *sink,
+                             hipStream_t stream) {
+  const size_t vecs = bytes / 16;
+  hipLaunchKernelGGL(probe_read_kernel, dim3(grid_for(vecs / 4, 4096)), dim3(256),
+                     0, stream, reinterpret_cast<const u32x4 *>(buf), vecs, sink);
+  return hipGetLastError();
+}
+
+hipError_t launch_probe_copy(const void *src, void *dst, size_t bytes,
+                             hipStream_t stream) {
+  const size_t vecs = bytes / 16;
+  hipLaunchKernelGGL(probe_copy_kernel, dim3(grid_for(vecs / 4, 8192)), dim3(256),
+                     0, stream, reinterpret_cast<const u32x4 *>(src),
+                     reinterpret_cast<u32x4 *>(dst), vecs);
+  return hipGetLastError();
+}
+
+}  // namespace w4a16

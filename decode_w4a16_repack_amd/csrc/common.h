@@ -1,0 +1,94 @@
+// Internal declarations shared by the HIP translation units of libw4a16.so.
+// Not part of the C ABI (that is include/w4a16.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace w4a16 {
+
+typedef _Float16 f16;
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;        // CDNA wavefront width
+constexpr int kTileK = 128;      // k extent of one packed weight tile
+constexpr int kTileN = 16;       // columns of one packed weight tile
+constexpr int kTileBytes = 1024; // bytes of one packed tile (64 lanes x 16 B)
+
+inline size_t align256(size_t v) { return (v + 255) / 256 * 256; }
+
+// Byte offsets of the packed regions (layout version 1).
+struct PackedOffsets {
+  size_t scales;
+  size_t zeros;
+  size_t total;
+};
+
+inline PackedOffsets packed_offsets(int K, int N, int group, int scale_bytes,
+                                    bool has_zp) {
+  PackedOffsets o;
+  size_t G = (size_t)(K / group);
+  size_t w_bytes = (size_t)K * (size_t)N / 2;
+  o.scales = align256(w_bytes);
+  size_t s_end = o.scales + (size_t)N * G * (size_t)scale_bytes;
+  size_t zrow = (G + 1) / 2;
+  o.zeros = has_zp ? align256(s_end) : 0;
+  size_t end = has_zp ? o.zeros + (size_t)N * zrow : s_end;
+  o.total = align256(end);
+  return o;
+}
+
+// Everything a GEMM launch needs; filled by the API layer.
+struct GemmArgs {
+  const f16 *A;
+  int M, K, N;
+  const uint8_t *w[2];      // packed weight tiles (gate, up); w[1] only for gate_up
+  const void *scales[2];    // canonical [N][G] scales inside the packed buffer
+  const uint8_t *zeros[2];  // canonical [N][ceil(G/2)] zero-points, or null
+  int has_zp;
+  int epilogue;
+  const f16 *bias;
+  const f16 *gamma;  // null: no RMSNorm prologue
+  float eps;
+  f16 *out;
+  float *ws_part;     // [S][2 if gate_up][M][N] fp32 partial sums
+  float *ws_rms;      // [blocks][S][64] fp32 partial sums of squares
+  uint32_t *ws_cnt;   // [blocks] arrival counters, zero between calls
+  int split;          // number of K splits across workgroups
+  int cps;            // 128-wide k tiles per split
+};
+
+// Launch plan of one GEMM call, a pure function of the shape.
+struct Plan {
+  int mt;       // 16-row m tiles per wavefront (1, 2 or 4)
+  int gx, gy, gz;
+  int split, cps;
+  size_t ws_part_off, ws_rms_off, ws_cnt_off, ws_total;
+};
+
+Plan make_plan(int M, int K, int N, int group, bool gate_up);
+
+hipError_t launch_gemm(const GemmArgs &a, const Plan &p, int group,
+                       bool scale_f32, bool gate_up, hipStream_t stream);
+
+hipError_t launch_repack(const uint8_t *qweight, const void *scales,
+                         const uint8_t *zeros, int K, int N, int group,
+                         int scale_bytes, uint8_t *packed, hipStream_t stream);
+
+hipError_t launch_add_bias(const f16 *in, const f16 *bias, int M, int N,
+                           f16 *out, hipStream_t stream);
+hipError_t launch_relu(const f16 *in, int M, int N, f16 *out,
+                       hipStream_t stream);
+hipError_t launch_rmsnorm(const f16 *A, const f16 *gamma, float eps, int M,
+                          int K, f16 *out, hipStream_t stream);
+hipError_t launch_probe_read(const void *buf, size_t bytes, uint32_t *sink,
+                             hipStream_t stream);
+hipError_t launch_probe_copy(const void *src, void *dst, size_t bytes,
+                             hipStream_t stream);
+
+}  // namespace w4a16

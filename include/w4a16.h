@@ -1,0 +1,177 @@
+/*
+ * w4a16.h - C ABI of the MI355X (gfx950) fp16-activation x int4-weight
+ * group-quantized GEMM/GEMV library (libw4a16.so).
+ *
+ * The operation (onnx-genai pull request "Marlin-style fused fp16xint4
+ * tensor-core GEMM", section "What's landed"): activations A are fp16; the
+ * weights are 4-bit codes q with one scale per (output column, group of
+ * `group` consecutive k) and an optional asymmetric 4-bit zero-point zp; the
+ * weight used in the product is (q - zp) * scale, with zp = 8 when the
+ * weights are symmetric.  Group sizes 16, 32, 64 and 128 are supported, as on
+ * that page.
+ *
+ *   out[m][n] = epilogue( sum_k X[m][k] * (q[k][n] - zp[n][k/group]) * s[n][k/group] )
+ *
+ * with X = A, or X = RMSNorm(A) when a prologue weight gamma is given
+ * ("fused RMS-norm" update: x * gamma / sqrt(mean_k x^2 + eps)).  Epilogues:
+ * none, + bias, or max(+ bias, 0) ("Fusion benchmark" page: matmul plus bias
+ * plus relu).  w4a16_gemm_gate_up computes silu(X.Wg) * (X.Wu) ("gate_up
+ * SwiGLU MLP fusion" update).
+ *
+ * Numerics: (q - zp) is formed exactly in fp16, products with A are exact in
+ * fp32, sums are fp32, and each group's fp32 partial sum is multiplied by its
+ * scale after the contraction ("per-group scale AFTER the tensor-core
+ * accumulate").  The output is rounded once to fp16 (nearest even).  Results
+ * are run-to-run bit-identical: split-K partial sums are reduced in a fixed
+ * order, never with floating-point atomics.
+ *
+ * Conventions for every entry point:
+ *  - All data pointers are DEVICE pointers owned by the caller.  The library
+ *    never allocates, frees, synchronizes or reads data back to the host.
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
+ *    null stream).  The launch grid depends only on the arguments.
+ *  - Device pointers must be 16-byte aligned (W4A16_ERR_ALIGN otherwise).
+ *  - Arguments are validated on the host before any HIP call; on error
+ *    nothing is enqueued and a negative w4a16_status is returned.  A failed
+ *    launch returns W4A16_ERR_LAUNCH.
+ *  - Shapes: M >= 1, K a positive multiple of 128, N a positive multiple of
+ *    16, group in {16, 32, 64, 128} (W4A16_ERR_SHAPE / W4A16_ERR_GROUP).
+ *
+ * Canonical (input) weight format, the ONNX MatMulNBits reading:
+ *   qweight u8[N][K/2]        code k of column n is nibble (k mod 2) of byte
+ *                             k/2 of row n, even k in the low nibble
+ *   scales  fp16|fp32 [N][G]  G = K/group
+ *   zeros   u8[N][ceil(G/2)]  zero-point of group i in nibble (i mod 2) of
+ *                             byte i/2 of row n, even i low; NULL = symmetric
+ */
+#ifndef W4A16_H
+#define W4A16_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define W4A16_LAYOUT_VERSION 1
+
+typedef enum {
+  W4A16_OK = 0,
+  W4A16_ERR_NULL = -1,      /* a required pointer is NULL */
+  W4A16_ERR_SHAPE = -2,     /* M < 1, K % 128, N % 16, K % group, too large */
+  W4A16_ERR_GROUP = -3,     /* group not in {16, 32, 64, 128} */
+  W4A16_ERR_DTYPE = -4,     /* scale_dtype not a W4A16_SCALE_* value */
+  W4A16_ERR_EPILOGUE = -5,  /* unknown epilogue, or a bias epilogue without bias */
+  W4A16_ERR_WORKSPACE = -6, /* workspace NULL or smaller than required */
+  W4A16_ERR_ALIGN = -7,     /* a device pointer is not 16-byte aligned */
+  W4A16_ERR_LAUNCH = -8     /* the HIP launch failed (hipGetLastError) */
+} w4a16_status;
+
+enum { W4A16_SCALE_F16 = 0, W4A16_SCALE_F32 = 1 };
+
+enum { W4A16_EPI_NONE = 0, W4A16_EPI_BIAS = 1, W4A16_EPI_BIAS_RELU = 2 };
+
+typedef void *w4a16_stream; /* a hipStream_t */
+
+/*
+ * Packed layout, version 1 (KC = K/128, G = K/group).  The page requires a
+ * one-time, bijective reorder of the weights for coalesced loads, with the
+ * device repack byte-identical to the host reference ("What's landed").
+ *   Weights at offset 0, K*N/2 bytes: tile (t = n/16, kc = k/128) is 1 KiB
+ *     at byte (t*KC + kc)*1024; lane l (0..63) of a 64-lane wavefront owns
+ *     its 16 bytes at l*16; 32-bit word d (0..3) of lane l holds the codes
+ *     k = 128*kc + 32*d + 8*(l/16) + j, j = 0..7, of column n = 16*t + l%16,
+ *     code j in bits 4*(j/2) (even j) or 16 + 4*(j/2) (odd j).
+ *   Scales at offset align256(K*N/2): the canonical [N][G] array, bytes
+ *     unchanged.
+ *   Zero-points (only when zeros != NULL) at offset align256(end of scales):
+ *     the canonical u8[N][ceil(G/2)] array, bytes unchanged.
+ *   Total: align256(end of the last region).  Pad bytes are zero.
+ */
+size_t w4a16_packed_bytes(int K, int N, int group, int scale_dtype, int has_zp);
+
+/*
+ * One-time repack of canonical weights into the packed layout above.
+ * qweight, scales: required; zeros: NULL for symmetric weights.  packed
+ * must hold w4a16_packed_bytes(K, N, group, scale_dtype, zeros != NULL)
+ * bytes and must not overlap the inputs.  The packed buffer serves every M.
+ */
+int w4a16_repack(const uint8_t *qweight, const void *scales,
+                 const uint8_t *zeros, int K, int N, int group,
+                 int scale_dtype, void *packed, w4a16_stream stream);
+
+/*
+ * Workspace bytes w4a16_gemm (gate_up = 0) or w4a16_gemm_gate_up
+ * (gate_up = 1) needs for this shape: fp32 split-K partial sums and
+ * arrival counters.  0 when the shape runs without split-K.  The workspace
+ * must be zero-filled once after allocation; every call leaves its counters
+ * at zero again, so it can be reused by later calls.  Calls that share a
+ * workspace must not run concurrently.
+ */
+size_t w4a16_workspace_bytes(int M, int K, int N, int group, int gate_up);
+
+/*
+ * Fused GEMM.  A: fp16 [M][K] row-major.  packed: from w4a16_repack with
+ * the same K, N, group, scale_dtype and has_zp (has_zp = zeros were given).
+ * epilogue: W4A16_EPI_*; bias: fp16 [N], required for the bias epilogues.
+ * rms_gamma: fp16 [K] enables the RMSNorm prologue with rms_eps; NULL
+ * disables it.  out: fp16 [M][N] row-major; rows are written once, nothing
+ * outside out[0..M-1][0..N-1] is touched.  workspace: see
+ * w4a16_workspace_bytes (may be NULL when that returns 0).
+ */
+int w4a16_gemm(const void *A, int M, int K, int N, int group, int scale_dtype,
+               int has_zp, const void *packed, int epilogue, const void *bias,
+               const void *rms_gamma, float rms_eps, void *out,
+               void *workspace, size_t workspace_bytes, w4a16_stream stream);
+
+/*
+ * Paired gate/up projection with the SwiGLU epilogue:
+ * out = silu(X.Wg) * (X.Wu), silu(v) = v / (1 + exp(-v)), computed in fp32
+ * and rounded once.  packed_gate and packed_up are two separately repacked
+ * weights with the same K, N, group, scale_dtype and has_zp.  Optional
+ * RMSNorm prologue as in w4a16_gemm.
+ */
+int w4a16_gemm_gate_up(const void *A, int M, int K, int N, int group,
+                       int scale_dtype, int has_zp, const void *packed_gate,
+                       const void *packed_up, const void *rms_gamma,
+                       float rms_eps, void *out, void *workspace,
+                       size_t workspace_bytes, w4a16_stream stream);
+
+/* Static, human-readable text for a w4a16_status value. */
+const char *w4a16_status_string(int status);
+
+/* W4A16_LAYOUT_VERSION of the packed layout this library reads and writes. */
+int w4a16_layout_version(void);
+
+/*
+ * Measurement aids.  The "Fusion benchmark" page compares a fused kernel
+ * with the unfused chain built from the same source; these are the unfused
+ * chain's separate passes, each one kernel reading and writing HBM.
+ *   w4a16_add_bias: out[m][n] = fp16(in[m][n] + bias[n])
+ *   w4a16_relu:     out[m][n] = max(in[m][n], 0)
+ *   w4a16_rmsnorm:  out[m][k] = fp16(A[m][k] * gamma[k] / sqrt(mean A^2 + eps))
+ * All fp16, row-major; in-place (out == in) is allowed for the first two.
+ */
+int w4a16_add_bias(const void *in, const void *bias, int M, int N, void *out,
+                   w4a16_stream stream);
+int w4a16_relu(const void *in, int M, int N, void *out, w4a16_stream stream);
+int w4a16_rmsnorm(const void *A, const void *gamma, float eps, int M, int K,
+                  void *out, w4a16_stream stream);
+
+/*
+ * Streaming probes for the achievable HBM rate.  w4a16_probe_read reads
+ * `bytes` (a multiple of 16) and writes one 32-bit value per workgroup to
+ * sink (at least 4096 * 4 bytes) so the reads cannot be elided;
+ * w4a16_probe_copy copies `bytes` (a multiple of 16) from src to dst.
+ */
+int w4a16_probe_read(const void *buf, size_t bytes, void *sink,
+                     w4a16_stream stream);
+int w4a16_probe_copy(const void *src, void *dst, size_t bytes,
+                     w4a16_stream stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A16_H */

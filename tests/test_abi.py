@@ -1,0 +1,139 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/w4a16.h declares, and rejects bad arguments on the host before any
+HIP call (every error status is forced here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from decode_w4a16_repack_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w4a16.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(w4a16_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libw4a16.so is not built; run __graft_entry__.build()")
+    return _lib.lib()
+
+
+def test_exports_every_header_function(L):
+    names = header_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(_lib.EXPORTS)
+
+
+def test_header_enums_match_binding():
+    text = open(HEADER).read()
+    for name, val in [("W4A16_ERR_NULL", -1), ("W4A16_ERR_SHAPE", -2),
+                      ("W4A16_ERR_GROUP", -3), ("W4A16_ERR_DTYPE", -4),
+                      ("W4A16_ERR_EPILOGUE", -5), ("W4A16_ERR_WORKSPACE", -6),
+                      ("W4A16_ERR_ALIGN", -7), ("W4A16_ERR_LAUNCH", -8)]:
+        assert re.search(rf"{name}\s*=\s*{val}\b", text), name
+        assert getattr(_lib, name[6:]) == val
+    assert re.search(r"W4A16_EPI_BIAS_RELU\s*=\s*2", text)
+    assert re.search(r"W4A16_SCALE_F32\s*=\s*1", text)
+
+
+def test_layout_version_and_status_strings(L):
+    assert L.w4a16_layout_version() == 1
+    for st in range(-8, 1):
+        assert len(L.w4a16_status_string(st)) > 0
+    assert L.w4a16_status_string(-99) == b"unknown status"
+
+
+def test_packed_bytes_matches_oracle_layout(L, oracle_lib):
+    import oracle
+    for K, N, g, sdt, zp in [(5120, 13824, 128, 0, 1), (5120, 13824, 128, 0, 0),
+                             (512, 512, 32, 1, 1), (4096, 4096, 16, 0, 1),
+                             (128, 16, 16, 1, 0), (384, 48, 128, 0, 1)]:
+        esize = 2 if sdt == 0 else 4
+        assert L.w4a16_packed_bytes(K, N, g, sdt, zp) == oracle.packed_layout(K, N, g, esize, zp)[2]
+
+
+def test_packed_bytes_rejects_bad_shapes(L):
+    assert L.w4a16_packed_bytes(100, 16, 16, 0, 1) == 0
+    assert L.w4a16_packed_bytes(128, 15, 16, 0, 1) == 0
+    assert L.w4a16_packed_bytes(128, 16, 8, 0, 1) == 0
+    assert L.w4a16_packed_bytes(128, 16, 16, 7, 1) == 0
+
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: validation fails first
+
+
+def gemm(L, A=FAKE, M=2, K=512, N=512, group=32, sdt=0, zp=1, packed=FAKE, epi=0,
+         bias=None, gamma=None, out=FAKE, ws=None, ws_n=0):
+    return L.w4a16_gemm(A, M, K, N, group, sdt, zp, packed, epi, bias, gamma, 1e-6, out,
+                        ws, ws_n, None)
+
+
+def test_gemm_validation_statuses(L):
+    assert gemm(L, A=None) == _lib.ERR_NULL
+    assert gemm(L, packed=None) == _lib.ERR_NULL
+    assert gemm(L, out=None) == _lib.ERR_NULL
+    assert gemm(L, M=0) == _lib.ERR_SHAPE
+    assert gemm(L, K=500) == _lib.ERR_SHAPE
+    assert gemm(L, N=24) == _lib.ERR_SHAPE
+    assert gemm(L, group=48) == _lib.ERR_GROUP
+    assert gemm(L, group=256) == _lib.ERR_GROUP
+    assert gemm(L, sdt=2) == _lib.ERR_DTYPE
+    assert gemm(L, epi=3) == _lib.ERR_EPILOGUE
+    assert gemm(L, epi=1, bias=None) == _lib.ERR_EPILOGUE
+    assert gemm(L, epi=2, bias=None) == _lib.ERR_EPILOGUE
+    assert gemm(L, A=FAKE + 2) == _lib.ERR_ALIGN
+    assert gemm(L, out=FAKE + 8) == _lib.ERR_ALIGN
+    assert gemm(L, epi=1, bias=FAKE + 4) == _lib.ERR_ALIGN
+    # a shape that needs split-K partials must get a workspace
+    M, K, N, g = 1, 5120, 13824, 128
+    need = L.w4a16_workspace_bytes(M, K, N, g, 0)
+    assert need > 0
+    assert gemm(L, M=M, K=K, N=N, group=g, ws=None) == _lib.ERR_WORKSPACE
+    assert gemm(L, M=M, K=K, N=N, group=g, ws=FAKE, ws_n=need - 1) == _lib.ERR_WORKSPACE
+    assert gemm(L, M=M, K=K, N=N, group=g, ws=FAKE + 4, ws_n=need) == _lib.ERR_ALIGN
+
+
+def test_gate_up_and_repack_validation(L):
+    f = L.w4a16_gemm_gate_up
+    assert f(FAKE, 2, 512, 512, 32, 0, 1, FAKE, None, None, 1e-6, FAKE, None, 0, None) == _lib.ERR_NULL
+    assert f(FAKE, 2, 512, 512, 33, 0, 1, FAKE, FAKE, None, 1e-6, FAKE, None, 0, None) == _lib.ERR_GROUP
+    assert f(FAKE, 2, 512, 512, 32, 0, 1, FAKE, FAKE + 1, None, 1e-6, FAKE, None, 0, None) == _lib.ERR_ALIGN
+    r = L.w4a16_repack
+    assert r(None, FAKE, None, 512, 512, 32, 0, FAKE, None) == _lib.ERR_NULL
+    assert r(FAKE, FAKE, None, 512, 520, 32, 0, FAKE, None) == _lib.ERR_SHAPE
+    assert r(FAKE, FAKE, None, 512, 512, 32, 5, FAKE, None) == _lib.ERR_DTYPE
+    assert r(FAKE, FAKE, FAKE + 8, 512, 512, 32, 0, FAKE, None) == _lib.ERR_ALIGN
+
+
+def test_aux_validation(L):
+    assert L.w4a16_add_bias(FAKE, None, 2, 16, FAKE, None) == _lib.ERR_NULL
+    assert L.w4a16_relu(FAKE, 2, 20, FAKE, None) == _lib.ERR_SHAPE
+    assert L.w4a16_rmsnorm(FAKE, FAKE, 1e-6, 2, 100, FAKE, None) == _lib.ERR_SHAPE
+    assert L.w4a16_probe_read(FAKE, 15, FAKE, None) == _lib.ERR_SHAPE
+    assert L.w4a16_probe_copy(FAKE, FAKE + 4, 16, None) == _lib.ERR_ALIGN
+
+
+def test_workspace_is_zero_without_split_and_grows_with_m(L):
+    # large N at M=128 has enough workgroups without split-K
+    assert L.w4a16_workspace_bytes(128, 5120, 13824, 128, 0) == 0
+    assert L.w4a16_workspace_bytes(0, 5120, 13824, 128, 0) == 0
+    w1 = L.w4a16_workspace_bytes(1, 5120, 13824, 128, 0)
+    w1g = L.w4a16_workspace_bytes(1, 5120, 13824, 128, 1)
+    assert 0 < w1 < w1g
+
+
+def test_single_hip_runtime_after_load(L):
+    """The library must bind to the HIP runtime torch loaded (one per process)."""
+    maps = open("/proc/self/maps").read()
+    libs = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
+    assert len(libs) <= 1, libs

@@ -1,0 +1,276 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Every input is seeded and synthetic (decode_w4a16_repack_amd.synth); expected
+values come only from ``oracle``.  Sizes: small shapes compared element by
+element (several 16x128 tiles and ragged M), and the K=5120 N=13824 g=128
+decode shape compared on sampled columns in the launch configuration the
+benchmark times.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import decode_w4a16_repack_amd as w4
+from decode_w4a16_repack_amd import synth
+
+from gpu_cases import check_close, repack_dev, sample_cols, to_dev
+
+pytestmark = pytest.mark.gpu
+
+F16, F32 = np.float16, np.float32
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import oracle as o
+    o.build(force=False)
+    torch.manual_seed(0)
+
+
+def run_gemm(p, **kw):
+    w = repack_dev(p.w)
+    A = to_dev(p.A)
+    out = w4.gemm(A, w, bias=to_dev(p.bias) if kw.get("epilogue", "none") != "none" else None,
+                  gamma=to_dev(p.gamma) if kw.get("rms") else None,
+                  epilogue=kw.get("epilogue", "none"), eps=kw.get("eps", 1e-6))
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def ref_gemm(p, cols=None, **kw):
+    return oracle.gemm(p.A, p.w.qweight, p.w.scales, p.w.zeros, p.group, p.N,
+                       gamma=p.gamma if kw.get("rms") else None, eps=kw.get("eps", 1e-6),
+                       epilogue=kw.get("epilogue", "none"),
+                       bias=p.bias if kw.get("epilogue", "none") != "none" else None,
+                       cols=cols)
+
+
+# ------------------------------------------------------------------- repack
+
+
+@pytest.mark.parametrize("K,N,g,sdt,asym", [
+    (512, 512, 32, F16, True), (4096, 4096, 16, F32, False),
+    (256, 48, 64, F32, True), (5120, 13824, 128, F16, True), (1024, 4096, 128, F16, False)])
+def test_device_repack_is_byte_identical_to_host(K, N, g, sdt, asym):
+    p = synth.make_problem(1, K, N, g, seed=0, scale_dtype=sdt, asym=asym)
+    host = oracle.repack(p.w.qweight, p.w.scales, p.w.zeros, K, N, g)
+    dev = repack_dev(p.w).data.cpu().numpy()
+    assert dev.shape == host.shape
+    assert np.array_equal(dev, host)
+
+
+# ------------------------------------------------------------- small shapes
+
+
+def test_tiny_config_full_output():
+    """M=2 K=512 N=512 g=32, asymmetric zp, fp16 scales, seed 0: every output."""
+    p = synth.make_problem(2, 512, 512, 32, seed=0)
+    check_close(run_gemm(p), ref_gemm(p), "tiny")
+
+
+SMALL_M = [1, 2, 3, 7, 16, 17, 33, 64, 65, 128, 130]
+
+
+@pytest.mark.parametrize("M", SMALL_M)
+@pytest.mark.parametrize("g", [16, 32, 64, 128])
+def test_small_shapes_all_outputs(M, g):
+    i = SMALL_M.index(M) + g
+    sdt = F32 if i % 2 else F16
+    asym = (i // 2) % 2 == 0
+    p = synth.make_problem(M, 1024, 384, g, seed=M * 7 + g, scale_dtype=sdt, asym=asym)
+    check_close(run_gemm(p), ref_gemm(p), f"M={M} g={g} {sdt.__name__} asym={asym}")
+
+
+@pytest.mark.parametrize("sdt", [F16, F32])
+@pytest.mark.parametrize("asym", [True, False])
+@pytest.mark.parametrize("M", [1, 16, 40])
+def test_scale_dtype_and_zp_variants(sdt, asym, M):
+    p = synth.make_problem(M, 2048, 256, 64, seed=3, scale_dtype=sdt, asym=asym)
+    check_close(run_gemm(p), ref_gemm(p), f"M={M} {sdt.__name__} asym={asym}")
+
+
+def test_rows_beyond_m_untouched():
+    for M in (7, 33):
+        p = synth.make_problem(M, 1024, 256, 32, seed=M)
+        w = repack_dev(p.w)
+        big = torch.full((M + 3, 256), 1234.0, dtype=torch.float16, device="cuda")
+        w4.gemm(to_dev(p.A), w, out=big[:M])
+        torch.cuda.synchronize()
+        got = big.cpu().numpy()
+        assert np.all(got[M:] == np.float16(1234.0))
+        check_close(got[:M], ref_gemm(p), f"canary M={M}")
+
+
+# ----------------------------------------------- decode shape, sampled columns
+
+
+DECODE_M = [1, 2, 4, 7, 8, 16, 32, 33, 64, 128]
+
+
+@pytest.mark.parametrize("M", DECODE_M)
+def test_decode_shape_sampled(M):
+    K, N, g = 5120, 13824, 128
+    p = synth.make_problem(M, K, N, g, seed=0)
+    got = run_gemm(p)
+    cols = sample_cols(N, 160 if M <= 32 else 64, seed=M)
+    err, tol = check_close(got[:, cols], ref_gemm(p, cols=cols), f"decode M={M}")
+    assert np.all(np.isfinite(got))
+
+
+@pytest.mark.parametrize("sdt,asym", [(F16, False), (F32, True), (F32, False)])
+def test_decode_shape_variants_sampled(sdt, asym):
+    K, N, g, M = 5120, 13824, 128, 16
+    p = synth.make_problem(M, K, N, g, seed=1, scale_dtype=sdt, asym=asym)
+    got = run_gemm(p)
+    cols = sample_cols(N, 96, seed=2)
+    check_close(got[:, cols], ref_gemm(p, cols=cols), f"decode {sdt.__name__} asym={asym}")
+
+
+# ------------------------------------------------------- exactness properties
+
+
+@pytest.mark.parametrize("M", [1, 16, 64])
+def test_run_to_run_bit_identical(M):
+    p = synth.make_problem(M, 5120, 13824, 128, seed=4)
+    w = repack_dev(p.w)
+    A = to_dev(p.A)
+    y1 = w4.gemm(A, w).clone()
+    y2 = w4.gemm(A, w).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+
+
+def test_explicit_zp8_bit_identical_to_symmetric():
+    p = synth.make_problem(16, 1024, 512, 32, seed=6, asym=False)
+    G = p.K // p.group
+    z8 = synth.pack_nibbles_rows(np.full((p.N, G), 8, np.uint8))
+    A = to_dev(p.A)
+    w_sym = w4.repack(to_dev(p.w.qweight), to_dev(p.w.scales), None, p.K, p.N, p.group)
+    w_z8 = w4.repack(to_dev(p.w.qweight), to_dev(p.w.scales), to_dev(z8), p.K, p.N, p.group)
+    assert torch.equal(w4.gemm(A, w_sym), w4.gemm(A, w_z8))
+
+
+def test_unit_scale_integer_case_exact():
+    """s = 1, zp = 0, small integer A: the fp32 sums are exact integers, so the
+    GPU result equals the int64 product rounded once to fp16."""
+    rng = np.random.default_rng(8)
+    K, N, M, g = 1024, 256, 5, 128
+    codes = rng.integers(0, 16, size=(K, N), dtype=np.uint8)
+    w = synth.weight_from_codes(codes, np.ones((N, K // g), F16), np.zeros((N, K // g), np.uint8), g)
+    A = rng.integers(-2, 3, size=(M, K)).astype(F16)
+    dev = w4.gemm(to_dev(A), repack_dev(w))
+    ref = (A.astype(np.int64) @ codes.astype(np.int64)).astype(np.float64).astype(F16)
+    assert np.array_equal(dev.cpu().numpy(), ref)
+
+
+def test_workspace_reuse_across_shapes():
+    """Split-K counters must be left at zero: alternate shapes on one workspace."""
+    ws = w4.Workspace()
+    cases = [synth.make_problem(M, 5120, 4096, 128, seed=M) for M in (1, 4, 1, 8)]
+    for p in cases:
+        w = repack_dev(p.w)
+        got = w4.gemm(to_dev(p.A), w, workspace=ws).cpu().numpy()
+        cols = sample_cols(p.N, 64, seed=p.M)
+        check_close(got[:, cols], ref_gemm(p, cols=cols), f"reuse M={p.M}")
+
+
+# ------------------------------------------------------------------ epilogues
+
+
+@pytest.mark.parametrize("g", [16, 32, 64, 128])
+@pytest.mark.parametrize("epi", ["bias", "bias_relu"])
+def test_bias_epilogues_group_sweep(g, epi):
+    p = synth.make_problem(16, 4096, 4096, g, seed=g, bias=True)
+    got = run_gemm(p, epilogue=epi)
+    cols = sample_cols(p.N, 512, seed=g)
+    check_close(got[:, cols], ref_gemm(p, cols=cols, epilogue=epi), f"{epi} g={g}")
+    if epi == "bias_relu":
+        assert (got >= 0).all()
+
+
+@pytest.mark.parametrize("g", [16, 32, 64, 128])
+def test_rmsnorm_prologue_group_sweep(g):
+    p = synth.make_problem(16, 4096, 4096, g, seed=100 + g, gamma=True)
+    got = run_gemm(p, rms=True)
+    cols = sample_cols(p.N, 512, seed=g)
+    check_close(got[:, cols], ref_gemm(p, cols=cols, rms=True), f"rmsnorm g={g}")
+
+
+@pytest.mark.parametrize("M", [1, 5, 40])
+def test_rmsnorm_prologue_small(M):
+    p = synth.make_problem(M, 1024, 256, 32, seed=M, gamma=True)
+    check_close(run_gemm(p, rms=True), ref_gemm(p, rms=True), f"rmsnorm M={M}")
+
+
+def test_unfused_chain_matches_fused():
+    """FUSED=0 chain (GEMM -> bias pass -> ReLU pass; RMSNorm pass -> GEMM)
+    computes the same as the fused kernels, within the tolerance."""
+    p = synth.make_problem(16, 4096, 4096, 64, seed=7, bias=True, gamma=True)
+    w = repack_dev(p.w)
+    A, b, gm = to_dev(p.A), to_dev(p.bias), to_dev(p.gamma)
+    y = w4.relu(w4.add_bias(w4.gemm(A, w), b))
+    fused = w4.gemm(A, w, epilogue="bias_relu", bias=b)
+    cols = sample_cols(p.N, 256)
+    ref = ref_gemm(p, cols=cols, epilogue="bias_relu")
+    check_close(y.cpu().numpy()[:, cols], ref, "unfused bias_relu", strict=False)
+    check_close(fused.cpu().numpy()[:, cols], ref, "fused bias_relu")
+    xn = w4.rmsnorm(A, gm, 1e-6)
+    y2 = w4.gemm(xn, w)
+    ref2 = ref_gemm(p, cols=cols, rms=True)
+    check_close(y2.cpu().numpy()[:, cols], ref2, "unfused rmsnorm", strict=False)
+
+
+def test_unfused_passes_exact():
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((16, 256)).astype(F16)
+    b = rng.normal(0, 0.1, 256).astype(F16)
+    got_b = w4.add_bias(to_dev(x), to_dev(b)).cpu().numpy()
+    assert np.array_equal(got_b, (x.astype(F32) + b.astype(F32)).astype(F16))
+    got_r = w4.relu(to_dev(x)).cpu().numpy()
+    assert np.array_equal(got_r, np.maximum(x, F16(0)))
+
+
+# -------------------------------------------------------------------- gate_up
+
+
+def run_gate_up(p, rms=False):
+    wg, wu = repack_dev(p.w), repack_dev(p.w_up)
+    out = w4.gemm_gate_up(to_dev(p.A), wg, wu, gamma=to_dev(p.gamma) if rms else None)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def ref_gate_up(p, cols=None, rms=False):
+    return oracle.gate_up(p.A, (p.w.qweight, p.w.scales, p.w.zeros),
+                          (p.w_up.qweight, p.w_up.scales, p.w_up.zeros), p.group, p.N,
+                          gamma=p.gamma if rms else None, cols=cols)
+
+
+def test_gate_up_config_sampled():
+    """M=32, K=5120, N=13824, g=128 asym: silu(A.Wg) * (A.Wu)."""
+    p = synth.make_problem(32, 5120, 13824, 128, seed=0, gate_up=True)
+    got = run_gate_up(p)
+    cols = sample_cols(p.N, 128)
+    check_close(got[:, cols], ref_gate_up(p, cols=cols), "gate_up M=32")
+
+
+@pytest.mark.parametrize("M,g,rms", [(1, 128, False), (8, 16, True), (3, 32, False), (70, 64, True)])
+def test_gate_up_small_all_outputs(M, g, rms):
+    p = synth.make_problem(M, 1024, 256, g, seed=M + g, gate_up=True, gamma=rms)
+    check_close(run_gate_up(p, rms), ref_gate_up(p, rms=rms), f"gate_up M={M} g={g} rms={rms}")
+
+
+# --------------------------------------------------------------------- probes
+
+
+def test_probes():
+    src = torch.randint(0, 255, (1 << 22,), dtype=torch.uint8, device="cuda")
+    dst = torch.zeros_like(src)
+    w4.probe_copy(src, dst)
+    sink = torch.zeros(4096, dtype=torch.int32, device="cuda")
+    w4.probe_read(src, sink)
+    torch.cuda.synchronize()
+    assert torch.equal(src, dst)
