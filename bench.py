@@ -1,0 +1,306 @@
+"""Benchmark of the W4A16 hot path on one MI355X.
+
+Headline (one JSON line on stdout): the decode GEMV, M=1 K=5120 N=13824
+group 128 with asymmetric 4-bit zero-points and fp16 scales.  One step is one
+fused call (w4a16_gemm) over one resident input set; input sets rotate so the
+36.8 MB of packed weights per call come from HBM, not from the 256 MiB
+Infinity Cache.  `value` is algorithmic bytes per call / time per call.
+
+Also reported (stderr table and the JSON `m_sweep` field): the same shape for
+M = 2..128, with µs, TFLOP/s (2MNK / t, croqtile tutorial "TFLOPS"), GB/s and
+the fraction of the HBM and fp16-MFMA peaks; a streaming-read probe of the
+achievable HBM rate; and the CPU oracle timed on the host's cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+                       [--profile-kernel M]   (launch only that M, for rocprofv3)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("W4A16 GEMM µs + TFLOP/s + HBM GB/s (% peak), K=5120 N=13824 g=128, M=1..128")
+K, N, GROUP = 5120, 13824, 128
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, published
+INFINITY_CACHE = 256 << 20
+PAGE_M1_US = 69.5  # the pages' M=1 time for this shape (H200, context only)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemv_m1.json")
+KERNEL_SOURCES = ["decode_w4a16_repack_amd/csrc/ring.hip", "decode_w4a16_repack_amd/csrc/device.h", "decode_w4a16_repack_amd/csrc/gemm.hip", "decode_w4a16_repack_amd/csrc/common.h"]
+
+
+def algorithmic_bytes(M, K=K, N=N, group=GROUP, scale_bytes=2, has_zp=True, n_weights=1):
+    """Bytes the method must move once: packed int4 weights, scales,
+    zero-points, A read once, out written once."""
+    G = K // group
+    w = K * N // 2 + N * G * scale_bytes + (N * ((G + 1) // 2) if has_zp else 0)
+    return n_weights * w + 2 * M * K + 2 * M * N
+
+
+def flops(M, K=K, N=N, n_weights=1):
+    return 2 * M * N * K * n_weights
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class InputSets:
+    """R rotating resident input sets of one shape (packed weights + A)."""
+
+    def __init__(self, M, R, seed=0):
+        import torch
+        import decode_w4a16_repack_amd as w4
+        from decode_w4a16_repack_amd import synth
+        self.M = M
+        G = K // GROUP
+        self.sets = []
+        p0 = synth.make_problem(M, K, N, GROUP, seed=seed)
+        dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+        g = torch.Generator(device="cuda")
+        g.manual_seed(seed + 1)
+        for r in range(R):
+            if r == 0:
+                q, s, z, A = dev(p0.w.qweight), dev(p0.w.scales), dev(p0.w.zeros), dev(p0.A)
+            else:
+                q = torch.randint(0, 256, (N, K // 2), dtype=torch.uint8, device="cuda", generator=g)
+                s = (torch.rand((N, G), device="cuda", generator=g) * 0.019 + 0.001).half()
+                z = torch.randint(0, 256, (N, (G + 1) // 2), dtype=torch.uint8, device="cuda", generator=g)
+                A = torch.randn((M, K), device="cuda", generator=g).half()
+            pw = w4.repack(q, s, z, K, N, GROUP)
+            out = torch.empty((M, N), dtype=torch.float16, device="cuda")
+            self.sets.append((A, pw, out))
+            del q, s, z
+        torch.cuda.synchronize()
+
+
+def rotations_needed(M):
+    per = algorithmic_bytes(M)
+    return max(2, math.ceil(2 * INFINITY_CACHE / per))
+
+
+def time_calls(sets, steps, warmup, ws):
+    """Device time per call.  The R rotating calls are captured once in a HIP
+    graph (no host launch cost between calls) and replayed; HIP events on the
+    launch stream bracket the whole timed region, synchronized on both sides.
+    Returns (us per call from events, wall seconds of the timed region,
+    number of calls timed)."""
+    import torch
+    import decode_w4a16_repack_amd as w4
+    R = len(sets.sets)
+    for i in range(max(warmup, R)):       # eager warmup (also sets kernel attributes)
+        A, pw, out = sets.sets[i % R]
+        w4.gemm(A, pw, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            for A, pw, out in sets.sets:
+                w4.gemm(A, pw, out=out, workspace=ws)
+    reps = max(1, steps // R)
+    with torch.cuda.stream(stream):
+        for _ in range(max(1, warmup // R)):
+            g.replay()
+        torch.cuda.synchronize()
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        start.record(stream)
+        for _ in range(reps):
+            g.replay()
+        stop.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    n = reps * R
+    us = start.elapsed_time(stop) * 1e3 / n
+    return us, wall, n
+
+
+def self_check(sets, ws):
+    """Cheap checks of the timed launch configuration that need no oracle:
+    every output finite, and a repeated call bit-identical (fixed-order
+    split-K reduction).  Element parity of this configuration against the
+    oracle is the GPU test suite's job."""
+    import torch
+    import decode_w4a16_repack_amd as w4
+    A, pw, out = sets.sets[0]
+    y1 = w4.gemm(A, pw, workspace=ws).clone()
+    y2 = w4.gemm(A, pw, workspace=ws)
+    torch.cuda.synchronize()
+    return {"finite": bool(torch.isfinite(y1).all()), "repeat_bit_identical": bool(torch.equal(y1, y2))}
+
+
+def hbm_probe(nbytes=1 << 30, reps=20):
+    import torch
+    import decode_w4a16_repack_amd as w4
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    sink = torch.zeros(4096, dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        w4.probe_read(buf, sink)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        w4.probe_read(buf, sink)
+        b.record()
+        b.synchronize()
+        times.append(a.elapsed_time(b) * 1e-3)
+    del buf
+    return nbytes / float(np.median(times)) / 1e9
+
+
+def cpu_baseline(budget_s=12.0):
+    """The oracle as it stands, on the host's cores, over whole M=1 calls of
+    the headline shape (dequantization inside the timed region)."""
+    import oracle
+    from decode_w4a16_repack_amd import synth
+    oracle.build(force=False)
+    p = synth.make_problem(1, K, N, GROUP, seed=0)
+    times = []
+    t_start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        oracle.gemm(p.A, p.w.qweight, p.w.scales, p.w.zeros, GROUP, N)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_start > budget_s or len(times) >= 50:
+            break
+    t = float(np.median(times))
+    cores = int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count() or 1)
+    return {"value": algorithmic_bytes(1) / t / 1e9, "unit": "GB/s", "cores": cores,
+            "kind": "oracle", "us_per_call": t * 1e6,
+            "sample": f"{len(times)} whole M=1 calls (K=5120 N=13824 g=128, all 13824 columns), "
+                      f"f64, median; {sum(times):.1f} s of CPU work"}
+
+
+def load_traffic():
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they
+    were taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=480)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--profile-kernel", type=int, default=0,
+                    help="only launch the GEMM at this M (for rocprofv3)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import decode_w4a16_repack_amd as w4
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    ws = w4.Workspace()
+
+    if args.profile_kernel:
+        M = args.profile_kernel
+        sets = InputSets(M, rotations_needed(M))
+        us, _, n = time_calls(sets, args.steps, args.warmup, ws)
+        log(f"profile M={M}: {us:.2f} us per call over {n} graph-replayed calls")
+        return
+
+    # headline: M = 1
+    M = 1
+    R = rotations_needed(M)
+    log(f"[bench] headline M=1 K={K} N={N} g={GROUP}: {R} rotating input sets")
+    sets = InputSets(M, R)
+    us_mean, wall, n_timed = time_calls(sets, args.steps, args.warmup, ws)
+    parity = self_check(sets, ws)
+    log(f"[bench] self-check {parity}")
+    b1 = algorithmic_bytes(M)
+    ms_per_step = wall / n_timed * 1e3
+    value = b1 / (ms_per_step * 1e-3) / 1e9
+    achieved = b1 / (us_mean * 1e-6) / 1e9
+    log(f"[bench] M=1: {us_mean:.2f} us per call (events), {ms_per_step * 1e3:.2f} us per step (wall)")
+    del sets
+    torch.cuda.empty_cache()
+
+    sweep = []
+    if not args.no_sweep:
+        for Ms in (1, 2, 4, 8, 16, 32, 64, 128):
+            s2 = InputSets(Ms, rotations_needed(Ms), seed=Ms)
+            t, _, _ = time_calls(s2, 160, 16, ws)
+            byt, fl = algorithmic_bytes(Ms), flops(Ms)
+            row = {"M": Ms, "us": t, "GBps": byt / t / 1e3, "TFLOPs": fl / t / 1e6,
+                   "pct_hbm_peak": 100 * byt / t / 1e3 / HBM_PEAK_GBS,
+                   "pct_mfma_peak": 100 * fl / t / 1e6 / MFMA_F16_PEAK_TFLOPS,
+                   "level": "HBM (rotated inputs), graph replay"}
+            sweep.append(row)
+            log(f"[bench] M={Ms:4d} {t:8.2f} us  {row['GBps']:8.1f} GB/s ({row['pct_hbm_peak']:5.1f}% HBM)"
+                f"  {row['TFLOPs']:7.2f} TFLOP/s ({row['pct_mfma_peak']:5.2f}% MFMA)")
+            del s2
+            torch.cuda.empty_cache()
+
+    probe = hbm_probe()
+    log(f"[bench] streaming-read probe: {probe:.1f} GB/s")
+    cpu = None if args.no_cpu else cpu_baseline()
+    if cpu:
+        log(f"[bench] cpu oracle: {cpu['value']:.3f} GB/s on {cpu['cores']} threads")
+
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": n_timed,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "decode GEMV M=1 K=5120 N=13824 group=128, asymmetric 4-bit zp, "
+                               "fp16 scales, fp16 A ~ N(0,1), 16 rotating resident input sets",
+                   "M": 1, "K": K, "N": N, "group": GROUP},
+        "us_per_call": us_mean,
+        "tflops": flops(1) / us_mean / 1e6,
+        "pct_hbm_peak": 100 * value / HBM_PEAK_GBS,
+        "hbm_probe_GBps": probe,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": load_traffic(),
+                     "algorithmic_bytes_per_launch": b1, "avg_launch_us": us_mean},
+        "cpu_baseline": cpu,
+        "self_check": parity,
+        "m_sweep": sweep,
+        "page_context": {"M1_us_H200": PAGE_M1_US, "note": "other hardware, context only"},
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

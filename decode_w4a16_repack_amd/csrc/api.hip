@@ -63,6 +63,12 @@ void fill_workspace(GemmArgs &a, const Plan &pl, void *ws) {
   uint8_t *b = static_cast<uint8_t *>(ws);
   a.split = pl.split;
   a.cps = pl.cps;
+  a.rows_pow2 = pl.rows_pow2;
+  a.lds_g = pl.lds_g;
+  a.lds_s = pl.lds_s;
+  a.lds_z = pl.lds_z;
+  a.gr = pl.gr;
+  a.lds_r = pl.lds_r;
   a.ws_part = pl.ws_total ? reinterpret_cast<float *>(b + pl.ws_part_off) : nullptr;
   a.ws_rms = pl.ws_total ? reinterpret_cast<float *>(b + pl.ws_rms_off) : nullptr;
   a.ws_cnt = pl.ws_total ? reinterpret_cast<uint32_t *>(b + pl.ws_cnt_off) : nullptr;
@@ -100,7 +106,11 @@ int w4a16_repack(const uint8_t *qweight, const void *scales,
 
 size_t w4a16_workspace_bytes(int M, int K, int N, int group, int gate_up) {
   if (M < 1 || M > kMaxDim || check_kn(K, N, group) != W4A16_OK) return 0;
-  return make_plan(M, K, N, group, gate_up != 0).ws_total;
+  // the plan (and so the workspace) may differ with the scale width: take
+  // the larger of fp16 and fp32 scales
+  const size_t a = make_plan(M, K, N, group, 2, gate_up != 0).ws_total;
+  const size_t b = make_plan(M, K, N, group, 4, gate_up != 0).ws_total;
+  return a > b ? a : b;
 }
 
 int w4a16_gemm(const void *A, int M, int K, int N, int group, int scale_dtype,
@@ -117,7 +127,7 @@ int w4a16_gemm(const void *A, int M, int K, int N, int group, int scale_dtype,
   if ((bias != nullptr && !aligned16(bias)) ||
       (rms_gamma != nullptr && !aligned16(rms_gamma)))
     return W4A16_ERR_ALIGN;
-  const Plan pl = make_plan(M, K, N, group, false);
+  const Plan pl = make_plan(M, K, N, group, scale_bytes_of(scale_dtype), false);
   st = check_workspace(pl, workspace, workspace_bytes);
   if (st != W4A16_OK) return st;
 
@@ -148,7 +158,7 @@ int w4a16_gemm_gate_up(const void *A, int M, int K, int N, int group,
   int st = check_gemm(A, M, K, N, group, scale_dtype, pk, 2, out);
   if (st != W4A16_OK) return st;
   if (rms_gamma != nullptr && !aligned16(rms_gamma)) return W4A16_ERR_ALIGN;
-  const Plan pl = make_plan(M, K, N, group, true);
+  const Plan pl = make_plan(M, K, N, group, scale_bytes_of(scale_dtype), true);
   st = check_workspace(pl, workspace, workspace_bytes);
   if (st != W4A16_OK) return st;
 

@@ -19,6 +19,24 @@ constexpr int kWave = 64;        // CDNA wavefront width
 constexpr int kTileK = 128;      // k extent of one packed weight tile
 constexpr int kTileN = 16;       // columns of one packed weight tile
 constexpr int kTileBytes = 1024; // bytes of one packed tile (64 lanes x 16 B)
+constexpr int kMaxSplitBlocks = 1024;  // split-K only below this many workgroups
+
+// Tile configurations of the ring kernel: MT 16-row m tiles per wavefront,
+// NWC column tiles x NWK k slices of wavefronts per workgroup, DA packed k
+// tiles per round.
+struct RingCfg {
+  int mt, nwc, nwk, da;
+};
+constexpr int kNumRingCfgs = 5;
+extern const RingCfg kRingCfgs[kNumRingCfgs];
+
+// Tile configurations of the small-M one-shot kernel: NWC column tiles x NWK
+// k slices per workgroup, at most CW packed k tiles per wavefront.
+struct OneshotCfg {
+  int mt, nwc, nwk, cw;
+};
+constexpr int kNumOneshotCfgs = 3;
+extern const OneshotCfg kOneshotCfgs[kNumOneshotCfgs];
 
 inline size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 
@@ -36,9 +54,8 @@ inline PackedOffsets packed_offsets(int K, int N, int group, int scale_bytes,
   size_t w_bytes = (size_t)K * (size_t)N / 2;
   o.scales = align256(w_bytes);
   size_t s_end = o.scales + (size_t)N * G * (size_t)scale_bytes;
-  size_t zrow = (G + 1) / 2;
   o.zeros = has_zp ? align256(s_end) : 0;
-  size_t end = has_zp ? o.zeros + (size_t)N * zrow : s_end;
+  size_t end = has_zp ? o.zeros + (size_t)N * G / 2 : s_end;
   o.total = align256(end);
   return o;
 }
@@ -48,8 +65,8 @@ struct GemmArgs {
   const f16 *A;
   int M, K, N;
   const uint8_t *w[2];      // packed weight tiles (gate, up); w[1] only for gate_up
-  const void *scales[2];    // canonical [N][G] scales inside the packed buffer
-  const uint8_t *zeros[2];  // canonical [N][ceil(G/2)] zero-points, or null
+  const void *scales[2];    // packed scales [N/16][G][16] inside the packed buffer
+  const uint8_t *zeros[2];  // packed zero-points [N/16][G][16 nibbles], or null
   int has_zp;
   int epilogue;
   const f16 *bias;
@@ -61,17 +78,35 @@ struct GemmArgs {
   uint32_t *ws_cnt;   // [blocks] arrival counters, zero between calls
   int split;          // number of K splits across workgroups
   int cps;            // 128-wide k tiles per split
+  int rows_pow2;      // staged activation rows: power of two >= min(M, 16*MT)
+  int lds_g;          // byte offset of the staged RMSNorm weight in LDS
+  int lds_s, lds_z;   // byte offsets of the staged scales / zero-points in LDS
+  int gr;             // staged groups per column tile
+  int lds_r;          // byte offset of the sum-of-squares scratch in LDS
 };
 
 // Launch plan of one GEMM call, a pure function of the shape.
 struct Plan {
-  int mt;       // 16-row m tiles per wavefront (1, 2 or 4)
+  int oneshot;  // 1: oneshot.hip kernel (kOneshotCfgs), 0: ring.hip kernel (kRingCfgs)
+  int cfg;      // index into the kernel's configuration table
   int gx, gy, gz;
   int split, cps;
+  int rows_pow2;
+  int lds_g, lds_s, lds_z, gr, lds_r;
+  size_t lds_bytes;
   size_t ws_part_off, ws_rms_off, ws_cnt_off, ws_total;
 };
 
-Plan make_plan(int M, int K, int N, int group, bool gate_up);
+// force_kind: -1 automatic, 0 ring kernel, 1 one-shot kernel; force_cfg < 0 /
+// force_split <= 0 select the built-in choice.
+Plan make_plan(int M, int K, int N, int group, int scale_bytes, bool gate_up,
+               int force_kind = -1, int force_cfg = -1, int force_split = 0);
+
+hipError_t launch_oneshot(const GemmArgs &a, const Plan &p, int group, bool scale_f32,
+                          bool gate_up, hipStream_t stream);
+
+hipError_t launch_ring(const GemmArgs &a, const Plan &p, int group, bool scale_f32,
+                       bool gate_up, hipStream_t stream);
 
 hipError_t launch_gemm(const GemmArgs &a, const Plan &p, int group,
                        bool scale_f32, bool gate_up, hipStream_t stream);

@@ -1,0 +1,165 @@
+// Device-side building blocks shared by the GEMM kernels.
+#pragma once
+
+#include "common.h"
+
+namespace w4a16 {
+
+__device__ __forceinline__ f16x2 as_f16x2(uint32_t v) {
+  return __builtin_bit_cast(f16x2, v);
+}
+
+// Eight codes of one packed word -> fp16 (q - z), exact.  Code j of the word
+// sits in bits 4*(j/2) (even j) or 16 + 4*(j/2) (odd j).  OR-ing a nibble into
+// the mantissa of fp16 1024.0 gives 1024 + q (bits 0-3 of a half) or
+// 1024 + 16q (bits 4-7); subtracting 1024 + z, or scaling by 1/16 and
+// subtracting 64 + z, leaves the integer q - z in [-15, 15], exact in fp16.
+// zlo = -(1024 + z), zhi = -(64 + z) in both halves.
+__device__ __forceinline__ f16x8 unpack8(uint32_t w, f16x2 zlo, f16x2 zhi) {
+  const uint32_t magic = 0x64006400u;  // fp16 1024.0 in both halves
+  const uint32_t w8 = w >> 8;
+  const f16x2 t0 = as_f16x2((w & 0x000F000Fu) | magic);   // j = 0, 1
+  const f16x2 t1 = as_f16x2((w & 0x00F000F0u) | magic);   // j = 2, 3 (x16)
+  const f16x2 t2 = as_f16x2((w8 & 0x000F000Fu) | magic);  // j = 4, 5
+  const f16x2 t3 = as_f16x2((w8 & 0x00F000F0u) | magic);  // j = 6, 7 (x16)
+  const f16x2 sixteenth = {(f16)0.0625f, (f16)0.0625f};
+  const f16x2 h0 = t0 + zlo;
+  const f16x2 h1 = t1 * sixteenth + zhi;
+  const f16x2 h2 = t2 + zlo;
+  const f16x2 h3 = t3 * sixteenth + zhi;
+  typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+  const f16x4 lo = __builtin_shufflevector(h0, h1, 0, 1, 2, 3);
+  const f16x4 hi = __builtin_shufflevector(h2, h3, 0, 1, 2, 3);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// fp16 constants -(1024 + z) and -(64 + z) in both halves, for z in 0..15,
+// built from their bit patterns: 1024 + z has exponent field 25 and
+// mantissa z (0x6400 | z); 64 + z has exponent field 21 and mantissa 16z
+// (0x5400 | z << 4); the sign bit makes them negative.
+__device__ __forceinline__ void zero_consts(uint32_t z, f16x2 &zlo, f16x2 &zhi) {
+  zlo = as_f16x2(0xE400E400u | (z * 0x00010001u));
+  zhi = as_f16x2(0xD400D400u | (z * 0x00100010u));
+}
+
+// D = A(16x32 fp16) x B(32x16 fp16) + C, fp32.  Lane l supplies A row l%16 and
+// B column l%16 at k slots 8*(l/16)..+7 (any k order works as long as A and
+// B agree, which the packed layout and the LDS reads guarantee); lane l gets
+// D rows 4*(l/16)+e, e = 0..3, of column l%16.
+__device__ __forceinline__ f32x4 mfma16(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float silu(float v) { return v / (1.0f + expf(-v)); }
+
+// Contract one packed k tile (128 k, four 32-deep MFMA steps) of one 16-column
+// weight tile with MT 16-row m tiles of activations and add the scaled group
+// sums into acc.
+//  * a_lane[t]: this lane's 16-byte activation slot of step 0 for m tile t;
+//    step d is d * dstride bytes further.  The tile is in fragment order
+//    (slot ((d * 4 + kq) * R + row)), so the 16 rows one MFMA operand reads
+//    are 16 consecutive slots.  Lanes whose row is beyond M point at a valid
+//    row instead: an A row only feeds its own output row, never written.
+//  * zp_of(gl) / scale_of(gl): zero-point (0..15) / scale of group gl
+//    (0 .. 128/G - 1) of the tile for this lane's column; each is asked for
+//    once per group.
+template <int MT, int G, class ZpOf, class ScaleOf>
+__device__ __forceinline__ void contract_tile_frag(f32x4 (&acc)[MT], const u32x4 &w,
+                                                   const uint8_t *const (&a_lane)[MT],
+                                                   int dstride, int kq, ZpOf zp_of,
+                                                   ScaleOf scale_of) {
+  constexpr int GPC = 128 / G;
+  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+  f16x8 a[4][MT];
+#pragma unroll
+  for (int d = 0; d < 4; ++d)
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+      a[d][t] = *reinterpret_cast<const f16x8 *>(a_lane[t] + d * dstride);
+  // zero-point constants of this lane's B slots (one group per 32-k step
+  // for G >= 32; for G = 16 the slot's group is 2d + kq/2)
+  f16x2 zlo[4], zhi[4];
+  if constexpr (G >= 32) {
+#pragma unroll
+    for (int gl = 0; gl < GPC; ++gl) {
+      f16x2 l, h;
+      zero_consts((uint32_t)zp_of(gl), l, h);
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+        if ((32 * d) / G == gl) { zlo[d] = l; zhi[d] = h; }
+    }
+  } else {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) zero_consts((uint32_t)zp_of(2 * d + (kq >> 1)), zlo[d], zhi[d]);
+  }
+  if constexpr (G >= 32) {
+    constexpr int SPG = G / 32;  // MFMA steps per group
+    f32x4 accg[MT];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const f16x8 b = unpack8(w[d], zlo[d], zhi[d]);
+#pragma unroll
+      for (int t = 0; t < MT; ++t)
+        accg[t] = mfma16(a[d][t], b, (d % SPG == 0) ? zero4 : accg[t]);
+      if ((d + 1) % SPG == 0) {
+        const float s = scale_of((32 * d) / G);
+#pragma unroll
+        for (int t = 0; t < MT; ++t) acc[t] += accg[t] * s;
+      }
+    }
+  } else {
+    // group 16: k slots kq = 0, 1 belong to group 2d, kq = 2, 3 to 2d + 1;
+    // two MFMAs per step, each with the other group's B lanes zeroed
+    const f16x8 zero8 = {};
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const f16x8 b = unpack8(w[d], zlo[d], zhi[d]);
+      const f16x8 blo = (kq < 2) ? b : zero8;
+      const f16x8 bhi = (kq < 2) ? zero8 : b;
+      const float s0 = scale_of(2 * d);
+      const float s1 = scale_of(2 * d + 1);
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        const f32x4 p0 = mfma16(a[d][t], blo, zero4);
+        const f32x4 p1 = mfma16(a[d][t], bhi, zero4);
+        acc[t] += p0 * s0;
+        acc[t] += p1 * s1;
+      }
+    }
+  }
+}
+
+// Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4):
+// lane l's 16 bytes at src land at lds_base + 16 * l.  lds_base must be the
+// same for the whole wavefront.  Completion is tracked by the vector-memory
+// counter, like any load.
+__device__ __forceinline__ void copy16_to_lds(const void *src, void *lds_base) {
+  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1))) *)src,
+                                   (void __attribute__((address_space(3))) *)lds_base, 16, 0, 0);
+}
+
+// Same with 4 bytes per lane (global_load_lds_dword): lane l's 4 bytes land
+// at lds_base + 4 * l.
+__device__ __forceinline__ void copy4_to_lds(const void *src, void *lds_base) {
+  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1))) *)src,
+                                   (void __attribute__((address_space(3))) *)lds_base, 4, 0, 0);
+}
+
+// s_waitcnt with only the vector-memory counter limited to n (< 64); the
+// other counters at their maximum (no wait).  GFX9 encoding: vmcnt[3:0] in
+// bits 3:0, expcnt in 6:4, lgkmcnt in 11:8, vmcnt[5:4] in 15:14.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt out of range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier that orders LDS only: global loads in flight stay in
+// flight (a plain __syncthreads also waits for every outstanding global load).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+}  // namespace w4a16

@@ -43,22 +43,33 @@ repack_weights_kernel(const uint32_t *__restrict__ q, uint32_t *__restrict__ out
   out[o] = y;
 }
 
-// Copies the scale and zero-point arrays into their regions and zero-fills
-// the pad words, so the whole metadata tail of the packed buffer is written.
+// Writes the metadata tail of the packed buffer byte by byte: scales in
+// [N/16][G][16] element order, zero-points in [N/16][G][16]-nibble order, and
+// zero pad bytes.  One-time work (a few MB at most), kept simple.
 __global__ void __launch_bounds__(256)
-repack_meta_kernel(const uint32_t *__restrict__ scales, size_t s_words,
-                   const uint32_t *__restrict__ zeros, size_t z_words,
-                   uint32_t *__restrict__ tail, size_t z_start_word,
-                   size_t tail_words) {
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < tail_words;
-       i += (size_t)gridDim.x * blockDim.x) {
-    uint32_t v = 0;
-    if (i < s_words) {
-      v = scales[i];
-    } else if (zeros != nullptr && i >= z_start_word && i < z_start_word + z_words) {
-      v = zeros[i - z_start_word];
+repack_meta_kernel(const uint8_t *__restrict__ scales, const uint8_t *__restrict__ zeros,
+                   int N, int G, int sb, size_t s_bytes, size_t z_off, size_t z_bytes,
+                   uint8_t *__restrict__ tail, size_t tail_bytes) {
+  const size_t zrow = (size_t)(G + 1) / 2;
+  for (size_t b = (size_t)blockIdx.x * blockDim.x + threadIdx.x; b < tail_bytes;
+       b += (size_t)gridDim.x * blockDim.x) {
+    uint8_t v = 0;
+    if (b < s_bytes) {
+      const size_t e = b / sb;  // packed element (t, i, c)
+      const size_t t = e / ((size_t)G * 16);
+      const size_t i = (e / 16) % G;
+      const size_t n = t * 16 + e % 16;
+      v = scales[(n * G + i) * sb + b % sb];
+    } else if (zeros != nullptr && b >= z_off && b < z_off + z_bytes) {
+      const size_t zb = b - z_off;  // packed byte: nibbles 2p, 2p+1 of (t, i)
+      const size_t t = zb / ((size_t)G * 8);
+      const size_t i = (zb / 8) % G;
+      const size_t n0 = t * 16 + 2 * (zb % 8);
+      const uint8_t lo = (zeros[n0 * zrow + i / 2] >> (4 * (i & 1))) & 15;
+      const uint8_t hi = (zeros[(n0 + 1) * zrow + i / 2] >> (4 * (i & 1))) & 15;
+      v = (uint8_t)(lo | (hi << 4));
     }
-    tail[i] = v;
+    tail[b] = v;
   }
 }
 
@@ -74,18 +85,16 @@ hipError_t launch_repack(const uint8_t *qweight, const void *scales,
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
-  const size_t G = (size_t)(K / group);
-  const size_t s_words = (size_t)N * G * (size_t)scale_bytes / 4;
-  const size_t z_words = zeros ? (size_t)N * ((G + 1) / 2) / 4 : 0;
-  const size_t tail_words = (off.total - off.scales) / 4;
-  const size_t z_start = zeros ? (off.zeros - off.scales) / 4 : 0;
-  unsigned mblocks = (unsigned)((tail_words + 255) / 256);
-  if (mblocks > 4096) mblocks = 4096;
+  const int G = K / group;
+  const size_t s_bytes = (size_t)N * G * scale_bytes;
+  const size_t tail_bytes = off.total - off.scales;
+  const size_t z_off = zeros ? off.zeros - off.scales : 0;
+  const size_t z_bytes = zeros ? (size_t)N * G / 2 : 0;
+  unsigned mblocks = (unsigned)((tail_bytes + 255) / 256);
+  if (mblocks > 8192) mblocks = 8192;
   hipLaunchKernelGGL(repack_meta_kernel, dim3(mblocks), dim3(256), 0, stream,
-                     reinterpret_cast<const uint32_t *>(scales), s_words,
-                     reinterpret_cast<const uint32_t *>(zeros), z_words,
-                     reinterpret_cast<uint32_t *>(packed + off.scales), z_start,
-                     tail_words);
+                     static_cast<const uint8_t *>(scales), zeros, N, G, scale_bytes, s_bytes,
+                     z_off, z_bytes, packed + off.scales, tail_bytes);
   return hipGetLastError();
 }
 

@@ -83,10 +83,12 @@ typedef void *w4a16_stream; /* a hipStream_t */
  *     its 16 bytes at l*16; 32-bit word d (0..3) of lane l holds the codes
  *     k = 128*kc + 32*d + 8*(l/16) + j, j = 0..7, of column n = 16*t + l%16,
  *     code j in bits 4*(j/2) (even j) or 16 + 4*(j/2) (odd j).
- *   Scales at offset align256(K*N/2): the canonical [N][G] array, bytes
- *     unchanged.
- *   Zero-points (only when zeros != NULL) at offset align256(end of scales):
- *     the canonical u8[N][ceil(G/2)] array, bytes unchanged.
+ *   Scales at offset align256(K*N/2), N*G elements of the scale dtype:
+ *     element ((n/16)*G + i)*16 + n%16 is scales[n][i] (bytes unchanged), so
+ *     the 16 scales of one column tile and group are contiguous.
+ *   Zero-points (only when zeros != NULL) at offset align256(end of scales),
+ *     N*G/2 bytes: nibble ((n/16)*G + i)*16 + n%16 (low nibble first) is the
+ *     zero-point of column n, group i; 8 bytes per column tile and group.
  *   Total: align256(end of the last region).  Pad bytes are zero.
  */
 size_t w4a16_packed_bytes(int K, int N, int group, int scale_dtype, int has_zp);
@@ -105,9 +107,10 @@ int w4a16_repack(const uint8_t *qweight, const void *scales,
  * Workspace bytes w4a16_gemm (gate_up = 0) or w4a16_gemm_gate_up
  * (gate_up = 1) needs for this shape: fp32 split-K partial sums and
  * arrival counters.  0 when the shape runs without split-K.  The workspace
- * must be zero-filled once after allocation; every call leaves its counters
- * at zero again, so it can be reused by later calls.  Calls that share a
- * workspace must not run concurrently.
+ * must be zero-filled once after allocation; the counters occupy its first
+ * 4096 bytes for every shape and every call leaves them at zero again, so
+ * one workspace (sized for the largest shape) serves calls of any shape.
+ * Calls that share a workspace must not run concurrently.
  */
 size_t w4a16_workspace_bytes(int M, int K, int N, int group, int gate_up);
 

@@ -22,11 +22,12 @@
  *   So lane `lane` of tile (n/16, k/128) owns 16 contiguous bytes; 32-bit
  *   word d of them holds the 8 codes k = 128*kc + 32*d + 8*kq + j of column n,
  *   even j in bits 4*(j/2).., odd j in bits 16 + 4*(j/2)...
- *   Region S (offset align256(K*N/2), N*G*esize bytes): the canonical
- *   scales [N][G], bytes unchanged (a lane that owns column n then reads the
- *   scales of consecutive groups from one contiguous run).
- *   Region Z (only with zero-points; offset align256(end of S),
- *   N*ceil(G/2) bytes): the canonical zero-point rows, bytes unchanged.
+ *   Region S (offset align256(K*N/2), N*G*esize bytes).  Element
+ *   ((n/16) * G + i) * 16 + (n mod 16) holds scales[n][i], bytes unchanged:
+ *   the 16 scales of one column tile and group are contiguous.
+ *   Region Z (only with zero-points; offset align256(end of S), N*G/2
+ *   bytes).  Nibble ((n/16) * G + i) * 16 + (n mod 16), low nibble first,
+ *   holds z[n][i]: 8 bytes per column tile and group.
  *   Total size: align256(end of the last region); pad bytes are zero.
  */
 #include <stddef.h>
@@ -53,7 +54,7 @@ int oracle_packed_layout(int K, int N, int group, int esize, int has_zp,
   size_t so = align256(w_bytes);
   size_t s_end = so + (size_t)N * G * (size_t)esize;
   size_t zo = align256(s_end);
-  size_t end = has_zp ? zo + (size_t)N * ((G + 1) / 2) : s_end;
+  size_t end = has_zp ? zo + (size_t)N * G / 2 : s_end;
   *s_off = so;
   *z_off = has_zp ? zo : 0;
   *total = align256(end);
@@ -101,8 +102,20 @@ int oracle_repack(const uint8_t *qweight, const uint8_t *scales,
       int q = get_nibble(qweight + (long)n * (K / 2), k);
       put_nibble(packed, oracle_weight_nibble_index(K, k, n), q);
     }
-  memcpy(packed + so, scales, (size_t)N * G * esize);
-  if (zeros != NULL) memcpy(packed + zo, zeros, (size_t)N * ((G + 1) / 2));
+  for (int n = 0; n < N; ++n)
+    for (int i = 0; i < G; ++i) {
+      long e = ((long)(n / 16) * G + i) * 16 + (n % 16);
+      memcpy(packed + so + (size_t)e * esize,
+             scales + ((size_t)n * G + i) * esize, (size_t)esize);
+    }
+  if (zeros != NULL) {
+    long zrow = (G + 1) / 2;
+    for (int n = 0; n < N; ++n)
+      for (int i = 0; i < G; ++i) {
+        long e = ((long)(n / 16) * G + i) * 16 + (n % 16);
+        put_nibble(packed + zo, e, get_nibble(zeros + (long)n * zrow, i));
+      }
+  }
   return ORACLE_OK;
 }
 
@@ -120,7 +133,20 @@ int oracle_unrepack(const uint8_t *packed, int K, int N, int group, int esize,
     for (int k = 0; k < K; ++k)
       put_nibble(qweight + (long)n * (K / 2), k,
                  get_nibble(packed, oracle_weight_nibble_index(K, k, n)));
-  memcpy(scales, packed + so, (size_t)N * G * esize);
-  if (has_zp && zeros != NULL) memcpy(zeros, packed + zo, (size_t)N * ((G + 1) / 2));
+  for (int n = 0; n < N; ++n)
+    for (int i = 0; i < G; ++i) {
+      long e = ((long)(n / 16) * G + i) * 16 + (n % 16);
+      memcpy(scales + ((size_t)n * G + i) * esize,
+             packed + so + (size_t)e * esize, (size_t)esize);
+    }
+  if (has_zp && zeros != NULL) {
+    long zrow = (G + 1) / 2;
+    memset(zeros, 0, (size_t)N * (size_t)zrow);
+    for (int n = 0; n < N; ++n)
+      for (int i = 0; i < G; ++i) {
+        long e = ((long)(n / 16) * G + i) * 16 + (n % 16);
+        put_nibble(zeros + (long)n * zrow, i, get_nibble(packed + zo, e));
+      }
+  }
   return ORACLE_OK;
 }

@@ -24,6 +24,12 @@ def to_dev(a):
     return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
+def nan_out(M: int, N: int) -> torch.Tensor:
+    """Output buffer pre-filled with NaN, so an output the kernel never wrote
+    fails the comparison instead of passing on stale memory."""
+    return torch.full((M, N), float("nan"), dtype=torch.float16, device="cuda")
+
+
 def ulp16(x):
     """fp16 unit in the last place at |x| (normal range)."""
     x = np.abs(np.asarray(x, np.float64))

@@ -95,7 +95,7 @@ def test_gemm_validation_statuses(L):
     assert gemm(L, out=FAKE + 8) == _lib.ERR_ALIGN
     assert gemm(L, epi=1, bias=FAKE + 4) == _lib.ERR_ALIGN
     # a shape that needs split-K partials must get a workspace
-    M, K, N, g = 1, 5120, 13824, 128
+    M, K, N, g = 4, 5120, 512, 128   # a narrow grid: the plan splits k across workgroups
     need = L.w4a16_workspace_bytes(M, K, N, g, 0)
     assert need > 0
     assert gemm(L, M=M, K=K, N=N, group=g, ws=None) == _lib.ERR_WORKSPACE
@@ -123,12 +123,14 @@ def test_aux_validation(L):
     assert L.w4a16_probe_copy(FAKE, FAKE + 4, 16, None) == _lib.ERR_ALIGN
 
 
-def test_workspace_is_zero_without_split_and_grows_with_m(L):
-    # large N at M=128 has enough workgroups without split-K
-    assert L.w4a16_workspace_bytes(128, 5120, 13824, 128, 0) == 0
+def test_workspace_only_for_narrow_grids(L):
+    # wide N fills the chip without k splits across workgroups: no workspace
+    for M in (1, 2, 16, 32, 64, 128):
+        assert L.w4a16_workspace_bytes(M, 5120, 13824, 128, 0) == 0
+        assert L.w4a16_workspace_bytes(M, 5120, 13824, 128, 1) == 0
     assert L.w4a16_workspace_bytes(0, 5120, 13824, 128, 0) == 0
-    w1 = L.w4a16_workspace_bytes(1, 5120, 13824, 128, 0)
-    w1g = L.w4a16_workspace_bytes(1, 5120, 13824, 128, 1)
+    w1 = L.w4a16_workspace_bytes(1, 5120, 256, 128, 0)
+    w1g = L.w4a16_workspace_bytes(1, 5120, 256, 128, 1)
     assert 0 < w1 < w1g
 
 

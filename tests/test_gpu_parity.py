@@ -14,7 +14,7 @@ import oracle
 import decode_w4a16_repack_amd as w4
 from decode_w4a16_repack_amd import synth
 
-from gpu_cases import check_close, repack_dev, sample_cols, to_dev
+from gpu_cases import check_close, nan_out, repack_dev, sample_cols, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -35,7 +35,8 @@ def run_gemm(p, **kw):
     A = to_dev(p.A)
     out = w4.gemm(A, w, bias=to_dev(p.bias) if kw.get("epilogue", "none") != "none" else None,
                   gamma=to_dev(p.gamma) if kw.get("rms") else None,
-                  epilogue=kw.get("epilogue", "none"), eps=kw.get("eps", 1e-6))
+                  epilogue=kw.get("epilogue", "none"), eps=kw.get("eps", 1e-6),
+                  out=nan_out(p.M, p.N))
     torch.cuda.synchronize()
     return out.cpu().numpy()
 
@@ -137,8 +138,9 @@ def test_run_to_run_bit_identical(M):
     p = synth.make_problem(M, 5120, 13824, 128, seed=4)
     w = repack_dev(p.w)
     A = to_dev(p.A)
-    y1 = w4.gemm(A, w).clone()
-    y2 = w4.gemm(A, w).clone()
+    y1 = w4.gemm(A, w, out=nan_out(M, p.N))
+    y2 = w4.gemm(A, w, out=nan_out(M, p.N))
+    assert not torch.isnan(y1).any()
     torch.cuda.synchronize()
     assert torch.equal(y1, y2)
 
@@ -169,10 +171,12 @@ def test_unit_scale_integer_case_exact():
 def test_workspace_reuse_across_shapes():
     """Split-K counters must be left at zero: alternate shapes on one workspace."""
     ws = w4.Workspace()
-    cases = [synth.make_problem(M, 5120, 4096, 128, seed=M) for M in (1, 4, 1, 8)]
+    cases = [synth.make_problem(M, K, N, 128, seed=M)
+             for M, K, N in ((1, 5120, 4096), (4, 5120, 4096), (2, 1024, 512),
+                             (1, 5120, 4096), (8, 5120, 4096), (1, 1024, 512))]
     for p in cases:
         w = repack_dev(p.w)
-        got = w4.gemm(to_dev(p.A), w, workspace=ws).cpu().numpy()
+        got = w4.gemm(to_dev(p.A), w, workspace=ws, out=nan_out(p.M, p.N)).cpu().numpy()
         cols = sample_cols(p.N, 64, seed=p.M)
         check_close(got[:, cols], ref_gemm(p, cols=cols), f"reuse M={p.M}")
 
@@ -238,7 +242,8 @@ def test_unfused_passes_exact():
 
 def run_gate_up(p, rms=False):
     wg, wu = repack_dev(p.w), repack_dev(p.w_up)
-    out = w4.gemm_gate_up(to_dev(p.A), wg, wu, gamma=to_dev(p.gamma) if rms else None)
+    out = w4.gemm_gate_up(to_dev(p.A), wg, wu, gamma=to_dev(p.gamma) if rms else None,
+                          out=nan_out(p.M, p.N))
     torch.cuda.synchronize()
     return out.cpu().numpy()
 

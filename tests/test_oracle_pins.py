@@ -324,15 +324,16 @@ def test_repack_round_trip(oracle_lib, sdt, asym, K, N, group):
     assert np.array_equal(s.view(np.uint8), p.w.scales.view(np.uint8))
     if asym:
         assert np.array_equal(z, p.w.zeros)
-    # scale and zero-point regions: the canonical arrays, bytes unchanged
+    # scale and zero-point regions: element (t, i, c) is (n = 16t + c, group i)
     so, zo, total = oracle.packed_layout(K, N, group, np.dtype(sdt).itemsize, asym)
     G = K // group
-    sreg = packed[so: so + N * G * np.dtype(sdt).itemsize]
-    assert np.array_equal(sreg, p.w.scales.view(np.uint8).reshape(-1))
+    sreg = packed[so: so + N * G * np.dtype(sdt).itemsize].view(sdt).reshape(N // 16, G, 16)
+    assert np.array_equal(sreg.transpose(0, 2, 1).reshape(N, G).view(np.uint8),
+                          p.w.scales.view(np.uint8))
     if asym:
-        zb = packed[zo: zo + N * ((G + 1) // 2)]
-        zn = np.stack([zb & 15, zb >> 4], axis=1).reshape(N, -1)[:, :G]
-        assert np.array_equal(zn, p.w.zp)
+        zb = packed[zo: zo + N * G // 2]
+        zn = np.stack([zb & 15, zb >> 4], axis=1).reshape(N // 16, G, 16)
+        assert np.array_equal(zn.transpose(0, 2, 1).reshape(N, G), p.w.zp)
     assert not packed[K * N // 2: so].any()
 
 
