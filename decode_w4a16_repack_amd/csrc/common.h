@@ -31,9 +31,10 @@ constexpr int kNumRingCfgs = 5;
 extern const RingCfg kRingCfgs[kNumRingCfgs];
 
 // Tile configurations of the small-M one-shot kernel: NWC column tiles x NWK
-// k slices per workgroup, at most CW packed k tiles per wavefront.
+// k slices per workgroup, at most CW packed k tiles per wavefront, PD of
+// them in flight.
 struct OneshotCfg {
-  int mt, nwc, nwk, cw;
+  int mt, nwc, nwk, cw, pd;
 };
 constexpr int kNumOneshotCfgs = 3;
 extern const OneshotCfg kOneshotCfgs[kNumOneshotCfgs];

@@ -15,13 +15,22 @@ __device__ __forceinline__ f16x2 as_f16x2(uint32_t v) {
 // 1024 + 16q (bits 4-7); subtracting 1024 + z, or scaling by 1/16 and
 // subtracting 64 + z, leaves the integer q - z in [-15, 15], exact in fp16.
 // zlo = -(1024 + z), zhi = -(64 + z) in both halves.
+// (x & m) | o in one VALU instruction.  Written out because the compiler
+// splits it into v_and + v_or when both constants are literals (GFX9 VOP3
+// encodings take no literal): m goes in an SGPR, o in a VGPR.
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t o) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(m), "v"(o));
+  return r;
+}
+
 __device__ __forceinline__ f16x8 unpack8(uint32_t w, f16x2 zlo, f16x2 zhi) {
   const uint32_t magic = 0x64006400u;  // fp16 1024.0 in both halves
   const uint32_t w8 = w >> 8;
-  const f16x2 t0 = as_f16x2((w & 0x000F000Fu) | magic);   // j = 0, 1
-  const f16x2 t1 = as_f16x2((w & 0x00F000F0u) | magic);   // j = 2, 3 (x16)
-  const f16x2 t2 = as_f16x2((w8 & 0x000F000Fu) | magic);  // j = 4, 5
-  const f16x2 t3 = as_f16x2((w8 & 0x00F000F0u) | magic);  // j = 6, 7 (x16)
+  const f16x2 t0 = as_f16x2(and_or(w, 0x000F000Fu, magic));   // j = 0, 1
+  const f16x2 t1 = as_f16x2(and_or(w, 0x00F000F0u, magic));   // j = 2, 3 (x16)
+  const f16x2 t2 = as_f16x2(and_or(w8, 0x000F000Fu, magic));  // j = 4, 5
+  const f16x2 t3 = as_f16x2(and_or(w8, 0x00F000F0u, magic));  // j = 6, 7 (x16)
   const f16x2 sixteenth = {(f16)0.0625f, (f16)0.0625f};
   const f16x2 h0 = t0 + zlo;
   const f16x2 h1 = t1 * sixteenth + zhi;

@@ -27,9 +27,10 @@ namespace w4a16 {
 
 namespace {
 
-template <int MT, int NWC, int NWK, int CW, int G, bool SF32, bool GU>
+template <int MT, int NWC, int NWK, int CW, int PD, int G, bool SF32, bool GU>
 __global__ void __launch_bounds__(64 * NWC * NWK)
 oneshot_kernel(const GemmArgs p) {
+  static_assert(PD >= 1 && PD <= CW, "prefetch depth");
   constexpr int NWAVE = NWC * NWK;
   constexpr int NT = 64 * NWAVE;
   constexpr int NW = GU ? 2 : 1;
@@ -134,24 +135,29 @@ oneshot_kernel(const GemmArgs p) {
     }
   }
 
-  // 3'. every weight tile of this wavefront (CW loads per stream, unconditional)
+  // 3'. the first PD weight tiles of this wavefront (one 16-byte load per
+  //     lane per tile and stream, unconditional: tail tiles re-read a valid
+  //     tile); tile j + PD is issued when tile j is contracted, so each
+  //     wavefront keeps PD tiles in flight and its arithmetic follows its
+  //     own arrivals instead of bunching up after the whole stream.
   const uint8_t *wbase[NW];
 #pragma unroll
   for (int i = 0; i < NW; ++i)
     wbase[i] = p.w[i] + (size_t)ctc * KC * kTileBytes + (size_t)lane * 16;
   u32x4 wv[NW][CW];
-#pragma unroll
-  for (int j = 0; j < CW; ++j) {
+  auto issue_tile = [&](int j) __attribute__((always_inline)) {
     const int kc = min(my_kb + min(j, max(my_n - 1, 0)), KC - 1);
 #pragma unroll
     for (int i = 0; i < NW; ++i)
       wv[i][j] = *reinterpret_cast<const u32x4 *>(wbase[i] + (size_t)kc * kTileBytes);
-  }
+  };
+#pragma unroll
+  for (int j = 0; j < PD; ++j) issue_tile(j);
 
-  // 3. the copies into LDS (issued before the CW tiles) have landed; with
+  // 3. the copies into LDS (issued before the PD tiles) have landed; with
   //    more than 63 loads in flight the issue itself waited, which already
   //    retired the copies (completion is in issue order)
-  wait_vmcnt<(CW * LOADS_PER_TILE < 63 ? CW * LOADS_PER_TILE : 63)>();
+  wait_vmcnt<(PD * LOADS_PER_TILE < 63 ? PD * LOADS_PER_TILE : 63)>();
   lds_barrier();
 
   // 4. RMSNorm prologue: per-row sums of squares (fixed order), x * gamma
@@ -204,6 +210,7 @@ oneshot_kernel(const GemmArgs p) {
   if (active) {
 #pragma unroll
     for (int j = 0; j < CW; ++j) {
+      if (j + PD < CW) issue_tile(j + PD);
       if (j < my_n) {
         const int gi0 = (wk * cpw + j) * GPC;  // first group of tile j, split-relative
         const uint8_t *a_lane[MT];
@@ -341,9 +348,9 @@ oneshot_kernel(const GemmArgs p) {
     }
 }
 
-template <int MT, int NWC, int NWK, int CW, int G, bool SF32, bool GU>
+template <int MT, int NWC, int NWK, int CW, int PD, int G, bool SF32, bool GU>
 hipError_t launch_t(const GemmArgs &a, const Plan &pl, hipStream_t stream) {
-  auto kern = oneshot_kernel<MT, NWC, NWK, CW, G, SF32, GU>;
+  auto kern = oneshot_kernel<MT, NWC, NWK, CW, PD, G, SF32, GU>;
   // Raise the kernel's dynamic-LDS limit when a plan needs more than the
   // default 64 KiB; only the first launch that needs a larger size makes the
   // attribute call, so repeated launches (also under stream capture) make none.
@@ -363,39 +370,39 @@ hipError_t launch_t(const GemmArgs &a, const Plan &pl, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int MT, int NWC, int NWK, int CW, int G>
+template <int MT, int NWC, int NWK, int CW, int PD, int G>
 hipError_t launch_g(const GemmArgs &a, const Plan &pl, bool sf32, bool gu, hipStream_t st) {
-  if (sf32) return gu ? launch_t<MT, NWC, NWK, CW, G, true, true>(a, pl, st)
-                      : launch_t<MT, NWC, NWK, CW, G, true, false>(a, pl, st);
-  return gu ? launch_t<MT, NWC, NWK, CW, G, false, true>(a, pl, st)
-            : launch_t<MT, NWC, NWK, CW, G, false, false>(a, pl, st);
+  if (sf32) return gu ? launch_t<MT, NWC, NWK, CW, PD, G, true, true>(a, pl, st)
+                      : launch_t<MT, NWC, NWK, CW, PD, G, true, false>(a, pl, st);
+  return gu ? launch_t<MT, NWC, NWK, CW, PD, G, false, true>(a, pl, st)
+            : launch_t<MT, NWC, NWK, CW, PD, G, false, false>(a, pl, st);
 }
 
-template <int MT, int NWC, int NWK, int CW>
+template <int MT, int NWC, int NWK, int CW, int PD>
 hipError_t launch_c(const GemmArgs &a, const Plan &pl, int group, bool sf32, bool gu,
                     hipStream_t st) {
   switch (group) {
-    case 16: return launch_g<MT, NWC, NWK, CW, 16>(a, pl, sf32, gu, st);
-    case 32: return launch_g<MT, NWC, NWK, CW, 32>(a, pl, sf32, gu, st);
-    case 64: return launch_g<MT, NWC, NWK, CW, 64>(a, pl, sf32, gu, st);
-    default: return launch_g<MT, NWC, NWK, CW, 128>(a, pl, sf32, gu, st);
+    case 16: return launch_g<MT, NWC, NWK, CW, PD, 16>(a, pl, sf32, gu, st);
+    case 32: return launch_g<MT, NWC, NWK, CW, PD, 32>(a, pl, sf32, gu, st);
+    case 64: return launch_g<MT, NWC, NWK, CW, PD, 64>(a, pl, sf32, gu, st);
+    default: return launch_g<MT, NWC, NWK, CW, PD, 128>(a, pl, sf32, gu, st);
   }
 }
 
 }  // namespace
 
 const OneshotCfg kOneshotCfgs[kNumOneshotCfgs] = {
-    {1, 1, 4, 10},  // 0: M <= 16, one column tile, four k slices, <= 10 tiles each
-    {1, 1, 8, 10},  // 1: eight k slices (512 threads) for narrow N / long K
-    {1, 2, 2, 10},  // 2: two column tiles share the activations
+    {1, 1, 4, 10, 2},  // 0: M <= 16, one column tile, four k slices, <= 10 tiles each
+    {1, 1, 8, 10, 2},  // 1: eight k slices (512 threads) for narrow N / long K
+    {1, 2, 2, 10, 2},  // 2: two column tiles share the activations
 };
 
 hipError_t launch_oneshot(const GemmArgs &a, const Plan &pl, int group, bool scale_f32,
                           bool gate_up, hipStream_t stream) {
   switch (pl.cfg) {
-    case 0: return launch_c<1, 1, 4, 10>(a, pl, group, scale_f32, gate_up, stream);
-    case 1: return launch_c<1, 1, 8, 10>(a, pl, group, scale_f32, gate_up, stream);
-    default: return launch_c<1, 2, 2, 10>(a, pl, group, scale_f32, gate_up, stream);
+    case 0: return launch_c<1, 1, 4, 10, 2>(a, pl, group, scale_f32, gate_up, stream);
+    case 1: return launch_c<1, 1, 8, 10, 2>(a, pl, group, scale_f32, gate_up, stream);
+    default: return launch_c<1, 2, 2, 10, 2>(a, pl, group, scale_f32, gate_up, stream);
   }
 }
 
