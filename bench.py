@@ -12,7 +12,16 @@ the fraction of the HBM and fp16-MFMA peaks; a streaming-read probe of the
 achievable HBM rate; and the CPU oracle timed on the host's cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
-                       [--profile-kernel M]   (launch only that M, for rocprofv3)
+                       [--profile-kernel M [--eager]]
+                       [--traffic-summary FETCH_DIR WRITE_DIR]
+
+--profile-kernel M launches only the GEMM at M (graph-replayed, or eagerly
+with --eager, the form for rocprofv3 --pmc runs) and then a plain 256 MiB copy
+whose FETCH_SIZE / WRITE_SIZE readings calibrate those counters.
+--traffic-summary reads the counter CSVs of a FETCH_SIZE run and a WRITE_SIZE
+run of that command and writes the per-launch HBM traffic to
+profiles/traffic_gemv_m1.json (taken into `roofline.traffic` while the kernel
+sources are unchanged).
 """
 from __future__ import annotations
 
@@ -36,7 +45,9 @@ MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, published
 INFINITY_CACHE = 256 << 20
 PAGE_M1_US = 69.5  # the pages' M=1 time for this shape (H200, context only)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemv_m1.json")
-KERNEL_SOURCES = ["decode_w4a16_repack_amd/csrc/ring.hip", "decode_w4a16_repack_amd/csrc/device.h", "decode_w4a16_repack_amd/csrc/gemm.hip", "decode_w4a16_repack_amd/csrc/common.h"]
+KERNEL_SOURCES = ["decode_w4a16_repack_amd/csrc/" + f for f in
+                  ("oneshot.hip", "ring.hip", "device.h", "gemm.hip", "common.h")]
+COPY_PROBE_BYTES = 256 << 20  # plain copy of known size, counter calibration
 
 
 def algorithmic_bytes(M, K=K, N=N, group=GROUP, scale_bytes=2, has_zp=True, n_weights=1):
@@ -182,7 +193,7 @@ def cpu_baseline(budget_s=12.0):
         t0 = time.perf_counter()
         oracle.gemm(p.A, p.w.qweight, p.w.scales, p.w.zeros, GROUP, N)
         times.append(time.perf_counter() - t0)
-        if time.perf_counter() - t_start > budget_s or len(times) >= 50:
+        if time.perf_counter() - t_start > budget_s or len(times) >= 400:
             break
     t = float(np.median(times))
     cores = int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count() or 1)
@@ -205,6 +216,51 @@ def load_traffic():
     return t.get("bytes_per_launch")
 
 
+def _counter_rows(d, counter):
+    """{kernel name: [per-dispatch value]} from the rocprofv3 counter CSVs
+    under directory d (values of one dispatch summed over their instances)."""
+    import csv
+    import glob
+    per = {}
+    for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(path, newline="") as f:
+            for row in csv.DictReader(f):
+                if row.get("Counter_Name") != counter:
+                    continue
+                key = (row["Kernel_Name"], row.get("Dispatch_Id") or row.get("Correlation_Id"))
+                per[key] = per.get(key, 0.0) + float(row["Counter_Value"])
+    out = {}
+    for (name, _), v in per.items():
+        out.setdefault(name, []).append(v)
+    return out
+
+
+def traffic_summary(fetch_dir, write_dir):
+    """HBM bytes per GEMM launch: FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch), each scaled by what the counter reads for the plain copy of
+    COPY_PROBE_BYTES in the same run."""
+    res = {"kernel_source_hash": kernel_source_hash(), "copy_probe_bytes": COPY_PROBE_BYTES}
+    total = 0.0
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = _counter_rows(d, counter)
+        gemm = [n for n in rows if "oneshot_kernel" in n or "ring_kernel" in n]
+        copy = [n for n in rows if "probe_copy_kernel" in n]
+        if len(gemm) != 1 or len(copy) != 1:
+            raise SystemExit(f"{counter}: expected one GEMM and one copy kernel, got {sorted(rows)}")
+        g, c = float(np.median(rows[gemm[0]])), float(np.median(rows[copy[0]]))
+        factor = COPY_PROBE_BYTES / (c * 1024.0)
+        byts = g * 1024.0 * factor
+        total += byts
+        res[counter] = {"gemm_kib_per_dispatch": g, "copy_kib_per_dispatch": c,
+                        "scale_factor": factor, "bytes_per_launch": byts,
+                        "dispatches": len(rows[gemm[0]]), "kernel": gemm[0]}
+    res["bytes_per_launch"] = total
+    res["algorithmic_bytes_per_launch"] = algorithmic_bytes(1)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(res, f, indent=1)
+    print(json.dumps(res, indent=1))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -214,7 +270,13 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--profile-kernel", type=int, default=0,
                     help="only launch the GEMM at this M (for rocprofv3)")
+    ap.add_argument("--eager", action="store_true",
+                    help="with --profile-kernel: eager launches, no graph")
+    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     args = ap.parse_args()
+    if args.traffic_summary:
+        traffic_summary(*args.traffic_summary)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(this build has no multi-GPU path).", file=sys.stderr)
@@ -229,8 +291,24 @@ def main():
     if args.profile_kernel:
         M = args.profile_kernel
         sets = InputSets(M, rotations_needed(M))
-        us, _, n = time_calls(sets, args.steps, args.warmup, ws)
-        log(f"profile M={M}: {us:.2f} us per call over {n} graph-replayed calls")
+        if args.eager:
+            R = len(sets.sets)
+            for i in range(args.warmup + args.steps):
+                A, pw, out = sets.sets[i % R]
+                w4.gemm(A, pw, out=out, workspace=ws)
+            torch.cuda.synchronize()
+            log(f"profile M={M}: {args.warmup + args.steps} eager calls")
+        else:
+            us, _, n = time_calls(sets, args.steps, args.warmup, ws)
+            log(f"profile M={M}: {us:.2f} us per call over {n} graph-replayed calls")
+        del sets
+        torch.cuda.empty_cache()
+        src = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device="cuda").fill_(3)
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            w4.probe_copy(src, dst)
+        torch.cuda.synchronize()
+        log(f"profile: 4 copies of {COPY_PROBE_BYTES} bytes")
         return
 
     # headline: M = 1
