@@ -39,6 +39,15 @@ struct OneshotCfg {
 constexpr int kNumOneshotCfgs = 3;
 extern const OneshotCfg kOneshotCfgs[kNumOneshotCfgs];
 
+// Tile configurations of the small-M stream kernel: CPW 16-column tiles per
+// wavefront, KPW 128-k tiles per wavefront (its activation fragments stay in
+// registers), NWK wavefronts (k slices) per workgroup, PD tiles in flight.
+struct StreamCfg {
+  int cpw, kpw, nwk, pd;
+};
+constexpr int kNumStreamCfgs = 3;
+extern const StreamCfg kStreamCfgs[kNumStreamCfgs];
+
 inline size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 
 // Byte offsets of the packed regions (layout version 1).
@@ -87,8 +96,10 @@ struct GemmArgs {
 };
 
 // Launch plan of one GEMM call, a pure function of the shape.
+enum PlanKind { kKindRing = 0, kKindOneshot = 1, kKindStream = 2 };
+
 struct Plan {
-  int oneshot;  // 1: oneshot.hip kernel (kOneshotCfgs), 0: ring.hip kernel (kRingCfgs)
+  int kind;     // PlanKind: ring.hip (kRingCfgs), oneshot.hip (kOneshotCfgs), stream.hip (kStreamCfgs)
   int cfg;      // index into the kernel's configuration table
   int gx, gy, gz;
   int split, cps;
@@ -98,13 +109,16 @@ struct Plan {
   size_t ws_part_off, ws_rms_off, ws_cnt_off, ws_total;
 };
 
-// force_kind: -1 automatic, 0 ring kernel, 1 one-shot kernel; force_cfg < 0 /
+// force_kind: -1 automatic, else a PlanKind; force_cfg < 0 /
 // force_split <= 0 select the built-in choice.
 Plan make_plan(int M, int K, int N, int group, int scale_bytes, bool gate_up,
                int force_kind = -1, int force_cfg = -1, int force_split = 0);
 
 hipError_t launch_oneshot(const GemmArgs &a, const Plan &p, int group, bool scale_f32,
                           bool gate_up, hipStream_t stream);
+
+hipError_t launch_stream(const GemmArgs &a, const Plan &p, int group, bool scale_f32,
+                         bool gate_up, hipStream_t stream);
 
 hipError_t launch_ring(const GemmArgs &a, const Plan &p, int group, bool scale_f32,
                        bool gate_up, hipStream_t stream);

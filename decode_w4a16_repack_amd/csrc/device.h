@@ -64,27 +64,17 @@ __device__ __forceinline__ float silu(float v) { return v / (1.0f + expf(-v)); }
 // Contract one packed k tile (128 k, four 32-deep MFMA steps) of one 16-column
 // weight tile with MT 16-row m tiles of activations and add the scaled group
 // sums into acc.
-//  * a_lane[t]: this lane's 16-byte activation slot of step 0 for m tile t;
-//    step d is d * dstride bytes further.  The tile is in fragment order
-//    (slot ((d * 4 + kq) * R + row)), so the 16 rows one MFMA operand reads
-//    are 16 consecutive slots.  Lanes whose row is beyond M point at a valid
-//    row instead: an A row only feeds its own output row, never written.
+//  * a[d][t]: this lane's activation fragment of 32-k step d for m tile t
+//    (row l%16 of the tile, k slots 8*(l/16)..+7 of the step).
 //  * zp_of(gl) / scale_of(gl): zero-point (0..15) / scale of group gl
 //    (0 .. 128/G - 1) of the tile for this lane's column; each is asked for
 //    once per group.
 template <int MT, int G, class ZpOf, class ScaleOf>
-__device__ __forceinline__ void contract_tile_frag(f32x4 (&acc)[MT], const u32x4 &w,
-                                                   const uint8_t *const (&a_lane)[MT],
-                                                   int dstride, int kq, ZpOf zp_of,
-                                                   ScaleOf scale_of) {
+__device__ __forceinline__ void contract_tile(f32x4 (&acc)[MT], const u32x4 &w,
+                                              const f16x8 (&a)[4][MT], int kq, ZpOf zp_of,
+                                              ScaleOf scale_of) {
   constexpr int GPC = 128 / G;
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
-  f16x8 a[4][MT];
-#pragma unroll
-  for (int d = 0; d < 4; ++d)
-#pragma unroll
-    for (int t = 0; t < MT; ++t)
-      a[d][t] = *reinterpret_cast<const f16x8 *>(a_lane[t] + d * dstride);
   // zero-point constants of this lane's B slots (one group per 32-k step
   // for G >= 32; for G = 16 the slot's group is 2d + kq/2)
   f16x2 zlo[4], zhi[4];
@@ -136,6 +126,26 @@ __device__ __forceinline__ void contract_tile_frag(f32x4 (&acc)[MT], const u32x4
       }
     }
   }
+}
+
+// contract_tile with the activation fragments read from LDS:
+//  * a_lane[t]: this lane's 16-byte activation slot of step 0 for m tile t;
+//    step d is d * dstride bytes further.  The tile is in fragment order
+//    (slot ((d * 4 + kq) * R + row)), so the 16 rows one MFMA operand reads
+//    are 16 consecutive slots.  Lanes whose row is beyond M point at a valid
+//    row instead: an A row only feeds its own output row, never written.
+template <int MT, int G, class ZpOf, class ScaleOf>
+__device__ __forceinline__ void contract_tile_frag(f32x4 (&acc)[MT], const u32x4 &w,
+                                                   const uint8_t *const (&a_lane)[MT],
+                                                   int dstride, int kq, ZpOf zp_of,
+                                                   ScaleOf scale_of) {
+  f16x8 a[4][MT];
+#pragma unroll
+  for (int d = 0; d < 4; ++d)
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+      a[d][t] = *reinterpret_cast<const f16x8 *>(a_lane[t] + d * dstride);
+  contract_tile<MT, G>(acc, w, a, kq, zp_of, scale_of);
 }
 
 // Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4):

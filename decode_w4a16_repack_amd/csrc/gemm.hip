@@ -1,4 +1,5 @@
-// Launch planning for the fused W4A16 GEMM (kernels in ring.hip).
+// Launch planning for the fused W4A16 GEMM (kernels in stream.hip for
+// M <= 16, ring.hip above).
 //
 // The plan is a pure function of the shape: it picks the tile configuration,
 // the grid and, only for grids too small to fill the chip, a k split across
@@ -75,7 +76,7 @@ bool plan_oneshot(Plan &p, int M, int K, int N, int group, int scale_bytes, bool
   const int KC = K / kTileK;
   const int NW = gate_up ? 2 : 1;
   if (M > 16) return false;
-  p.oneshot = 1;
+  p.kind = kKindOneshot;
   p.cfg = (force_cfg >= 0 && force_cfg < kNumOneshotCfgs) ? force_cfg : (NTL >= 512 ? 0 : 1);
   const OneshotCfg c = kOneshotCfgs[p.cfg];
   const int nwave = c.nwc * c.nwk;
@@ -106,22 +107,67 @@ bool plan_oneshot(Plan &p, int M, int K, int N, int group, int scale_bytes, bool
   return true;
 }
 
+// Stream kernel plan (M <= 16): as many column tiles per wavefront as keep
+// the grid at >= 200 workgroups; k split across workgroups only when the
+// k range exceeds the workgroup's NWK x KPW tiles or the grid is short of
+// wavefronts.
+bool plan_stream(Plan &p, int M, int K, int N, int group, int scale_bytes, bool gate_up,
+                 int force_cfg, int force_split) {
+  const int NTL = N / kTileN;
+  const int KC = K / kTileK;
+  const int NW = gate_up ? 2 : 1;
+  if (M > 16) return false;
+  p.kind = kKindStream;
+  if (force_cfg >= 0 && force_cfg < kNumStreamCfgs) {
+    p.cfg = force_cfg;
+  } else {
+    p.cfg = kNumStreamCfgs - 1;
+    for (int i = 0; i < kNumStreamCfgs; ++i)
+      if ((NTL + kStreamCfgs[i].cpw - 1) / kStreamCfgs[i].cpw >= 200) { p.cfg = i; break; }
+  }
+  const StreamCfg c = kStreamCfgs[p.cfg];
+  const int per_wg = c.nwk * c.kpw;  // k tiles one workgroup covers
+  p.gx = (NTL + c.cpw - 1) / c.cpw;
+  p.gz = 1;
+  const int base = p.gx * p.gz;
+  int S = choose_split(base, c.nwk, KC, 1, force_split);
+  const int s_min = (KC + per_wg - 1) / per_wg;
+  if (S < s_min) S = s_min;
+  if (S > KC) S = KC;
+  if (S > 1 && base >= kMaxSplitBlocks) return false;  // arrival counters are per workgroup
+  p.cps = (KC + S - 1) / S;
+  p.split = (KC + p.cps - 1) / p.cps;
+  p.gy = p.split;
+  p.rows_pow2 = 16;
+  const size_t red = (size_t)c.nwk * NW * c.cpw * 4 * 64 * 4;
+  p.lds_g = 0;
+  size_t off = plan_meta_lds(p, align16(red), group, scale_bytes, c.cpw, NW);
+  p.lds_r = (int)off;
+  p.lds_bytes = off + (size_t)(64 * c.nwk + 16) * 4;
+  plan_workspace(p, M, N, base, NW);
+  return true;
+}
+
 }  // namespace
 
 Plan make_plan(int M, int K, int N, int group, int scale_bytes, bool gate_up, int force_kind,
                int force_cfg, int force_split) {
   Plan p{};
-  if (force_kind != 0) {
+  if (force_kind == kKindOneshot) {
     Plan q{};
-    if (plan_oneshot(q, M, K, N, group, scale_bytes, gate_up, force_kind == 1 ? force_cfg : -1,
-                     force_kind == 1 ? force_split : 0))
+    if (plan_oneshot(q, M, K, N, group, scale_bytes, gate_up, force_cfg, force_split)) return q;
+  } else if (force_kind == kKindStream || force_kind < 0) {
+    Plan q{};
+    if (plan_stream(q, M, K, N, group, scale_bytes, gate_up,
+                    force_kind == kKindStream ? force_cfg : -1,
+                    force_kind == kKindStream ? force_split : 0))
       return q;
   }
   const int NTL = N / kTileN;
   const int KC = K / kTileK;
   const int NW = gate_up ? 2 : 1;
-  p.oneshot = 0;
-  if (force_cfg >= 0 && force_cfg < kNumRingCfgs) {
+  p.kind = kKindRing;
+  if (force_kind == kKindRing && force_cfg >= 0 && force_cfg < kNumRingCfgs) {
     p.cfg = force_cfg;
   } else if (M <= 16) {
     p.cfg = NTL >= 512 ? 0 : 2;
@@ -154,8 +200,11 @@ Plan make_plan(int M, int K, int N, int group, int scale_bytes, bool gate_up, in
 
 hipError_t launch_gemm(const GemmArgs &a, const Plan &pl, int group,
                        bool scale_f32, bool gate_up, hipStream_t stream) {
-  if (pl.oneshot) return launch_oneshot(a, pl, group, scale_f32, gate_up, stream);
-  return launch_ring(a, pl, group, scale_f32, gate_up, stream);
+  switch (pl.kind) {
+    case kKindStream: return launch_stream(a, pl, group, scale_f32, gate_up, stream);
+    case kKindOneshot: return launch_oneshot(a, pl, group, scale_f32, gate_up, stream);
+    default: return launch_ring(a, pl, group, scale_f32, gate_up, stream);
+  }
 }
 
 }  // namespace w4a16
