@@ -105,6 +105,7 @@ struct Plan {
   int split, cps;
   int rows_pow2;
   int lds_g, lds_s, lds_z, gr, lds_r;
+  int alds;  // stream kernel: activation rows staged through LDS
   size_t lds_bytes;
   size_t ws_part_off, ws_rms_off, ws_cnt_off, ws_total;
 };

@@ -46,9 +46,11 @@ __device__ __forceinline__ f16x8 unpack8(uint32_t w, f16x2 zlo, f16x2 zhi) {
 // built from their bit patterns: 1024 + z has exponent field 25 and
 // mantissa z (0x6400 | z); 64 + z has exponent field 21 and mantissa 16z
 // (0x5400 | z << 4); the sign bit makes them negative.
+// (The OR of disjoint bit fields is written as an add so that each constant
+// is one multiply-add.)
 __device__ __forceinline__ void zero_consts(uint32_t z, f16x2 &zlo, f16x2 &zhi) {
-  zlo = as_f16x2(0xE400E400u | (z * 0x00010001u));
-  zhi = as_f16x2(0xD400D400u | (z * 0x00100010u));
+  zlo = as_f16x2(z * 0x00010001u + 0xE400E400u);
+  zhi = as_f16x2(z * 0x00100010u + 0xD400D400u);
 }
 
 // D = A(16x32 fp16) x B(32x16 fp16) + C, fp32.  Lane l supplies A row l%16 and
@@ -103,7 +105,9 @@ __device__ __forceinline__ void contract_tile(f32x4 (&acc)[MT], const u32x4 &w,
       if ((d + 1) % SPG == 0) {
         const float s = scale_of((32 * d) / G);
 #pragma unroll
-        for (int t = 0; t < MT; ++t) acc[t] += accg[t] * s;
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[t][e] = __builtin_fmaf(accg[t][e], s, acc[t][e]);
       }
     }
   } else {
@@ -121,8 +125,9 @@ __device__ __forceinline__ void contract_tile(f32x4 (&acc)[MT], const u32x4 &w,
       for (int t = 0; t < MT; ++t) {
         const f32x4 p0 = mfma16(a[d][t], blo, zero4);
         const f32x4 p1 = mfma16(a[d][t], bhi, zero4);
-        acc[t] += p0 * s0;
-        acc[t] += p1 * s1;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          acc[t][e] = __builtin_fmaf(p1[e], s1, __builtin_fmaf(p0[e], s0, acc[t][e]));
       }
     }
   }

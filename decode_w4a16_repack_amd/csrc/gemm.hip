@@ -110,7 +110,9 @@ bool plan_oneshot(Plan &p, int M, int K, int N, int group, int scale_bytes, bool
 // Stream kernel plan (M <= 16): as many column tiles per wavefront as keep
 // the grid at >= 200 workgroups; k split across workgroups only when the
 // k range exceeds the workgroup's NWK x KPW tiles or the grid is short of
-// wavefronts.
+// wavefronts.  Each wavefront has a private LDS region: its slice's scales
+// and zero-points, for M <= 8 its activation rows, and at the end its
+// partial sums.
 bool plan_stream(Plan &p, int M, int K, int N, int group, int scale_bytes, bool gate_up,
                  int force_cfg, int force_split) {
   const int NTL = N / kTileN;
@@ -134,17 +136,45 @@ bool plan_stream(Plan &p, int M, int K, int N, int group, int scale_bytes, bool 
   const int s_min = (KC + per_wg - 1) / per_wg;
   if (S < s_min) S = s_min;
   if (S > KC) S = KC;
-  if (S > 1 && base >= kMaxSplitBlocks) return false;  // arrival counters are per workgroup
+  if (S > 1 && NTL * p.gz > kMaxSplitBlocks) return false;  // one arrival counter per column tile
   p.cps = (KC + S - 1) / S;
   p.split = (KC + p.cps - 1) / p.cps;
   p.gy = p.split;
-  p.rows_pow2 = 16;
-  const size_t red = (size_t)c.nwk * NW * c.cpw * 4 * 64 * 4;
-  p.lds_g = 0;
-  size_t off = plan_meta_lds(p, align16(red), group, scale_bytes, c.cpw, NW);
-  p.lds_r = (int)off;
-  p.lds_bytes = off + (size_t)(64 * c.nwk + 16) * 4;
-  plan_workspace(p, M, N, base, NW);
+  // private region of one wavefront
+  const int gpw = c.kpw * (kTileK / group);
+  const size_t ms = (size_t)c.cpw * gpw * 16 * scale_bytes;
+  const size_t mz = align16((size_t)c.cpw * gpw * 8);
+  const size_t meta = NW * (ms + mz);
+  const size_t red = (size_t)NW * c.cpw * 1024;
+  p.rows_pow2 = pow2_at_least(M);
+  const size_t a_lds = (size_t)c.kpw * 256 * p.rows_pow2;
+  const size_t limit = 160 * 1024;
+  p.alds = 0;
+  size_t region = align16(meta > red ? meta : red);
+  if (M <= 8) {
+    const size_t with_a = align16(meta + a_lds > red ? meta + a_lds : red);
+    if ((size_t)c.nwk * with_a + (size_t)c.nwk * 64 <= limit) {
+      p.alds = 1;
+      region = with_a;
+    }
+  }
+  if ((size_t)c.nwk * region + (size_t)c.nwk * 64 > limit) return false;
+  p.lds_s = (int)region;
+  p.lds_r = (int)(c.nwk * region);
+  p.lds_bytes = (size_t)p.lds_r + (size_t)c.nwk * 16 * 4;
+  p.lds_g = p.lds_z = p.gr = 0;
+  // workspace: arrival counters (one per column tile), row sums of squares
+  // [column tile][S][16], partial sums [S][NW][M][N]
+  size_t off = 0;
+  if (p.split > 1) {
+    p.ws_cnt_off = 0;
+    off = align256((size_t)kMaxSplitBlocks * 4);
+    p.ws_rms_off = off;
+    off = align256(off + (size_t)NTL * p.gz * p.split * 16 * 4);
+    p.ws_part_off = off;
+    off = align256(off + (size_t)p.split * NW * M * N * 4);
+  }
+  p.ws_total = off;
   return true;
 }
 

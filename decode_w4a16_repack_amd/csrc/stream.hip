@@ -18,38 +18,48 @@
 //    across workgroups, which only narrow or very deep shapes need);
 //  * each lane keeps its activation fragments for the wavefront's k slice in
 //    registers for the whole kernel (row l%16, k slots 8*(l/16)..+7 of every
-//    32-k step: one 16-byte global load each), so the CPW column tiles reuse
-//    them and no activation staging, LDS traffic or barrier sits in the loop;
+//    32-k step), so the CPW column tiles reuse them and no activation
+//    traffic or barrier sits in the loop;
 //  * the wavefront streams its CPW x KPW weight tiles (one 16-byte load per
 //    lane per 1 KiB tile), PD tiles ahead of the contraction, k tile outer
 //    and column tile inner so consecutive MFMA chains are independent;
-//  * scales and zero-points of the workgroup's column tiles are contiguous
-//    runs in the packed layout, copied into LDS with direct global-to-LDS
-//    loads before the stream starts;
-//  * wavefront c < CPW finishes column tile c: slice sum, RMSNorm factor,
-//    epilogue, one fp16 write.
+//  * each wavefront copies the scales and zero-points of its slice (runs of
+//    the packed layout) into a private LDS region with direct global-to-LDS
+//    loads, and for M <= 8 also its activation rows (unique data, then read
+//    back as fragments); nothing is shared between wavefronts until the
+//    final reduction, so the only barrier is the one before it;
+//  * the slice partial sums go through the same private regions; wavefront
+//    c < CPW finishes column tile c: slice sum in slice order, RMSNorm
+//    factor, epilogue, one fp16 write.
 #include "device.h"
 
 namespace w4a16 {
 
 namespace {
 
-template <int CPW, int KPW, int NWK, int PD, int G, bool SF32, bool GU>
+template <int CPW, int KPW, int NWK, int PD, bool ALDS, int G, bool SF32, bool GU>
 __global__ void __launch_bounds__(64 * NWK)
 stream_kernel(const GemmArgs p) {
   static_assert(CPW <= NWK, "one finishing wavefront per column tile");
   static_assert(PD >= 1 && PD <= CPW * KPW, "prefetch depth");
-  constexpr int NT = 64 * NWK;
   constexpr int NW = GU ? 2 : 1;
+  // tiles in flight: gate_up loads two per tile, so half as many tiles
+  constexpr int PDE = GU ? (PD + 1) / 2 : PD;
   constexpr int GPC = 128 / G;
   constexpr int SB = SF32 ? 4 : 2;
   constexpr int NTILE = CPW * KPW;
-  // loads issued after the metadata copies that may still be in flight at
-  // the first barrier: the activation fragments and the first PD tiles
-  constexpr int AFTER_COPIES = 4 * KPW + PD * NW;
+  constexpr int GPW = KPW * GPC;                 // groups of one wavefront's k slice
+  constexpr int MS_BYTES = CPW * GPW * 16 * SB;  // its scales, [CPW][GPW][16]
+  constexpr int MZ_BYTES = CPW * GPW * 8;        // its zero-points, [CPW][GPW][8 bytes]
+  constexpr int MZ_PAD = (MZ_BYTES + 15) / 16 * 16;
+  constexpr int SU = GPW * SB;                   // 16-byte scale units per column tile
+  constexpr int ZU = GPW * 2;                    // 4-byte zero-point units per column tile
+  // loads issued after the direct-to-LDS copies that may still be in
+  // flight when the copies are waited for: the register activation
+  // fragments (unless they come through LDS) and the first PD tiles
+  constexpr int AFTER_COPIES = (ALDS ? 0 : 4 * KPW) + PDE * NW;
 
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  __shared__ int is_last;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -70,54 +80,80 @@ stream_kernel(const GemmArgs p) {
   const bool has_zp = p.has_zp != 0;
   const int kq = lane >> 4;
   const int c = lane & 15;
+  const int R = p.rows_pow2;  // activation rows staged in LDS (ALDS)
 
-  // LDS: scales and zero-points [NW][CPW] runs, slice partial sums, sums of
-  // squares.
-  const int GRC = p.gr;  // staged groups per column tile (capacity)
-  const int scopy = (GRC * 16 * SB + 1023) / 1024 * 1024;
-  const int zcopy = (GRC * 8 + 255) / 256 * 256;
-  uint8_t *lS = smem + p.lds_s;
-  uint8_t *lZ = smem + p.lds_z;
-  float *lRed = reinterpret_cast<float *>(smem);            // [NWK][NW*CPW][4][64]
-  float *lRms = reinterpret_cast<float *>(smem + p.lds_r);  // [NWK][64] + [16]
-  float *lRow = lRms + NT;
+  // LDS: one private region per wavefront (its scales, zero-points and,
+  // with ALDS, activation slots; reused for its partial sums at the end),
+  // then the per-slice row sums of squares.  No region is shared before
+  // the final reduction, so nothing waits for another wavefront until then.
+  uint8_t *region = smem + wk * p.lds_s;
+  uint8_t *ms = region;                   // [NW] x MS_BYTES
+  uint8_t *mz = region + NW * MS_BYTES;   // [NW] x MZ_PAD
+  uint8_t *aslots = mz + NW * MZ_PAD;     // ALDS: KPW * 16 * R slots of 16 bytes
+  float *lRms = reinterpret_cast<float *>(smem + p.lds_r);  // [NWK][16]
 
-  // 1. scales and zero-points of the column tiles over the workgroup's
-  //    groups: contiguous runs in the packed layout, copied straight to LDS
-  const int gb = kb * GPC;
-  const int ngr = nkc * GPC;
+  // 1. this slice's scales and zero-points of the CPW column tiles: runs of
+  //    the packed layout, copied straight into the region (reads clamped to
+  //    the column tile's own groups; lanes past the copy write nothing)
+  const int g0 = my_kb * GPC;
+  const size_t srun = (size_t)Gall * 16 * SB;  // scale bytes of one column tile
 #pragma unroll
   for (int i = 0; i < NW; ++i) {
+    uint8_t *msi = ms + i * MS_BYTES;
+    uint8_t *mzi = mz + i * MZ_PAD;
+    const uint8_t *sbase = reinterpret_cast<const uint8_t *>(p.scales[i]);
 #pragma unroll
-    for (int w = 0; w < CPW; ++w) {
-      const int tw = min(ct0 + w, NTL - 1);
-      const size_t first = (size_t)tw * Gall + gb;  // first (tile, group) record
-      const int sbytes = ngr * 16 * SB;
-      const uint8_t *ssrc = reinterpret_cast<const uint8_t *>(p.scales[i]) + first * 16 * SB;
-      uint8_t *sdst = lS + (i * CPW + w) * scopy;
-      for (int q = wk; q * 1024 < sbytes; q += NWK)
-        copy16_to_lds(ssrc + min(q * 1024 + lane * 16, sbytes - 16), sdst + q * 1024);
-      uint8_t *zdst = lZ + (i * CPW + w) * zcopy;
-      if (has_zp) {
-        const int zbytes = ngr * 8;
-        const uint8_t *zsrc = p.zeros[i] + first * 8;
-        for (int q = wk; q * 256 < zbytes; q += NWK)
-          copy4_to_lds(zsrc + min(q * 256 + lane * 4, zbytes - 4), zdst + q * 256);
-      } else {
-        for (int e = tid; e * 4 < zcopy; e += NT)  // symmetric: every zero-point is 8
-          reinterpret_cast<uint32_t *>(zdst)[e] = 0x88888888u;
+    for (int q = 0; q < (CPW * SU + 63) / 64; ++q) {
+      const int u = q * 64 + lane;
+      if (u < CPW * SU) {
+        const int w = u / SU, o = u - w * SU;
+        const size_t tw = (size_t)min(ct0 + w, NTL - 1);
+        const size_t off = min((size_t)g0 * 16 * SB + (size_t)o * 16, srun - 16);
+        copy16_to_lds(sbase + tw * srun + off, msi + q * 1024);
       }
+    }
+    if (has_zp) {
+      const size_t zrun = (size_t)Gall * 8;
+#pragma unroll
+      for (int q = 0; q < (CPW * ZU + 63) / 64; ++q) {
+        const int u = q * 64 + lane;
+        if (u < CPW * ZU) {
+          const int w = u / ZU, o = u - w * ZU;
+          const size_t tw = (size_t)min(ct0 + w, NTL - 1);
+          const size_t off = min((size_t)g0 * 8 + (size_t)o * 4, zrun - 4);
+          copy4_to_lds(p.zeros[i] + tw * zrun + off, mzi + q * 256);
+        }
+      }
+    } else {
+      for (int e = lane; e * 4 < MZ_BYTES; e += 64)  // symmetric: every zero-point is 8
+        reinterpret_cast<uint32_t *>(mzi)[e] = 0x88888888u;
     }
   }
 
-  // 2. activation fragments of this slice, in registers.  Rows past M read
-  //    row M-1 (an A row feeds only its own output row, never written); k
-  //    tiles past the slice read a valid tile and are zeroed, so they add
-  //    nothing.
-  const int arow = m0 + min(c, mrows - 1);
+  // 2. activation fragments of this slice (row l%16, k slots 8*(l/16)..+7 of
+  //    each 32-k step).  Rows past M read row M-1 (an A row feeds only its
+  //    own output row, never written); k tiles past the slice read a valid
+  //    tile and are zeroed below, so they add nothing.
+  //    ALDS: the slice's rows are first copied into the region in fragment
+  //    order (slot ((t*4 + d)*4 + kq)*R + row), unique data only.
+  const int arow = min(c, mrows - 1);
   f16x8 a[KPW][4][1];
-  {
-    const f16 *arow_p = p.A + (size_t)arow * p.K + 8 * kq;
+  if constexpr (ALDS) {
+    const int lr = __builtin_ctz(R);
+    const int n_slots = KPW * 16 * R;
+    for (int q = 0; q * 64 < n_slots; ++q) {
+      const int sl = q * 64 + lane;
+      if (sl < n_slots) {
+        const int row = sl & (R - 1);
+        const int rest = sl >> lr;
+        const int kqs = rest & 3, d = (rest >> 2) & 3, t = rest >> 4;
+        const int kc = min(my_kb + min(t, max(my_n - 1, 0)), KC - 1);
+        const f16 *src = p.A + (size_t)(m0 + min(row, mrows - 1)) * p.K + kc * kTileK + 32 * d + 8 * kqs;
+        copy16_to_lds(src, aslots + q * 1024);
+      }
+    }
+  } else {
+    const f16 *arow_p = p.A + (size_t)(m0 + arow) * p.K + 8 * kq;
 #pragma unroll
     for (int t = 0; t < KPW; ++t) {
       const int kc = min(my_kb + min(t, max(my_n - 1, 0)), KC - 1);
@@ -126,8 +162,34 @@ stream_kernel(const GemmArgs p) {
         a[t][d][0] = *reinterpret_cast<const f16x8 *>(arow_p + kc * kTileK + 32 * d);
     }
   }
-  f16x8 gam[KPW][4];
+  // activation fragments from the slots (ALDS), once the copies landed
+  auto read_slots = [&]() __attribute__((always_inline)) {
+    if constexpr (ALDS) {
+      const uint8_t *ap = aslots + (kq * R + arow) * 16;
+#pragma unroll
+      for (int t = 0; t < KPW; ++t)
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+          a[t][d][0] = *reinterpret_cast<const f16x8 *>(ap + (t * 4 + d) * 64 * R);
+    }
+  };
+  auto zero_tail = [&]() __attribute__((always_inline)) {
+    if (my_n < KPW) {
+#pragma unroll
+      for (int t = 0; t < KPW; ++t)
+        if (t >= my_n)
+#pragma unroll
+          for (int d = 0; d < 4; ++d) a[t][d][0] = f16x8{};
+    }
+  };
+
+  // 3. RMSNorm prologue on the fragments (before the weight stream starts,
+  //    so the gamma fragments are dead by then): per-lane sum of squares
+  //    (row l%16, this lane's k slots), x * gamma rounded once to fp16; the
+  //    factor 1/sqrt(mean + eps) is applied in the epilogue.
+  float ss = 0.f;
   if (rms) {
+    f16x8 gam[KPW][4];
 #pragma unroll
     for (int t = 0; t < KPW; ++t) {
       const int kc = min(my_kb + min(t, max(my_n - 1, 0)), KC - 1);
@@ -135,14 +197,27 @@ stream_kernel(const GemmArgs p) {
       for (int d = 0; d < 4; ++d)
         gam[t][d] = *reinterpret_cast<const f16x8 *>(p.gamma + kc * kTileK + 32 * d + 8 * kq);
     }
+    wait_vmcnt<0>();
+    read_slots();
+    zero_tail();
+#pragma unroll
+    for (int t = 0; t < KPW; ++t)
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        f16x8 x = a[t][d][0];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float xf = (float)x[e];
+          ss += xf * xf;
+          x[e] = (f16)(xf * (float)gam[t][d][e]);
+        }
+        a[t][d][0] = x;
+      }
   }
 
-  // 3. the first PD weight tiles; tile f = t * CPW + w (k tile t, column
+  // 4. the first PD weight tiles; tile f = t * CPW + w (k tile t, column
   //    tile w) is issued PD tiles before it is contracted.  Tiles past the
   //    slice or past N re-read a valid tile.
-  const uint8_t *wbase[NW];
-#pragma unroll
-  for (int i = 0; i < NW; ++i) wbase[i] = p.w[i] + (size_t)lane * 16;
   u32x4 wv[NW][NTILE];
   auto issue_tile = [&](int f) __attribute__((always_inline)) {
     const int t = f / CPW, w = f % CPW;
@@ -150,36 +225,17 @@ stream_kernel(const GemmArgs p) {
     const size_t tile = (size_t)min(ct0 + w, NTL - 1) * KC + kc;
 #pragma unroll
     for (int i = 0; i < NW; ++i)
-      wv[i][f] = *reinterpret_cast<const u32x4 *>(wbase[i] + tile * kTileBytes);
+      wv[i][f] = reinterpret_cast<const u32x4 *>(p.w[i] + tile * kTileBytes)[lane];
   };
 #pragma unroll
-  for (int f = 0; f < PD; ++f) issue_tile(f);
+  for (int f = 0; f < PDE; ++f) issue_tile(f);
 
-  // 4. the metadata copies (issued first) have landed
+  // 5. this wavefront's copies into its region have landed (completion is
+  //    in issue order); no other wavefront reads the region before the end
   wait_vmcnt<(AFTER_COPIES < 63 ? AFTER_COPIES : 63)>();
-  lds_barrier();
-
-  // 5. RMSNorm prologue on the fragments: per-lane sum of squares (row l%16,
-  //    this lane's k slots), x * gamma rounded once to fp16; the factor
-  //    1/sqrt(mean + eps) is applied in the epilogue.  Zeroing of the k
-  //    tiles past the slice happens here too.
-  float ss = 0.f;
-#pragma unroll
-  for (int t = 0; t < KPW; ++t) {
-    const bool valid = t < my_n;
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      f16x8 x = valid ? a[t][d][0] : f16x8{};
-      if (rms) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float xf = (float)x[e];
-          ss += xf * xf;
-          x[e] = (f16)(xf * (float)gam[t][d][e]);
-        }
-      }
-      a[t][d][0] = x;
-    }
+  if (!rms) {
+    read_slots();
+    zero_tail();
   }
 
   // 6. contraction, k tile outer, column tile inner
@@ -191,15 +247,13 @@ stream_kernel(const GemmArgs p) {
   const int zshift = 4 * (c & 1);
 #pragma unroll
   for (int f = 0; f < NTILE; ++f) {
-    if (f + PD < NTILE) issue_tile(f + PD);
+    if (f + PDE < NTILE) issue_tile(f + PDE);
     const int t = f / CPW, w = f % CPW;
-    // first group of k tile t in the workgroup's staged runs (clamped to a
-    // staged group for k tiles past the slice, whose activations are zero)
-    const int gi0 = min(wk * KPW + t, max(nkc - 1, 0)) * GPC;
+    const int gi0 = (w * KPW + t) * GPC;  // first group of the tile in the region
 #pragma unroll
     for (int i = 0; i < NW; ++i) {
-      const uint8_t *st = lS + (i * CPW + w) * scopy + (gi0 * 16 + c) * SB;
-      const uint8_t *zt = lZ + (i * CPW + w) * zcopy + gi0 * 8 + (c >> 1);
+      const uint8_t *st = ms + i * MS_BYTES + (gi0 * 16 + c) * SB;
+      const uint8_t *zt = mz + i * MZ_PAD + gi0 * 8 + (c >> 1);
       contract_tile<1, G>(
           acc[i][w], wv[i][f], a[t], kq,
           [&](int gl) __attribute__((always_inline)) { return (zt[gl * 8] >> zshift) & 15; },
@@ -212,102 +266,89 @@ stream_kernel(const GemmArgs p) {
     }
   }
 
-  // 7. slice partial sums -> LDS; wavefront w < CPW sums column tile w over
-  //    the slices in slice order
+  // 7. slice partial sums into the wavefront's own region ([i][w][lane],
+  //    16 bytes per lane), row sums of squares of the slice; one barrier;
+  //    wavefront w < CPW then sums column tile w over the slices in order
+  f32x4 *red = reinterpret_cast<f32x4 *>(region);
 #pragma unroll
   for (int i = 0; i < NW; ++i)
 #pragma unroll
-    for (int w = 0; w < CPW; ++w)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        lRed[((wk * NW * CPW + i * CPW + w) * 4 + e) * 64 + lane] = acc[i][w][0][e];
-  if (rms) lRms[wk * 64 + lane] = ss;
+    for (int w = 0; w < CPW; ++w) red[(i * CPW + w) * 64 + lane] = acc[i][w][0];
+  if (rms) {
+    // row l%16's k slots of this slice are spread over lanes l%16 + 16j
+    ss += __shfl_xor(ss, 16);
+    ss += __shfl_xor(ss, 32);
+    if (lane < 16) lRms[wk * 16 + lane] = ss;
+  }
   lds_barrier();
   const int wfin = wk;  // the column tile this wavefront finishes (if < CPW)
-  const bool owner = wfin < CPW && ct0 + wfin < NTL;
+  if (wfin >= CPW || ct0 + wfin >= NTL) return;
   f32x4 fin[NW];
-  if (wfin < CPW) {
 #pragma unroll
-    for (int i = 0; i < NW; ++i) {
-      f32x4 v = {0.f, 0.f, 0.f, 0.f};
-      for (int w2 = 0; w2 < NWK; ++w2)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          v[e] += lRed[((w2 * NW * CPW + i * CPW + wfin) * 4 + e) * 64 + lane];
-      fin[i] = v;
-    }
-  }
-  // row sums of squares: row r is held by lanes r, r+16, r+32, r+48 of
-  // every slice
-  if (rms && tid < mrows) {
-    float v = 0.f;
+  for (int i = 0; i < NW; ++i) {
+    f32x4 v = {0.f, 0.f, 0.f, 0.f};
     for (int w2 = 0; w2 < NWK; ++w2)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) v += lRms[w2 * 64 + 16 * g + tid];
-    lRow[tid] = v;
+      v += reinterpret_cast<const f32x4 *>(smem + w2 * p.lds_s)[(i * CPW + wfin) * 64 + lane];
+    fin[i] = v;
   }
+  // sums of squares of this lane's output rows 4*(l/16) + e
+  f32x4 rs = {0.f, 0.f, 0.f, 0.f};
+  if (rms)
+    for (int w2 = 0; w2 < NWK; ++w2) rs += reinterpret_cast<const f32x4 *>(lRms + w2 * 16)[kq];
   const int ncol = (ct0 + wfin) * kTileN + c;
 
-  // 8. k splits across workgroups (narrow grids and very deep k only):
-  //    partials, then the last arrival sums them in split order
-  const int blk = blockIdx.z * gridDim.x + blockIdx.x;
+  // 8. k splits across workgroups (narrow grids and very deep k only): the
+  //    finishing wavefronts store partials; the finishing wavefront of the
+  //    last workgroup to arrive (counted per column tile) sums them in split
+  //    order
   if (S > 1) {
-    lds_barrier();  // lRow complete
-    if (owner) {
+    const size_t cnt = (size_t)blockIdx.z * NTL + ct0 + wfin;  // per column tile
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = 4 * kq + e;
-        if (row < mrows) {
+    for (int e = 0; e < 4; ++e) {
+      const int row = 4 * kq + e;
+      if (row < mrows) {
 #pragma unroll
-          for (int i = 0; i < NW; ++i)
-            p.ws_part[(((size_t)s * NW + i) * p.M + m0 + row) * p.N + ncol] = fin[i][e];
+        for (int i = 0; i < NW; ++i)
+          p.ws_part[(((size_t)s * NW + i) * p.M + m0 + row) * p.N + ncol] = fin[i][e];
+        if (rms && c == 0) p.ws_rms[(cnt * S + s) * 16 + row] = rs[e];
+      }
+    }
+    __threadfence();
+    int last = 0;
+    if (lane == 0) last = atomicAdd(&p.ws_cnt[cnt], 1u) == (unsigned)(S - 1);
+    last = __shfl(last, 0);
+    if (!last) return;
+    __threadfence();
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = 4 * kq + e;
+      if (row < mrows) {
+#pragma unroll
+        for (int i = 0; i < NW; ++i) {
+          float v = 0.f;
+          for (int s2 = 0; s2 < S; ++s2)
+            v += (s2 == s) ? fin[i][e]
+                           : p.ws_part[(((size_t)s2 * NW + i) * p.M + m0 + row) * p.N + ncol];
+          fin[i][e] = v;
+        }
+        if (rms) {
+          float v = 0.f;
+          for (int s2 = 0; s2 < S; ++s2)
+            v += (s2 == s) ? rs[e] : p.ws_rms[(cnt * S + s2) * 16 + row];
+          rs[e] = v;
         }
       }
     }
-    if (rms && tid < mrows) p.ws_rms[((size_t)blk * S + s) * 64 + tid] = lRow[tid];
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-      const unsigned prev = atomicAdd(&p.ws_cnt[blk], 1u);
-      is_last = (prev == (unsigned)(S - 1));
-    }
-    __syncthreads();
-    if (!is_last) return;
-    __threadfence();
-    if (owner) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = 4 * kq + e;
-        if (row < mrows) {
-#pragma unroll
-          for (int i = 0; i < NW; ++i) {
-            float v = 0.f;
-            for (int s2 = 0; s2 < S; ++s2)
-              v += (s2 == s) ? fin[i][e]
-                             : p.ws_part[(((size_t)s2 * NW + i) * p.M + m0 + row) * p.N + ncol];
-            fin[i][e] = v;
-          }
-        }
-      }
-    }
-    if (rms && tid < mrows) {
-      float v = 0.f;
-      for (int s2 = 0; s2 < S; ++s2)
-        v += (s2 == s) ? lRow[tid] : p.ws_rms[((size_t)blk * S + s2) * 64 + tid];
-      lRow[tid] = v;
-    }
-    if (tid == 0) p.ws_cnt[blk] = 0u;
+    if (lane == 0) p.ws_cnt[cnt] = 0u;
   }
-  lds_barrier();  // lRow final
 
   // 9. epilogue, one fp16 write per output
-  if (!owner) return;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int row = 4 * kq + e;
     if (row < mrows) {
       float rsc = 1.0f;
-      if (rms) rsc = 1.0f / sqrtf(lRow[row] / (float)p.K + p.eps);
+      if (rms) rsc = 1.0f / sqrtf(rs[e] / (float)p.K + p.eps);
       float y;
       if constexpr (GU) {
         y = silu(fin[0][e] * rsc) * (fin[1][e] * rsc);
@@ -321,9 +362,9 @@ stream_kernel(const GemmArgs p) {
   }
 }
 
-template <int CPW, int KPW, int NWK, int PD, int G, bool SF32, bool GU>
+template <int CPW, int KPW, int NWK, int PD, bool ALDS, int G, bool SF32, bool GU>
 hipError_t launch_t(const GemmArgs &a, const Plan &pl, hipStream_t stream) {
-  auto kern = stream_kernel<CPW, KPW, NWK, PD, G, SF32, GU>;
+  auto kern = stream_kernel<CPW, KPW, NWK, PD, ALDS, G, SF32, GU>;
   // Raise the kernel's dynamic-LDS limit when a plan needs more than the
   // default 64 KiB; only the first launch that needs a larger size makes the
   // attribute call, so repeated launches (also under stream capture) make none.
@@ -342,40 +383,54 @@ hipError_t launch_t(const GemmArgs &a, const Plan &pl, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int CPW, int KPW, int NWK, int PD, int G>
+template <int CPW, int KPW, int NWK, int PD, bool ALDS, int G>
 hipError_t launch_g(const GemmArgs &a, const Plan &pl, bool sf32, bool gu, hipStream_t st) {
-  if (sf32) return gu ? launch_t<CPW, KPW, NWK, PD, G, true, true>(a, pl, st)
-                      : launch_t<CPW, KPW, NWK, PD, G, true, false>(a, pl, st);
-  return gu ? launch_t<CPW, KPW, NWK, PD, G, false, true>(a, pl, st)
-            : launch_t<CPW, KPW, NWK, PD, G, false, false>(a, pl, st);
+  if (sf32) return gu ? launch_t<CPW, KPW, NWK, PD, ALDS, G, true, true>(a, pl, st)
+                      : launch_t<CPW, KPW, NWK, PD, ALDS, G, true, false>(a, pl, st);
+  return gu ? launch_t<CPW, KPW, NWK, PD, ALDS, G, false, true>(a, pl, st)
+            : launch_t<CPW, KPW, NWK, PD, ALDS, G, false, false>(a, pl, st);
+}
+
+template <int CPW, int KPW, int NWK, int PD, int G>
+hipError_t launch_a(const GemmArgs &a, const Plan &pl, bool sf32, bool gu, hipStream_t st) {
+  return pl.alds ? launch_g<CPW, KPW, NWK, PD, true, G>(a, pl, sf32, gu, st)
+                 : launch_g<CPW, KPW, NWK, PD, false, G>(a, pl, sf32, gu, st);
 }
 
 template <int CPW, int KPW, int NWK, int PD>
 hipError_t launch_c(const GemmArgs &a, const Plan &pl, int group, bool sf32, bool gu,
                     hipStream_t st) {
   switch (group) {
-    case 16: return launch_g<CPW, KPW, NWK, PD, 16>(a, pl, sf32, gu, st);
-    case 32: return launch_g<CPW, KPW, NWK, PD, 32>(a, pl, sf32, gu, st);
-    case 64: return launch_g<CPW, KPW, NWK, PD, 64>(a, pl, sf32, gu, st);
-    default: return launch_g<CPW, KPW, NWK, PD, 128>(a, pl, sf32, gu, st);
+    case 16: return launch_a<CPW, KPW, NWK, PD, 16>(a, pl, sf32, gu, st);
+    case 32: return launch_a<CPW, KPW, NWK, PD, 32>(a, pl, sf32, gu, st);
+    case 64: return launch_a<CPW, KPW, NWK, PD, 64>(a, pl, sf32, gu, st);
+    default: return launch_a<CPW, KPW, NWK, PD, 128>(a, pl, sf32, gu, st);
   }
 }
 
 }  // namespace
 
+// (CPW, KPW, NWK, PD) of each configuration, in plan order: the planner
+// takes the first one whose grid reaches 200 workgroups.
+#define W4A16_STREAM_CFGS(X) \
+  X(4, 5, 8, 8)   /* 4 column tiles x 8 slices of 5 k tiles (K <= 5120) */ \
+  X(2, 5, 8, 6)   /* 2 column tiles, for narrower N */                     \
+  X(1, 5, 8, 4)   /* 1 column tile, for narrow N */
+
 const StreamCfg kStreamCfgs[kNumStreamCfgs] = {
-    {4, 5, 8, 8},  // 0: 4 column tiles x 8 slices of 5 k tiles (K <= 5120)
-    {2, 5, 8, 6},  // 1: 2 column tiles, for narrower N
-    {1, 5, 8, 4},  // 2: 1 column tile, for narrow N
+#define W4A16_CFG_ROW(cpw, kpw, nwk, pd) {cpw, kpw, nwk, pd},
+    W4A16_STREAM_CFGS(W4A16_CFG_ROW)
+#undef W4A16_CFG_ROW
 };
 
 hipError_t launch_stream(const GemmArgs &a, const Plan &pl, int group, bool scale_f32,
                          bool gate_up, hipStream_t stream) {
-  switch (pl.cfg) {
-    case 0: return launch_c<4, 5, 8, 8>(a, pl, group, scale_f32, gate_up, stream);
-    case 1: return launch_c<2, 5, 8, 6>(a, pl, group, scale_f32, gate_up, stream);
-    default: return launch_c<1, 5, 8, 4>(a, pl, group, scale_f32, gate_up, stream);
-  }
+  int i = 0;
+#define W4A16_CFG_CASE(cpw, kpw, nwk, pd) \
+  if (pl.cfg == i++) return launch_c<cpw, kpw, nwk, pd>(a, pl, group, scale_f32, gate_up, stream);
+  W4A16_STREAM_CFGS(W4A16_CFG_CASE)
+#undef W4A16_CFG_CASE
+  return hipErrorInvalidValue;
 }
 
 }  // namespace w4a16
