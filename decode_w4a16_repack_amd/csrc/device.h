@@ -133,6 +133,101 @@ __device__ __forceinline__ void contract_tile(f32x4 (&acc)[MT], const u32x4 &w,
   }
 }
 
+// ---------------------------------------------------------------------------
+// Contraction with the zero-point taken out of the weights.
+//
+// (q - z) * a summed over a group equals sum(q * a) - z * sum(a), so the
+// weights can enter the matrix core as the bare codes q and the zero-point
+// is applied per group with the group's activation row sums U:
+//   acc += s * sum_k q*a  -  s * z * U.
+// The codes are placed into fp16 without any arithmetic: masking nibble
+// pairs into the low mantissa bits of a zero exponent gives the fp16
+// subnormals q * 2^-24 (bits 0-3) or 16q * 2^-24 (bits 4-7), exact.  The
+// activation slots that meet a 16q code (slots 2, 3, 6, 7 of each 8) are
+// pre-scaled by 1/16 (exact for normal fp16 values), so every product is
+// q * a * 2^-24, exact in the fp32 accumulator; the group scale carries
+// the 2^24 back.  U comes from the same activation fragments times a
+// constant B of 1 (or 16 in the pre-scaled slots), one MFMA per 32-k step,
+// shared by every column tile that uses the fragments.
+
+// Eight codes of one packed word -> fp16 q * 2^-24 (slots 0, 1, 4, 5) and
+// 16q * 2^-24 (slots 2, 3, 6, 7).
+__device__ __forceinline__ f16x8 unpack8_sub(uint32_t w) {
+  const uint32_t w8 = w >> 8;
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  const u32x4_t v = {w & 0x000F000Fu, w & 0x00F000F0u, w8 & 0x000F000Fu, w8 & 0x00F000F0u};
+  return __builtin_bit_cast(f16x8, v);
+}
+
+// Activation fragment pre-scaled for unpack8_sub: slots 2, 3, 6, 7 times 1/16.
+__device__ __forceinline__ f16x8 prescale_frag(f16x8 x) {
+  const f16x8 m = {(f16)1.0f, (f16)1.0f, (f16)0.0625f, (f16)0.0625f,
+                   (f16)1.0f, (f16)1.0f, (f16)0.0625f, (f16)0.0625f};
+  return x * m;
+}
+
+// Group row sums of a pre-scaled activation k tile (128 k): ug[gl] holds,
+// for this lane's output rows 4*(l/16)+e, the sum of the activations of
+// group gl (0 .. 128/G - 1) of the tile.
+template <int G>
+__device__ __forceinline__ void group_row_sums(f32x4 (&ug)[128 / G], const f16x8 (&a)[4], int kq) {
+  const f16x8 ones = {(f16)1.0f, (f16)1.0f, (f16)16.0f, (f16)16.0f,
+                      (f16)1.0f, (f16)1.0f, (f16)16.0f, (f16)16.0f};
+  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (G >= 32) {
+    constexpr int SPG = G / 32;
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+      ug[d / SPG] = mfma16(a[d], ones, (d % SPG == 0) ? zero4 : ug[d / SPG]);
+  } else {
+    const f16x8 zero8 = {};
+    const f16x8 olo = (kq < 2) ? ones : zero8;
+    const f16x8 ohi = (kq < 2) ? zero8 : ones;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      ug[2 * d] = mfma16(a[d], olo, zero4);
+      ug[2 * d + 1] = mfma16(a[d], ohi, zero4);
+    }
+  }
+}
+
+// Contract one packed k tile of one 16-column weight tile with one 16-row
+// tile of pre-scaled activation fragments a[d] (d = 32-k step), given the
+// tile's group row sums ug; zp_of(gl) / scale_of(gl) as for contract_tile.
+template <int G, class ZpOf, class ScaleOf>
+__device__ __forceinline__ void contract_tile_sub(f32x4 &acc, const u32x4 &w, const f16x8 (&a)[4],
+                                                  const f32x4 (&ug)[128 / G], int kq, ZpOf zp_of,
+                                                  ScaleOf scale_of) {
+  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+  auto apply = [&](const f32x4 &part, int gl) __attribute__((always_inline)) {
+    const float s = scale_of(gl);
+    const float s24 = s * 16777216.0f;  // 2^24: the codes entered as q * 2^-24
+    const float sz = -s * (float)zp_of(gl);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      acc[e] = __builtin_fmaf(ug[gl][e], sz, __builtin_fmaf(part[e], s24, acc[e]));
+  };
+  if constexpr (G >= 32) {
+    constexpr int SPG = G / 32;
+    f32x4 accg;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      accg = mfma16(a[d], unpack8_sub(w[d]), (d % SPG == 0) ? zero4 : accg);
+      if ((d + 1) % SPG == 0) apply(accg, d / SPG);
+    }
+  } else {
+    const f16x8 zero8 = {};
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const f16x8 b = unpack8_sub(w[d]);
+      const f32x4 p0 = mfma16(a[d], (kq < 2) ? b : zero8, zero4);
+      const f32x4 p1 = mfma16(a[d], (kq < 2) ? zero8 : b, zero4);
+      apply(p0, 2 * d);
+      apply(p1, 2 * d + 1);
+    }
+  }
+}
+
 // contract_tile with the activation fragments read from LDS:
 //  * a_lane[t]: this lane's 16-byte activation slot of step 0 for m tile t;
 //    step d is d * dstride bytes further.  The tile is in fragment order

@@ -238,24 +238,36 @@ stream_kernel(const GemmArgs p) {
     zero_tail();
   }
 
-  // 6. contraction, k tile outer, column tile inner
+  // 6. contraction, k tile outer, column tile inner.  The codes enter the
+  //    matrix core bare (q * 2^-24); the activation slots facing 16q codes
+  //    are pre-scaled by 1/16, and each k tile's group row sums serve its
+  //    CPW column tiles for the zero-point term.
+#pragma unroll
+  for (int t = 0; t < KPW; ++t)
+#pragma unroll
+    for (int d = 0; d < 4; ++d) a[t][d][0] = prescale_frag(a[t][d][0]);
   f32x4 acc[NW][CPW][1];
 #pragma unroll
   for (int i = 0; i < NW; ++i)
 #pragma unroll
     for (int w = 0; w < CPW; ++w) acc[i][w][0] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int zshift = 4 * (c & 1);
+  f32x4 ug[GPC];
 #pragma unroll
   for (int f = 0; f < NTILE; ++f) {
     if (f + PDE < NTILE) issue_tile(f + PDE);
     const int t = f / CPW, w = f % CPW;
+    f16x8 at[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) at[d] = a[t][d][0];
+    if (w == 0) group_row_sums<G>(ug, at, kq);
     const int gi0 = (w * KPW + t) * GPC;  // first group of the tile in the region
 #pragma unroll
     for (int i = 0; i < NW; ++i) {
       const uint8_t *st = ms + i * MS_BYTES + (gi0 * 16 + c) * SB;
       const uint8_t *zt = mz + i * MZ_PAD + gi0 * 8 + (c >> 1);
-      contract_tile<1, G>(
-          acc[i][w], wv[i][f], a[t], kq,
+      contract_tile_sub<G>(
+          acc[i][w][0], wv[i][f], at, ug, kq,
           [&](int gl) __attribute__((always_inline)) { return (zt[gl * 8] >> zshift) & 15; },
           [&](int gl) __attribute__((always_inline)) {
             if constexpr (SF32)
