@@ -46,7 +46,7 @@ INFINITY_CACHE = 256 << 20
 PAGE_M1_US = 69.5  # the pages' M=1 time for this shape (H200, context only)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemv_m1.json")
 KERNEL_SOURCES = ["decode_w4a16_repack_amd/csrc/" + f for f in
-                  ("oneshot.hip", "ring.hip", "device.h", "gemm.hip", "common.h")]
+                  ("stream.hip", "oneshot.hip", "ring.hip", "device.h", "gemm.hip", "common.h")]
 COPY_PROBE_BYTES = 256 << 20  # plain copy of known size, counter calibration
 
 
@@ -243,7 +243,7 @@ def traffic_summary(fetch_dir, write_dir):
     total = 0.0
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = _counter_rows(d, counter)
-        gemm = [n for n in rows if "oneshot_kernel" in n or "ring_kernel" in n]
+        gemm = [n for n in rows if "stream_kernel" in n or "oneshot_kernel" in n or "ring_kernel" in n]
         copy = [n for n in rows if "probe_copy_kernel" in n]
         if len(gemm) != 1 or len(copy) != 1:
             raise SystemExit(f"{counter}: expected one GEMM and one copy kernel, got {sorted(rows)}")
