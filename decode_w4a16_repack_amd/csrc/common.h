@@ -96,10 +96,11 @@ struct GemmArgs {
 };
 
 // Launch plan of one GEMM call, a pure function of the shape.
-enum PlanKind { kKindRing = 0, kKindOneshot = 1, kKindStream = 2 };
+enum PlanKind { kKindRing = 0, kKindOneshot = 1, kKindStream = 2, kKindTile = 3 };
 
 struct Plan {
-  int kind;     // PlanKind: ring.hip (kRingCfgs), oneshot.hip (kOneshotCfgs), stream.hip (kStreamCfgs)
+  int kind;     // PlanKind: ring.hip (kRingCfgs), oneshot.hip (kOneshotCfgs), stream.hip
+                // (kStreamCfgs), tile.hip
   int cfg;      // index into the kernel's configuration table
   int gx, gy, gz;
   int split, cps;
@@ -120,6 +121,14 @@ hipError_t launch_oneshot(const GemmArgs &a, const Plan &p, int group, bool scal
 
 hipError_t launch_stream(const GemmArgs &a, const Plan &p, int group, bool scale_f32,
                          bool gate_up, hipStream_t stream);
+
+// tile.hip (M > 16): k slices per workgroup, LDS bytes, output columns per
+// workgroup
+int tile_k_slices(int group, bool scale_f32);
+size_t tile_lds_bytes(int group, int scale_bytes, bool gate_up);
+int tile_columns(bool gate_up);
+hipError_t launch_tile(const GemmArgs &a, const Plan &p, int group, bool scale_f32,
+                       bool gate_up, hipStream_t stream);
 
 hipError_t launch_ring(const GemmArgs &a, const Plan &p, int group, bool scale_f32,
                        bool gate_up, hipStream_t stream);

@@ -1,5 +1,5 @@
 // Launch planning for the fused W4A16 GEMM (kernels in stream.hip for
-// M <= 16, ring.hip above).
+// M <= 16, tile.hip above; oneshot.hip and ring.hip on request).
 //
 // The plan is a pure function of the shape: it picks the tile configuration,
 // the grid and, only for grids too small to fill the chip, a k split across
@@ -183,6 +183,19 @@ bool plan_stream(Plan &p, int M, int K, int N, int group, int scale_bytes, bool 
 Plan make_plan(int M, int K, int N, int group, int scale_bytes, bool gate_up, int force_kind,
                int force_cfg, int force_split) {
   Plan p{};
+  if (force_kind < 0 ? M > 16 : force_kind == kKindTile) {
+    // 64-row blocks x tile_columns() per workgroup over the whole K
+    p.kind = kKindTile;
+    p.cfg = 0;
+    p.gx = (N + tile_columns(gate_up) - 1) / tile_columns(gate_up);
+    p.gy = 1;
+    p.gz = (M + 63) / 64;
+    p.split = 1;
+    p.cps = K / kTileK;
+    p.lds_bytes = tile_lds_bytes(group, scale_bytes, gate_up);
+    p.ws_total = 0;
+    return p;
+  }
   if (force_kind == kKindOneshot) {
     Plan q{};
     if (plan_oneshot(q, M, K, N, group, scale_bytes, gate_up, force_cfg, force_split)) return q;
@@ -233,6 +246,7 @@ hipError_t launch_gemm(const GemmArgs &a, const Plan &pl, int group,
   switch (pl.kind) {
     case kKindStream: return launch_stream(a, pl, group, scale_f32, gate_up, stream);
     case kKindOneshot: return launch_oneshot(a, pl, group, scale_f32, gate_up, stream);
+    case kKindTile: return launch_tile(a, pl, group, scale_f32, gate_up, stream);
     default: return launch_ring(a, pl, group, scale_f32, gate_up, stream);
   }
 }
