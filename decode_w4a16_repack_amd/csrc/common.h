@@ -122,11 +122,11 @@ hipError_t launch_oneshot(const GemmArgs &a, const Plan &p, int group, bool scal
 hipError_t launch_stream(const GemmArgs &a, const Plan &p, int group, bool scale_f32,
                          bool gate_up, hipStream_t stream);
 
-// tile.hip (M > 16): k slices per workgroup, LDS bytes, output columns per
-// workgroup
-int tile_k_slices(int group, bool scale_f32);
-size_t tile_lds_bytes(int group, int scale_bytes, bool gate_up);
-int tile_columns(bool gate_up);
+// tile.hip (M > 16): column tiles per wavefront and weight stream (wide:
+// several 64-row blocks), LDS bytes, output columns per workgroup
+int tile_ct(bool wide, bool gate_up);
+size_t tile_lds_bytes(int ct, int group, int scale_bytes, bool gate_up);
+int tile_columns(int ct);
 hipError_t launch_tile(const GemmArgs &a, const Plan &p, int group, bool scale_f32,
                        bool gate_up, hipStream_t stream);
 

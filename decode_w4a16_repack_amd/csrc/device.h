@@ -281,4 +281,16 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Workgroup barrier that leaves global loads and global-to-LDS copies in
+// flight: this wavefront's LDS reads and writes are waited for (lgkmcnt(0);
+// vmcnt and expcnt untouched), the compiler may not move memory accesses
+// across it, and no cache or vector-memory wait is emitted (a release fence
+// on LDS would also wait for the copies still in flight).
+__device__ __forceinline__ void lds_only_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // vmcnt 63, expcnt 7, lgkmcnt 0
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 }  // namespace w4a16

@@ -184,15 +184,17 @@ Plan make_plan(int M, int K, int N, int group, int scale_bytes, bool gate_up, in
                int force_cfg, int force_split) {
   Plan p{};
   if (force_kind < 0 ? M > 16 : force_kind == kKindTile) {
-    // 64-row blocks x tile_columns() per workgroup over the whole K
+    // 64-row blocks x tile_columns() per workgroup over the whole K; wide
+    // column blocks only when several row blocks keep the grid full
     p.kind = kKindTile;
-    p.cfg = 0;
-    p.gx = (N + tile_columns(gate_up) - 1) / tile_columns(gate_up);
-    p.gy = 1;
     p.gz = (M + 63) / 64;
+    p.cfg = p.gz > 1 ? 1 : 0;
+    const int ct = tile_ct(p.cfg == 1, gate_up);
+    p.gx = (N + tile_columns(ct) - 1) / tile_columns(ct);
+    p.gy = 1;
     p.split = 1;
     p.cps = K / kTileK;
-    p.lds_bytes = tile_lds_bytes(group, scale_bytes, gate_up);
+    p.lds_bytes = tile_lds_bytes(ct, group, scale_bytes, gate_up);
     p.ws_total = 0;
     return p;
   }

@@ -8,25 +8,33 @@
 // reduced in a fixed order, so results are run-to-run identical.
 //
 // gfx950 design.  A workgroup computes a 64-row x (2*CT*16)-column output
-// tile over the whole K with 8 wavefronts (4 when LDS is short):
+// tile over the whole K with 4 wavefronts, one per SIMD (so each has the
+// whole 512-entry register file):
 //  * wavefront (wc, ks) owns column half wc (CT 16-column weight tiles) and
-//    k slice ks: it takes every NKS-th 128-k tile, so the NKS slices walk K
+//    k slice ks: it takes every other 128-k tile, so the two slices walk K
 //    side by side in steps;
-//  * its output block is 64 x (CT*16) = MT x CT MFMA tiles: each unpacked
-//    weight fragment feeds MT = 4 MFMAs and each activation fragment CT, which
-//    keeps both the unpack (VALU) and the activation reads (LDS) below the
+//  * its output block is 64 x (CT*16) = 4 x CT MFMA tiles: each unpacked
+//    weight fragment feeds 4 MFMAs and each activation fragment CT, which
+//    keeps the unpack (VALU) and the activation reads (LDS) below the
 //    matrix-core time;
-//  * per step and slice, the 64 x 128 activation tile goes straight from
-//    global memory into a double-buffered LDS tile (direct global-to-LDS
-//    loads of whole row segments; both column halves read it), its 16-byte
-//    chunks XOR-swizzled by row so an MFMA operand read is conflict-free;
-//    the wavefront's scales and zero-points of the step go the same way into
-//    its own double-buffered LDS slot;
-//  * the weights of the next step are loaded into registers (one 16-byte
-//    load per lane per 1 KiB tile) while the current step computes;
-//  * one barrier per step; after the last, the slices' partial sums meet in
-//    LDS and wavefront (wc, ks) finishes row tiles ks, ks + NKS, ... of its
-//    column half in slice order: RMSNorm factor, epilogue, one fp16 write.
+//  * everything a step reads goes straight from global memory into an LDS
+//    stage with direct global-to-LDS loads: the slice's 64 x 128 activation
+//    tile (whole row segments; both column halves read it), its 16-byte
+//    chunks XOR-swizzled by row so an MFMA operand read is conflict-free,
+//    and each wavefront's weight tiles (1 KiB each, one 16-byte piece per
+//    lane), scales, zero-points and gamma in its own slot;
+//  * ST stages: the copies of step j + ST - 1 are issued while step j
+//    computes, so ST - 1 steps of memory latency are covered; no register
+//    is held across steps and the step loop is not unrolled, which keeps the
+//    code small; the number of copies per step is fixed (tail steps re-read
+//    the last tile), which keeps the one wait per step exact;
+//  * one barrier per step (two with the RMSNorm prologue, which normalizes
+//    the stage's activation tiles in place); after the last step, the
+//    slices' partial sums meet in LDS and wavefront (wc, ks) finishes row
+//    tiles ks, ks + 2 of its column half in slice order: RMSNorm factor,
+//    epilogue, one fp16 write.
+#include <type_traits>
+
 #include "device.h"
 
 namespace w4a16 {
@@ -35,30 +43,54 @@ namespace {
 
 constexpr int kTileMT = 4;   // 16-row MFMA tiles per wavefront (64 rows per workgroup)
 constexpr int kTileNWC = 2;  // column halves per workgroup
+constexpr int kTileNKS = 2;  // k slices per workgroup
+constexpr int kTileNWave = kTileNWC * kTileNKS;
+constexpr int kTileABytes = 64 * kTileK * 2;  // one slice's 64 x 128 activation tile
+constexpr int kLdsMax = 160 * 1024;
 
-template <int G, bool SF32>
-constexpr int tile_nks() {
-  return (G == 16 && SF32) ? 2 : 4;  // k slices; fewer when the metadata slots need the LDS
+// metadata slot of one wavefront and step: scales, zero-points (per weight
+// stream), gamma
+constexpr int tile_meta_bytes(int ct, int group, int sb, int nw) {
+  return nw * (ct * (kTileK / group) * 16 * sb + (ct * (kTileK / group) * 8 + 15) / 16 * 16) +
+         kTileK * 2;
+}
+constexpr int tile_stage_bytes(int ct, int group, int sb, int nw) {
+  return kTileNKS * kTileABytes + kTileNWave * (nw * ct * kTileBytes + tile_meta_bytes(ct, group, sb, nw));
+}
+constexpr int tile_rms_bytes() { return kTileNKS * 64 * 4; }
+constexpr int tile_stages(int ct, int group, int sb, int nw) {
+  return 4 * tile_stage_bytes(ct, group, sb, nw) + tile_rms_bytes() <= kLdsMax   ? 4
+         : 3 * tile_stage_bytes(ct, group, sb, nw) + tile_rms_bytes() <= kLdsMax ? 3
+                                                                                 : 2;
 }
 
 template <int CT, int G, bool SF32, bool GU>
-__global__ void __launch_bounds__((64 * kTileNWC * tile_nks<G, SF32>()))
+__global__ void __launch_bounds__(64 * kTileNWave)
 tile_kernel(const GemmArgs p) {
   constexpr int MT = kTileMT;
   constexpr int NWC = kTileNWC;
-  constexpr int NKS = tile_nks<G, SF32>();
+  constexpr int NKS = kTileNKS;
   constexpr int NW = GU ? 2 : 1;
   constexpr int GPC = 128 / G;
   constexpr int SB = SF32 ? 4 : 2;
-  constexpr int A_BYTES = 64 * kTileK * 2;            // one slice's 64 x 128 activation tile
-  constexpr int MS = CT * GPC * 16 * SB;              // scales of one step, one stream
-  constexpr int MZ = (CT * GPC * 8 + 15) / 16 * 16;   // zero-points of one step, one stream
-  constexpr int GB = kTileK * 2;                       // gamma of one step (RMSNorm)
-  constexpr int MB = NW * (MS + MZ) + GB;             // one metadata slot
-  constexpr int SU = GPC * SB;                        // 16-byte scale units per column tile
-  constexpr int ZU = GPC * 2;                         // 4-byte zero-point units per column tile
-  constexpr int META_OFF = 2 * NKS * A_BYTES;
-  constexpr int RMS_OFF = META_OFF + NWC * NKS * 2 * MB;
+  constexpr int MS = CT * GPC * 16 * SB;             // scales of one step, one stream
+  constexpr int MZ = (CT * GPC * 8 + 15) / 16 * 16;  // zero-points of one step, one stream
+  constexpr int MB = tile_meta_bytes(CT, G, SB, NW);
+  constexpr int WB = NW * CT * kTileBytes;  // one wavefront's weight tiles of one step
+  constexpr int SLOT = WB + MB;             // one wavefront's slot of a stage
+  constexpr int SU = GPC * SB;  // 16-byte scale units per column tile
+  constexpr int ZU = GPC * 2;   // 4-byte zero-point units per column tile
+  constexpr int ST = tile_stages(CT, G, SB, NW);
+  constexpr int STAGE = tile_stage_bytes(CT, G, SB, NW);
+  constexpr int RMS_OFF = ST * STAGE;
+  static_assert(kTileNWave * NW * MT * CT * 1024 <= ST * STAGE, "reduction scratch");
+  // copies per step and wavefront (activations, weights, scales,
+  // zero-points, gamma); at the top of step j, those of the ST - 2 later
+  // steps may still be in flight
+  constexpr int CL = kTileABytes / 1024 / NWC + NW * CT + NW * ((CT * SU + 63) / 64) +
+                     NW * ((CT * ZU + 63) / 64) + 1;
+  constexpr int AFTER = (ST - 2) * CL;
+  static_assert(AFTER < 64, "vmcnt range");
 
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
@@ -78,21 +110,28 @@ tile_kernel(const GemmArgs p) {
   const int nsteps = (KC + NKS - 1) / NKS;
   const bool rms = p.gamma != nullptr;
   const bool has_zp = p.has_zp != 0;
-  uint8_t *mslot = smem + META_OFF + wave * 2 * MB;
   float *lRms = reinterpret_cast<float *>(smem + RMS_OFF);  // [NKS][64 rows]
 
-  // k tile of step j for this slice (clamped: steps past K re-read a valid
-  // tile and are skipped)
   auto ktile = [&](int j) __attribute__((always_inline)) { return j * NKS + ks; };
+  auto abuf_of = [&](int st) __attribute__((always_inline)) {
+    return smem + st * STAGE + ks * kTileABytes;
+  };
+  auto wslot_of = [&](int st) __attribute__((always_inline)) {
+    return smem + st * STAGE + NKS * kTileABytes + wave * SLOT;
+  };
+  auto slot_of = [&](int st) __attribute__((always_inline)) { return wslot_of(st) + WB; };
 
-  // direct-to-LDS copies of step j: this slice's activation tile (half of
-  // it per column half) and this wavefront's scales / zero-points (and
-  // gamma, with the RMSNorm prologue)
-  auto issue_copies = [&](int j) __attribute__((always_inline)) {
+  // loads of step j into stage st: the slice's activation tile (half of it
+  // per column half), this wavefront's scales / zero-points / gamma, and its
+  // weight tiles.  Always the same instructions: steps past K re-read the
+  // last k tile, symmetric weights copy scale bytes into the (unread)
+  // zero-point area, and without RMSNorm activation bytes go into the
+  // (unread) gamma area.
+  auto issue = [&](int j, int st) __attribute__((always_inline)) {
     const int kt = min(ktile(j), KC - 1);
-    uint8_t *abuf = smem + ((j & 1) * NKS + ks) * A_BYTES;
+    uint8_t *abuf = abuf_of(st);
 #pragma unroll
-    for (int q = wc; q < A_BYTES / 1024; q += NWC) {
+    for (int q = wc; q < kTileABytes / 1024; q += NWC) {
       // slot r * 16 + pos holds 16-byte chunk pos ^ (r % 16) of row r: one
       // copy reads four whole 256-byte row segments
       const int sl = q * 64 + lane;
@@ -100,57 +139,43 @@ tile_kernel(const GemmArgs p) {
       const f16 *src = p.A + (size_t)(m0 + min(row, mrows - 1)) * p.K + kt * kTileK + 8 * chunk;
       copy16_to_lds(src, abuf + q * 1024);
     }
-    uint8_t *slot = mslot + (j & 1) * MB;
+    uint8_t *slot = slot_of(st);
 #pragma unroll
     for (int i = 0; i < NW; ++i) {
       const uint8_t *sbase = reinterpret_cast<const uint8_t *>(p.scales[i]);
 #pragma unroll
       for (int q = 0; q < (CT * SU + 63) / 64; ++q) {
-        const int u = q * 64 + lane;
-        if (u < CT * SU) {
-          const int w = u / SU, o = u - w * SU;
-          const size_t t = (size_t)min(ctw + w, NTL - 1);
+        const int u = min(q * 64 + lane, CT * SU - 1);
+        const int w = u / SU, o = u - w * SU;
+        const size_t t = (size_t)min(ctw + w, NTL - 1);
+        if (q * 64 + lane < CT * SU)
           copy16_to_lds(sbase + ((t * Gall + (size_t)kt * GPC) * 16) * SB + o * 16,
                         slot + i * MS + q * 1024);
-        }
       }
-      if (has_zp) {
 #pragma unroll
-        for (int q = 0; q < (CT * ZU + 63) / 64; ++q) {
-          const int u = q * 64 + lane;
-          if (u < CT * ZU) {
-            const int w = u / ZU, o = u - w * ZU;
-            const size_t t = (size_t)min(ctw + w, NTL - 1);
-            copy4_to_lds(p.zeros[i] + (t * Gall + (size_t)kt * GPC) * 8 + o * 4,
-                         slot + NW * MS + i * MZ + q * 256);
-          }
-        }
+      for (int q = 0; q < (CT * ZU + 63) / 64; ++q) {
+        const int u = min(q * 64 + lane, CT * ZU - 1);
+        const int w = u / ZU, o = u - w * ZU;
+        const size_t t = (size_t)min(ctw + w, NTL - 1);
+        const size_t zoff = (t * Gall + (size_t)kt * GPC) * 8 + o * 4;
+        const uint8_t *zsrc = has_zp ? p.zeros[i] + zoff : sbase + zoff;
+        if (q * 64 + lane < CT * ZU) copy4_to_lds(zsrc, slot + NW * MS + i * MZ + q * 256);
       }
     }
-    if (rms && lane < 16) copy16_to_lds(p.gamma + kt * kTileK + lane * 8, slot + NW * (MS + MZ));
-  };
-
-  // symmetric weights: every zero-point is 8, in both slots
-  if (!has_zp) {
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int i = 0; i < NW; ++i)
-        for (int e = lane; e * 4 < MZ; e += 64)
-          reinterpret_cast<uint32_t *>(mslot + b * MB + NW * MS + i * MZ)[e] = 0x88888888u;
-  }
-
-  // weight tiles of step j (registers)
-  auto load_w = [&](int j, u32x4 (&wv)[NW][CT]) __attribute__((always_inline)) {
-    const int kt = min(ktile(j), KC - 1);
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct) {
-      const size_t tile = (size_t)min(ctw + ct, NTL - 1) * KC + kt;
-#pragma unroll
-      for (int i = 0; i < NW; ++i)
-        wv[i][ct] = reinterpret_cast<const u32x4 *>(p.w[i] + tile * kTileBytes)[lane];
+    {
+      const f16 *gsrc = rms ? p.gamma + kt * kTileK + lane * 8 : p.A + lane * 8;
+      if (lane < 16) copy16_to_lds(gsrc, slot + NW * (MS + MZ));
     }
+    uint8_t *wslot = wslot_of(st);
+#pragma unroll
+    for (int i = 0; i < NW; ++i)
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        const size_t tile = (size_t)min(ctw + ct, NTL - 1) * KC + kt;
+        copy16_to_lds(p.w[i] + tile * kTileBytes + lane * 16, wslot + (i * CT + ct) * kTileBytes);
+      }
   };
+
   f32x4 acc[NW][MT][CT];
 #pragma unroll
   for (int i = 0; i < NW; ++i)
@@ -158,41 +183,53 @@ tile_kernel(const GemmArgs p) {
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) acc[i][mt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-  f32x4 ssq = {0.f, 0.f, 0.f, 0.f};  // sum of squares of row 16mt + c, per mt (column half 0)
+  // RMSNorm prologue, in place on the stage: wavefront w normalizes rows
+  // 32*(w/2) .. +31 of slice w%2's activation tile; lane l takes chunks
+  // l + 64i (i = 0..7), i.e. row 32*(w/2) + 4i + l/16, and keeps that row's
+  // running sum of squares in ssq[i]
+  float ssq[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  auto rms_pass = [&](int st) __attribute__((always_inline)) {
+    const int sl = wave & 1, h = wave >> 1;
+    uint8_t *ab = smem + st * STAGE + sl * kTileABytes;
+    // gamma of slice sl's k tile sits in the slot of wavefront (0, sl)
+    const f16 *gm = reinterpret_cast<const f16 *>(smem + st * STAGE + NKS * kTileABytes +
+                                                 (sl * NWC) * SLOT + WB + NW * (MS + MZ));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int e = lane + 64 * i;
+      const int r = 32 * h + (e >> 4), pos = e & 15;
+      f16x8 *px = reinterpret_cast<f16x8 *>(ab + (r * 16 + pos) * 16);
+      const f16x8 g = *reinterpret_cast<const f16x8 *>(gm + 8 * (pos ^ (r & 15)));
+      f16x8 x = *px;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const float xf = (float)x[q];
+        ssq[i] = __builtin_fmaf(xf, xf, ssq[i]);
+      }
+      *px = x * g;
+    }
+  };
 
   const int zshift = 4 * (c & 1);
-  auto compute = [&](int j, const u32x4 (&wv)[NW][CT]) __attribute__((always_inline)) {
+  auto compute = [&](int st) __attribute__((always_inline)) {
     // row 16mt + c, chunk 4d + kq sits at slot row * 16 + ((4d + kq) ^ c): the
     // 16 rows of one operand read land in 16 different chunk positions
-    const uint8_t *abuf = smem + ((j & 1) * NKS + ks) * A_BYTES + c * 256;
-    const uint8_t *slot = mslot + (j & 1) * MB;
+    const uint8_t *abuf = abuf_of(st) + c * 256;
+    const uint8_t *slot = slot_of(st);
+    const u32x4 *wsl = reinterpret_cast<const u32x4 *>(wslot_of(st)) + lane;
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
-    // the step's activation fragments, all 4 x MT of them
     f16x8 a[4][MT];
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      f16x8 gam = {};
-      if (rms) gam = *reinterpret_cast<const f16x8 *>(slot + NW * (MS + MZ) + (32 * d + 8 * kq) * 2);
+    for (int d = 0; d < 4; ++d)
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
+      for (int mt = 0; mt < MT; ++mt)
         a[d][mt] = *reinterpret_cast<const f16x8 *>(abuf + mt * 4096 + ((4 * d + kq) ^ c) * 16);
-        if (rms) {
-          if (wc == 0) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const float x = (float)a[d][mt][e];
-              ssq[mt] = __builtin_fmaf(x, x, ssq[mt]);
-            }
-          }
-          a[d][mt] = a[d][mt] * gam;
-        }
-      }
-    }
 #pragma unroll
     for (int i = 0; i < NW; ++i) {
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
-        const uint8_t *sp = slot + i * MS + ((ct * GPC) * 16 + c) * SB;     // scale of group 0
+        const u32x4 wv = wsl[(i * CT + ct) * 64];
+        const uint8_t *sp = slot + i * MS + ((ct * GPC) * 16 + c) * SB;  // scale of group 0
         const uint8_t *zp = slot + NW * MS + i * MZ + (ct * GPC) * 8 + (c >> 1);
         auto scale = [&](int g2) __attribute__((always_inline)) {
           if constexpr (SF32)
@@ -201,7 +238,8 @@ tile_kernel(const GemmArgs p) {
             return (float)*reinterpret_cast<const f16 *>(sp + g2 * 16 * SB);
         };
         auto zconst = [&](int g2, f16x2 &zlo, f16x2 &zhi) __attribute__((always_inline)) {
-          zero_consts((uint32_t)((zp[g2 * 8] >> zshift) & 15), zlo, zhi);
+          const uint32_t z = has_zp ? (uint32_t)((zp[g2 * 8] >> zshift) & 15) : 8u;
+          zero_consts(z, zlo, zhi);
         };
         if constexpr (G >= 32) {
           constexpr int SPG = G / 32;  // 32-k steps per group
@@ -210,7 +248,7 @@ tile_kernel(const GemmArgs p) {
 #pragma unroll
           for (int d = 0; d < 4; ++d) {
             if (d % SPG == 0) zconst(d / SPG, zlo, zhi);
-            const f16x8 b = unpack8(wv[i][ct][d], zlo, zhi);
+            const f16x8 b = unpack8(wv[d], zlo, zhi);
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
               accg[mt] = mfma16(a[d][mt], b, (d % SPG == 0) ? zero4 : accg[mt]);
@@ -230,7 +268,7 @@ tile_kernel(const GemmArgs p) {
           for (int d = 0; d < 4; ++d) {
             f16x2 zlo, zhi;
             zconst(2 * d + (kq >> 1), zlo, zhi);
-            const f16x8 b = unpack8(wv[i][ct][d], zlo, zhi);
+            const f16x8 b = unpack8(wv[d], zlo, zhi);
             const f16x8 blo = (kq < 2) ? b : zero8;
             const f16x8 bhi = (kq < 2) ? zero8 : b;
             const float s0 = scale(2 * d), s1 = scale(2 * d + 1);
@@ -249,34 +287,27 @@ tile_kernel(const GemmArgs p) {
     }
   };
 
-  // Pipeline: copies and weights of step 0, then per step j: wait for its
-  // copies, barrier (also frees the other buffers), issue step j + 1,
-  // compute j.
-  u32x4 w0[NW][CT], w1[NW][CT];
-  issue_copies(0);
-  load_w(0, w0);
-  auto step = [&](int j, u32x4 (&wcur)[NW][CT], u32x4 (&wnext)[NW][CT])
-      __attribute__((always_inline)) {
-    // the copies of step j were issued before its weight loads
-    wait_vmcnt<NW * CT>();
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-    if (j + 1 < nsteps) {
-      issue_copies(j + 1);
-      load_w(j + 1, wnext);
+  // Pipeline: steps 0 .. ST-2 are issued up front; step j waits for its
+  // copies, meets the other wavefronts (which frees the stage read in step
+  // j - 1), issues step j + ST - 1 into that stage, and computes.
+#pragma unroll
+  for (int u = 0; u < ST - 1; ++u) issue(u, u);
+  int st = 0;
+  for (int j = 0; j < nsteps; ++j) {
+    wait_vmcnt<AFTER>();  // this wavefront's copies of step j have landed
+    lds_only_barrier();   // everyone's have, and step j - 1's reads are done
+    issue(j + ST - 1, st == 0 ? ST - 1 : st - 1);
+    if (rms) {
+      rms_pass(st);
+      lds_only_barrier();
     }
-    if (ktile(j) < KC) compute(j, wcur);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  };
-  for (int j = 0; j < nsteps; j += 2) {
-    step(j, w0, w1);
-    if (j + 1 < nsteps) step(j + 1, w1, w0);
+    if (ktile(j) < KC) compute(st);
+    st = st == ST - 1 ? 0 : st + 1;
   }
-  __syncthreads();  // every step done: the activation tiles become reduction scratch
+  __syncthreads();  // every step and every copy done: the stages become reduction scratch
 
   // slice partial sums -> LDS ([wave][i][mt][ct][lane], 16 bytes per lane)
   f32x4 *red = reinterpret_cast<f32x4 *>(smem);
-  constexpr int PER = NW * MT * CT;
 #pragma unroll
   for (int i = 0; i < NW; ++i)
 #pragma unroll
@@ -284,18 +315,20 @@ tile_kernel(const GemmArgs p) {
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct)
         red[((wave * NW + i) * MT + mt) * CT * 64 + ct * 64 + lane] = acc[i][mt][ct];
-  if (rms && wc == 0) {
-    // row 16mt + c's k slots are spread over lanes c + 16j
+  if (rms) {
+    // ssq[i] of lane l is row 32*(w/2) + 4i + l/16 of slice w%2: sum the 16
+    // lanes of each row
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      float v = ssq[mt];
-      v += __shfl_xor(v, 16);
-      v += __shfl_xor(v, 32);
-      if (lane < 16) lRms[ks * 64 + 16 * mt + lane] = v;
+    for (int i = 0; i < 8; ++i) {
+      float v = ssq[i];
+      v += __shfl_xor(v, 1);
+      v += __shfl_xor(v, 2);
+      v += __shfl_xor(v, 4);
+      v += __shfl_xor(v, 8);
+      if ((lane & 15) == 0) lRms[(wave & 1) * 64 + 32 * (wave >> 1) + 4 * i + (lane >> 4)] = v;
     }
   }
   __syncthreads();
-  (void)PER;
 
   // wavefront (wc, ks) finishes row tiles ks, ks + NKS, ... of column half wc
 #pragma unroll
@@ -354,37 +387,37 @@ hipError_t launch_t(const GemmArgs &a, const Plan &pl, hipStream_t stream) {
     }
     lds_limit = pl.lds_bytes;
   }
-  hipLaunchKernelGGL(kern, dim3(pl.gx, pl.gy, pl.gz), dim3(64 * kTileNWC * tile_nks<G, SF32>()),
-                     pl.lds_bytes, stream, a);
+  hipLaunchKernelGGL(kern, dim3(pl.gx, pl.gy, pl.gz), dim3(64 * kTileNWave), pl.lds_bytes,
+                     stream, a);
   return hipGetLastError();
 }
 
+// column tiles per wavefront and weight stream: 4 (2 for gate_up) when there
+// are several 64-row blocks (Plan::cfg == 1), else half as many, so that the
+// grid keeps its workgroup count
 template <int G>
 hipError_t launch_g(const GemmArgs &a, const Plan &pl, bool sf32, bool gu, hipStream_t st) {
-  if (sf32) return gu ? launch_t<2, G, true, true>(a, pl, st) : launch_t<4, G, true, false>(a, pl, st);
-  return gu ? launch_t<2, G, false, true>(a, pl, st) : launch_t<4, G, false, false>(a, pl, st);
+  const bool wide = pl.cfg == 1;
+  if (gu) {
+    if (sf32) return wide ? launch_t<2, G, true, true>(a, pl, st) : launch_t<1, G, true, true>(a, pl, st);
+    return wide ? launch_t<2, G, false, true>(a, pl, st) : launch_t<1, G, false, true>(a, pl, st);
+  }
+  if (sf32) return wide ? launch_t<4, G, true, false>(a, pl, st) : launch_t<2, G, true, false>(a, pl, st);
+  return wide ? launch_t<4, G, false, false>(a, pl, st) : launch_t<2, G, false, false>(a, pl, st);
 }
 
 }  // namespace
 
-int tile_k_slices(int group, bool scale_f32) {
-  if (scale_f32 && group == 16) return tile_nks<16, true>();
-  return 4;
-}
+int tile_ct(bool wide, bool gate_up) { return (wide ? 4 : 2) / (gate_up ? 2 : 1); }
 
-size_t tile_lds_bytes(int group, int scale_bytes, bool gate_up) {
-  const int nks = tile_k_slices(group, scale_bytes == 4);
+size_t tile_lds_bytes(int ct, int group, int scale_bytes, bool gate_up) {
   const int nw = gate_up ? 2 : 1;
-  const int ct = gate_up ? 2 : 4;
-  const int gpc = kTileK / group;
-  const size_t ms = (size_t)ct * gpc * 16 * scale_bytes;
-  const size_t mz = ((size_t)ct * gpc * 8 + 15) / 16 * 16;
-  const size_t mb = nw * (ms + mz) + kTileK * 2;
-  const size_t a = 2 * (size_t)nks * 64 * kTileK * 2;
-  return a + (size_t)kTileNWC * nks * 2 * mb + (size_t)nks * 64 * 4;
+  return (size_t)tile_stages(ct, group, scale_bytes, nw) *
+             tile_stage_bytes(ct, group, scale_bytes, nw) +
+         tile_rms_bytes();
 }
 
-int tile_columns(bool gate_up) { return kTileNWC * (gate_up ? 2 : 4) * kTileN; }
+int tile_columns(int ct) { return kTileNWC * ct * kTileN; }
 
 hipError_t launch_tile(const GemmArgs &a, const Plan &pl, int group, bool scale_f32,
                        bool gate_up, hipStream_t stream) {
