@@ -7,16 +7,15 @@
 // multiplied by its scale after the contraction; the k range is split and
 // reduced in a fixed order, so results are run-to-run identical.
 //
-// gfx950 design.  A workgroup computes a 64-row x (2*CT*16)-column output
-// tile over the whole K with 4 wavefronts, one per SIMD (so each has the
-// whole 512-entry register file):
-//  * wavefront (wc, ks) owns column half wc (CT 16-column weight tiles) and
-//    k slice ks: it takes every other 128-k tile, so the two slices walk K
-//    side by side in steps;
+// gfx950 design.  A workgroup computes a 64-row x (4*CT*16)-column output
+// tile over the whole K with 8 wavefronts, two per SIMD (one issues VALU
+// work while the other's MFMAs run):
+//  * wavefront (wc, ks) owns column quarter wc (CT 16-column weight tiles)
+//    and k slice ks: it takes every other 128-k tile, so the two slices walk
+//    K side by side in steps;
 //  * its output block is 64 x (CT*16) = 4 x CT MFMA tiles: each unpacked
-//    weight fragment feeds 4 MFMAs and each activation fragment CT, which
-//    keeps the unpack (VALU) and the activation reads (LDS) below the
-//    matrix-core time;
+//    weight fragment feeds 4 MFMAs and each activation fragment CT, and the
+//    activation tile of a step is shared by the four column quarters;
 //  * everything a step reads goes straight from global memory into an LDS
 //    stage with direct global-to-LDS loads: the slice's 64 x 128 activation
 //    tile (whole row segments; both column halves read it), its 16-byte
@@ -31,7 +30,7 @@
 //  * one barrier per step (two with the RMSNorm prologue, which normalizes
 //    the stage's activation tiles in place); after the last step, the
 //    slices' partial sums meet in LDS and wavefront (wc, ks) finishes row
-//    tiles ks, ks + 2 of its column half in slice order: RMSNorm factor,
+//    tiles ks, ks + 2 of its column quarter in slice order: RMSNorm factor,
 //    epilogue, one fp16 write.
 #include <type_traits>
 
@@ -42,7 +41,7 @@ namespace w4a16 {
 namespace {
 
 constexpr int kTileMT = 4;   // 16-row MFMA tiles per wavefront (64 rows per workgroup)
-constexpr int kTileNWC = 2;  // column halves per workgroup
+constexpr int kTileNWC = 4;  // column quarters per workgroup
 constexpr int kTileNKS = 2;  // k slices per workgroup
 constexpr int kTileNWave = kTileNWC * kTileNKS;
 constexpr int kTileABytes = 64 * kTileK * 2;  // one slice's 64 x 128 activation tile
@@ -88,7 +87,7 @@ tile_kernel(const GemmArgs p) {
   // zero-points, gamma); at the top of step j, those of the ST - 2 later
   // steps may still be in flight
   constexpr int CL = kTileABytes / 1024 / NWC + NW * CT + NW * ((CT * SU + 63) / 64) +
-                     NW * ((CT * ZU + 63) / 64) + 1;
+                     NW * ((CT * ZU + 63) / 64) + 1;  // = AQ + NW*(CT + SQ + ZQ) + 1
   constexpr int AFTER = (ST - 2) * CL;
   static_assert(AFTER < 64, "vmcnt range");
 
@@ -121,51 +120,46 @@ tile_kernel(const GemmArgs p) {
   };
   auto slot_of = [&](int st) __attribute__((always_inline)) { return wslot_of(st) + WB; };
 
-  // loads of step j into stage st: the slice's activation tile (half of it
-  // per column half), this wavefront's scales / zero-points / gamma, and its
-  // weight tiles.  Always the same instructions: steps past K re-read the
-  // last k tile, symmetric weights copy scale bytes into the (unread)
-  // zero-point area, and without RMSNorm activation bytes go into the
-  // (unread) gamma area.
+  // per-lane source offsets of the copies, fixed for the whole kernel (the
+  // per-step part of each address is wavefront-uniform)
+  constexpr int AQ = kTileABytes / 1024 / NWC;         // activation copies per wavefront
+  constexpr int SQ = (CT * SU + 63) / 64;              // scale copies per stream
+  constexpr int ZQ = (CT * ZU + 63) / 64;              // zero-point copies per stream
+  uint32_t aoff[AQ], soff[SQ], zoff[ZQ];
+#pragma unroll
+  for (int qi = 0; qi < AQ; ++qi) {
+    // slot r * 16 + pos holds 16-byte chunk pos ^ (r % 16) of row r: one
+    // copy reads four whole 256-byte row segments
+    const int sl = (wc + NWC * qi) * 64 + lane;
+    const int row = sl >> 4, chunk = (sl & 15) ^ (row & 15);
+    aoff[qi] = (uint32_t)(min(row, mrows - 1) * p.K + 8 * chunk) * 2u;
+  }
+#pragma unroll
+  for (int q = 0; q < SQ; ++q) {
+    const int u = min(q * 64 + lane, CT * SU - 1);
+    const int w = u / SU, o = u - w * SU;
+    soff[q] = (uint32_t)min(ctw + w, NTL - 1) * (uint32_t)(Gall * 16 * SB) + (uint32_t)o * 16u;
+  }
+#pragma unroll
+  for (int q = 0; q < ZQ; ++q) {
+    const int u = min(q * 64 + lane, CT * ZU - 1);
+    const int w = u / ZU, o = u - w * ZU;
+    zoff[q] = (uint32_t)min(ctw + w, NTL - 1) * (uint32_t)(Gall * 8) + (uint32_t)o * 4u;
+  }
+  const uint8_t *a_rows = reinterpret_cast<const uint8_t *>(p.A + (size_t)m0 * p.K);
+
+  // copies of step j into stage st: the slice's activation tile (a quarter
+  // of it per column quarter), this wavefront's weight tiles, scales,
+  // zero-points and gamma.  Always the same instructions: steps past K
+  // re-read the last k tile, symmetric weights copy scale bytes into the
+  // (unread) zero-point area, and without RMSNorm activation bytes go into
+  // the (unread) gamma area.
   auto issue = [&](int j, int st) __attribute__((always_inline)) {
     const int kt = min(ktile(j), KC - 1);
     uint8_t *abuf = abuf_of(st);
+    const uint8_t *abase = a_rows + (size_t)kt * kTileK * 2;
 #pragma unroll
-    for (int q = wc; q < kTileABytes / 1024; q += NWC) {
-      // slot r * 16 + pos holds 16-byte chunk pos ^ (r % 16) of row r: one
-      // copy reads four whole 256-byte row segments
-      const int sl = q * 64 + lane;
-      const int row = sl >> 4, chunk = (sl & 15) ^ (row & 15);
-      const f16 *src = p.A + (size_t)(m0 + min(row, mrows - 1)) * p.K + kt * kTileK + 8 * chunk;
-      copy16_to_lds(src, abuf + q * 1024);
-    }
-    uint8_t *slot = slot_of(st);
-#pragma unroll
-    for (int i = 0; i < NW; ++i) {
-      const uint8_t *sbase = reinterpret_cast<const uint8_t *>(p.scales[i]);
-#pragma unroll
-      for (int q = 0; q < (CT * SU + 63) / 64; ++q) {
-        const int u = min(q * 64 + lane, CT * SU - 1);
-        const int w = u / SU, o = u - w * SU;
-        const size_t t = (size_t)min(ctw + w, NTL - 1);
-        if (q * 64 + lane < CT * SU)
-          copy16_to_lds(sbase + ((t * Gall + (size_t)kt * GPC) * 16) * SB + o * 16,
-                        slot + i * MS + q * 1024);
-      }
-#pragma unroll
-      for (int q = 0; q < (CT * ZU + 63) / 64; ++q) {
-        const int u = min(q * 64 + lane, CT * ZU - 1);
-        const int w = u / ZU, o = u - w * ZU;
-        const size_t t = (size_t)min(ctw + w, NTL - 1);
-        const size_t zoff = (t * Gall + (size_t)kt * GPC) * 8 + o * 4;
-        const uint8_t *zsrc = has_zp ? p.zeros[i] + zoff : sbase + zoff;
-        if (q * 64 + lane < CT * ZU) copy4_to_lds(zsrc, slot + NW * MS + i * MZ + q * 256);
-      }
-    }
-    {
-      const f16 *gsrc = rms ? p.gamma + kt * kTileK + lane * 8 : p.A + lane * 8;
-      if (lane < 16) copy16_to_lds(gsrc, slot + NW * (MS + MZ));
-    }
+    for (int qi = 0; qi < AQ; ++qi) copy16_to_lds(abase + aoff[qi], abuf + (wc + NWC * qi) * 1024);
     uint8_t *wslot = wslot_of(st);
 #pragma unroll
     for (int i = 0; i < NW; ++i)
@@ -174,6 +168,22 @@ tile_kernel(const GemmArgs p) {
         const size_t tile = (size_t)min(ctw + ct, NTL - 1) * KC + kt;
         copy16_to_lds(p.w[i] + tile * kTileBytes + lane * 16, wslot + (i * CT + ct) * kTileBytes);
       }
+    uint8_t *slot = slot_of(st);
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+      const uint8_t *sbase = reinterpret_cast<const uint8_t *>(p.scales[i]) + (size_t)kt * GPC * 16 * SB;
+#pragma unroll
+      for (int q = 0; q < SQ; ++q)
+        if (q * 64 + lane < CT * SU) copy16_to_lds(sbase + soff[q], slot + i * MS + q * 1024);
+      const uint8_t *zbase = has_zp ? p.zeros[i] + (size_t)kt * GPC * 8 : sbase;
+#pragma unroll
+      for (int q = 0; q < ZQ; ++q)
+        if (q * 64 + lane < CT * ZU) copy4_to_lds(zbase + zoff[q], slot + NW * MS + i * MZ + q * 256);
+    }
+    {
+      const f16 *gsrc = rms ? p.gamma + kt * kTileK + lane * 8 : p.A + lane * 8;
+      if (lane < 16) copy16_to_lds(gsrc, slot + NW * (MS + MZ));
+    }
   };
 
   f32x4 acc[NW][MT][CT];
@@ -184,10 +194,10 @@ tile_kernel(const GemmArgs p) {
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) acc[i][mt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
   // RMSNorm prologue, in place on the stage: wavefront w normalizes rows
-  // 32*(w/2) .. +31 of slice w%2's activation tile; lane l takes chunks
-  // l + 64i (i = 0..7), i.e. row 32*(w/2) + 4i + l/16, and keeps that row's
+  // 16*(w/2) .. +15 of slice w%2's activation tile; lane l takes chunks
+  // l + 64i (i = 0..3), i.e. row 16*(w/2) + 4i + l/16, and keeps that row's
   // running sum of squares in ssq[i]
-  float ssq[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float ssq[4] = {0.f, 0.f, 0.f, 0.f};
   auto rms_pass = [&](int st) __attribute__((always_inline)) {
     const int sl = wave & 1, h = wave >> 1;
     uint8_t *ab = smem + st * STAGE + sl * kTileABytes;
@@ -195,9 +205,9 @@ tile_kernel(const GemmArgs p) {
     const f16 *gm = reinterpret_cast<const f16 *>(smem + st * STAGE + NKS * kTileABytes +
                                                  (sl * NWC) * SLOT + WB + NW * (MS + MZ));
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 4; ++i) {
       const int e = lane + 64 * i;
-      const int r = 32 * h + (e >> 4), pos = e & 15;
+      const int r = 16 * h + (e >> 4), pos = e & 15;
       f16x8 *px = reinterpret_cast<f16x8 *>(ab + (r * 16 + pos) * 16);
       const f16x8 g = *reinterpret_cast<const f16x8 *>(gm + 8 * (pos ^ (r & 15)));
       f16x8 x = *px;
@@ -316,21 +326,21 @@ tile_kernel(const GemmArgs p) {
       for (int ct = 0; ct < CT; ++ct)
         red[((wave * NW + i) * MT + mt) * CT * 64 + ct * 64 + lane] = acc[i][mt][ct];
   if (rms) {
-    // ssq[i] of lane l is row 32*(w/2) + 4i + l/16 of slice w%2: sum the 16
+    // ssq[i] of lane l is row 16*(w/2) + 4i + l/16 of slice w%2: sum the 16
     // lanes of each row
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 4; ++i) {
       float v = ssq[i];
       v += __shfl_xor(v, 1);
       v += __shfl_xor(v, 2);
       v += __shfl_xor(v, 4);
       v += __shfl_xor(v, 8);
-      if ((lane & 15) == 0) lRms[(wave & 1) * 64 + 32 * (wave >> 1) + 4 * i + (lane >> 4)] = v;
+      if ((lane & 15) == 0) lRms[(wave & 1) * 64 + 16 * (wave >> 1) + 4 * i + (lane >> 4)] = v;
     }
   }
   __syncthreads();
 
-  // wavefront (wc, ks) finishes row tiles ks, ks + NKS, ... of column half wc
+  // wavefront (wc, ks) finishes row tiles ks, ks + NKS, ... of column quarter wc
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     if (mt % NKS != ks) continue;
@@ -392,23 +402,20 @@ hipError_t launch_t(const GemmArgs &a, const Plan &pl, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// column tiles per wavefront and weight stream: 4 (2 for gate_up) when there
-// are several 64-row blocks (Plan::cfg == 1), else half as many, so that the
-// grid keeps its workgroup count
+// column tiles per wavefront: 2 when there are several 64-row blocks
+// (Plan::cfg == 1), else 1, so that the grid keeps its workgroup count;
+// gate_up (two weight streams) always 1
 template <int G>
 hipError_t launch_g(const GemmArgs &a, const Plan &pl, bool sf32, bool gu, hipStream_t st) {
   const bool wide = pl.cfg == 1;
-  if (gu) {
-    if (sf32) return wide ? launch_t<2, G, true, true>(a, pl, st) : launch_t<1, G, true, true>(a, pl, st);
-    return wide ? launch_t<2, G, false, true>(a, pl, st) : launch_t<1, G, false, true>(a, pl, st);
-  }
-  if (sf32) return wide ? launch_t<4, G, true, false>(a, pl, st) : launch_t<2, G, true, false>(a, pl, st);
-  return wide ? launch_t<4, G, false, false>(a, pl, st) : launch_t<2, G, false, false>(a, pl, st);
+  if (gu) return sf32 ? launch_t<1, G, true, true>(a, pl, st) : launch_t<1, G, false, true>(a, pl, st);
+  if (sf32) return wide ? launch_t<2, G, true, false>(a, pl, st) : launch_t<1, G, true, false>(a, pl, st);
+  return wide ? launch_t<2, G, false, false>(a, pl, st) : launch_t<1, G, false, false>(a, pl, st);
 }
 
 }  // namespace
 
-int tile_ct(bool wide, bool gate_up) { return (wide ? 4 : 2) / (gate_up ? 2 : 1); }
+int tile_ct(bool wide, bool gate_up) { return (wide && !gate_up) ? 2 : 1; }
 
 size_t tile_lds_bytes(int ct, int group, int scale_bytes, bool gate_up) {
   const int nw = gate_up ? 2 : 1;
