@@ -16,16 +16,18 @@
 //  * its output block is 64 x (CT*16) = 4 x CT MFMA tiles: each unpacked
 //    weight fragment feeds 4 MFMAs and each activation fragment CT, and the
 //    activation tile of a step is shared by the four column quarters;
-//  * everything a step reads goes straight from global memory into an LDS
-//    stage with direct global-to-LDS loads: the slice's 64 x 128 activation
-//    tile (whole row segments; both column halves read it), its 16-byte
-//    chunks XOR-swizzled by row so an MFMA operand read is conflict-free,
-//    and each wavefront's weight tiles (1 KiB each, one 16-byte piece per
-//    lane), scales, zero-points and gamma in its own slot;
-//  * ST stages: the copies of step j + ST - 1 are issued while step j
-//    computes, so ST - 1 steps of memory latency are covered; no register
-//    is held across steps and the step loop is not unrolled, which keeps the
-//    code small; the number of copies per step is fixed (tail steps re-read
+//  * the slice's 64 x 128 activation tile goes straight from global memory
+//    (L2) into an LDS stage with direct global-to-LDS loads (whole row
+//    segments; all four column quarters read it), its 16-byte chunks
+//    XOR-swizzled by row so an MFMA operand read is conflict-free; ST
+//    stages, so the copies of step j + ST - 1 are issued while step j
+//    computes; each wavefront's scales and zero-points go the same way into
+//    its own LDS blocks, several steps per copy (every copy costs issue time
+//    in the memory pipeline, whatever its size);
+//  * the weight tiles (the HBM stream: one 16-byte load per lane per 1 KiB
+//    tile) go straight into registers D = 3 steps ahead (a ring of four,
+//    the step loop unrolled by four);
+//  * the number of copies and loads per step is fixed (tail steps re-read
 //    the last tile), which keeps the one wait per step exact;
 //  * one barrier per step (two with the RMSNorm prologue, which normalizes
 //    the stage's activation tiles in place); after the last step, the
@@ -47,20 +49,30 @@ constexpr int kTileNWave = kTileNWC * kTileNKS;
 constexpr int kTileABytes = 64 * kTileK * 2;  // one slice's 64 x 128 activation tile
 constexpr int kLdsMax = 160 * 1024;
 
-// metadata slot of one wavefront and step: scales, zero-points (per weight
-// stream), gamma
-constexpr int tile_meta_bytes(int ct, int group, int sb, int nw) {
-  return nw * (ct * (kTileK / group) * 16 * sb + (ct * (kTileK / group) * 8 + 15) / 16 * 16) +
-         kTileK * 2;
+// Scales and zero-points of one wavefront go into LDS in blocks of
+// tile_mbs() steps (one copy per stream and kind for a whole block), in a
+// ring of tile_nbuf() blocks.
+constexpr int tile_step_scale_bytes(int ct, int group, int sb) { return ct * (kTileK / group) * 16 * sb; }
+constexpr int tile_step_zp_bytes(int ct, int group) { return ct * (kTileK / group) * 8; }
+constexpr int tile_mbs(int ct, int group, int sb) {
+  return 1024 / tile_step_scale_bytes(ct, group, sb) >= 8 ? 8
+         : 1024 / tile_step_scale_bytes(ct, group, sb) >= 1 ? 1024 / tile_step_scale_bytes(ct, group, sb)
+                                                             : 1;
 }
-constexpr int tile_stage_bytes(int ct, int group, int sb, int nw) {
-  return kTileNKS * kTileABytes + kTileNWave * (nw * ct * kTileBytes + tile_meta_bytes(ct, group, sb, nw));
+constexpr int tile_meta_block_bytes(int ct, int group, int sb, int nw) {
+  return nw * (tile_mbs(ct, group, sb) * tile_step_scale_bytes(ct, group, sb) +
+               (tile_mbs(ct, group, sb) * tile_step_zp_bytes(ct, group) + 15) / 16 * 16);
 }
+constexpr int tile_stage_bytes() { return kTileNKS * kTileABytes; }
 constexpr int tile_rms_bytes() { return kTileNKS * 64 * 4; }
+constexpr int tile_nbuf(int st, int mbs) { return (st - 1 + mbs - 1) / mbs + 1; }
+constexpr int tile_lds(int st, int ct, int group, int sb, int nw) {
+  return st * tile_stage_bytes() +
+         kTileNWave * tile_nbuf(st, tile_mbs(ct, group, sb)) * tile_meta_block_bytes(ct, group, sb, nw) +
+         tile_rms_bytes();
+}
 constexpr int tile_stages(int ct, int group, int sb, int nw) {
-  return 4 * tile_stage_bytes(ct, group, sb, nw) + tile_rms_bytes() <= kLdsMax   ? 4
-         : 3 * tile_stage_bytes(ct, group, sb, nw) + tile_rms_bytes() <= kLdsMax ? 3
-                                                                                 : 2;
+  return tile_lds(4, ct, group, sb, nw) <= kLdsMax ? 4 : tile_lds(3, ct, group, sb, nw) <= kLdsMax ? 3 : 2;
 }
 
 template <int CT, int G, bool SF32, bool GU>
@@ -72,23 +84,31 @@ tile_kernel(const GemmArgs p) {
   constexpr int NW = GU ? 2 : 1;
   constexpr int GPC = 128 / G;
   constexpr int SB = SF32 ? 4 : 2;
-  constexpr int MS = CT * GPC * 16 * SB;             // scales of one step, one stream
-  constexpr int MZ = (CT * GPC * 8 + 15) / 16 * 16;  // zero-points of one step, one stream
-  constexpr int MB = tile_meta_bytes(CT, G, SB, NW);
-  constexpr int WB = NW * CT * kTileBytes;  // one wavefront's weight tiles of one step
-  constexpr int SLOT = WB + MB;             // one wavefront's slot of a stage
-  constexpr int SU = GPC * SB;  // 16-byte scale units per column tile
-  constexpr int ZU = GPC * 2;   // 4-byte zero-point units per column tile
+  constexpr int PSS = CT * GPC * 16 * SB;  // scale bytes of one step, one stream
+  constexpr int PSZ = CT * GPC * 8;        // zero-point bytes of one step, one stream
   constexpr int ST = tile_stages(CT, G, SB, NW);
-  constexpr int STAGE = tile_stage_bytes(CT, G, SB, NW);
-  constexpr int RMS_OFF = ST * STAGE;
+  constexpr int MBS = tile_mbs(CT, G, SB);  // steps per metadata block
+  constexpr int NBUF = tile_nbuf(ST, MBS);  // metadata blocks in the ring
+  constexpr int BS = MBS * PSS;                        // scale bytes of a block, one stream
+  constexpr int BZ = (MBS * PSZ + 15) / 16 * 16;       // zero-point bytes of a block, one stream
+  constexpr int MBLK = tile_meta_block_bytes(CT, G, SB, NW);
+  constexpr int STAGE = tile_stage_bytes();
+  constexpr int META_OFF = ST * STAGE;
+  constexpr int RMS_OFF = META_OFF + kTileNWave * NBUF * MBLK;
+  constexpr int D = 3;  // steps the weight tiles are loaded ahead (ring of D + 1)
   static_assert(kTileNWave * NW * MT * CT * 1024 <= ST * STAGE, "reduction scratch");
-  // copies per step and wavefront (activations, weights, scales,
-  // zero-points, gamma); at the top of step j, those of the ST - 2 later
-  // steps may still be in flight
-  constexpr int CL = kTileABytes / 1024 / NWC + NW * CT + NW * ((CT * SU + 63) / 64) +
-                     NW * ((CT * ZU + 63) / 64) + 1;  // = AQ + NW*(CT + SQ + ZQ) + 1
-  constexpr int AFTER = (ST - 2) * CL;
+  static_assert(D >= ST - 1, "weights at least as far ahead as the copies");
+  static_assert(BS <= 1024 && BZ <= 256 + 15, "one copy per block, stream and kind");
+  static_assert(MBS >= ST - 1 || NBUF * MBS >= ST, "metadata ring");
+  // per step and wavefront at least: activation copies CL, then weight-tile
+  // loads WL.  At the top of step j, the loads issued after the copies of
+  // step j are the weights of that step and the copies and weights of the
+  // ST - 2 steps after it; metadata copies (one block every MBS steps) and
+  // the first steps' extra loads only add to that, which makes the wait
+  // stricter, never looser.
+  constexpr int CL = kTileABytes / 1024 / NWC;
+  constexpr int WL = NW * CT;
+  constexpr int AFTER = WL + (ST - 2) * (CL + WL);
   static_assert(AFTER < 64, "vmcnt range");
 
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -115,17 +135,16 @@ tile_kernel(const GemmArgs p) {
   auto abuf_of = [&](int st) __attribute__((always_inline)) {
     return smem + st * STAGE + ks * kTileABytes;
   };
-  auto wslot_of = [&](int st) __attribute__((always_inline)) {
-    return smem + st * STAGE + NKS * kTileABytes + wave * SLOT;
+  // metadata block b of this wavefront: scales [NW][MBS][CT][GPC][16],
+  // then zero-points [NW][MBS][CT][GPC][8 bytes]
+  auto mblk_of = [&](int b) __attribute__((always_inline)) {
+    return smem + META_OFF + (wave * NBUF + b % NBUF) * MBLK;
   };
-  auto slot_of = [&](int st) __attribute__((always_inline)) { return wslot_of(st) + WB; };
 
   // per-lane source offsets of the copies, fixed for the whole kernel (the
   // per-step part of each address is wavefront-uniform)
-  constexpr int AQ = kTileABytes / 1024 / NWC;         // activation copies per wavefront
-  constexpr int SQ = (CT * SU + 63) / 64;              // scale copies per stream
-  constexpr int ZQ = (CT * ZU + 63) / 64;              // zero-point copies per stream
-  uint32_t aoff[AQ], soff[SQ], zoff[ZQ];
+  constexpr int AQ = kTileABytes / 1024 / NWC;  // activation copies per wavefront
+  uint32_t aoff[AQ];
 #pragma unroll
   for (int qi = 0; qi < AQ; ++qi) {
     // slot r * 16 + pos holds 16-byte chunk pos ^ (r % 16) of row r: one
@@ -134,56 +153,61 @@ tile_kernel(const GemmArgs p) {
     const int row = sl >> 4, chunk = (sl & 15) ^ (row & 15);
     aoff[qi] = (uint32_t)(min(row, mrows - 1) * p.K + 8 * chunk) * 2u;
   }
-#pragma unroll
-  for (int q = 0; q < SQ; ++q) {
-    const int u = min(q * 64 + lane, CT * SU - 1);
-    const int w = u / SU, o = u - w * SU;
-    soff[q] = (uint32_t)min(ctw + w, NTL - 1) * (uint32_t)(Gall * 16 * SB) + (uint32_t)o * 16u;
-  }
-#pragma unroll
-  for (int q = 0; q < ZQ; ++q) {
-    const int u = min(q * 64 + lane, CT * ZU - 1);
-    const int w = u / ZU, o = u - w * ZU;
-    zoff[q] = (uint32_t)min(ctw + w, NTL - 1) * (uint32_t)(Gall * 8) + (uint32_t)o * 4u;
+  // metadata: lane u of the scale copy takes 16-byte unit u of the block,
+  // (step i, column tile ct, unit o); the zero-point copy 4-byte units
+  constexpr int SUS = PSS / 16;  // 16-byte scale units per step
+  constexpr int ZUS = PSZ / 4;   // 4-byte zero-point units per step
+  const bool s_on = lane < MBS * SUS, z_on = lane < MBS * ZUS;
+  uint32_t s_lane, z_lane;
+  int s_step, z_step;
+  {
+    const int u = min(lane, MBS * SUS - 1);
+    s_step = u / SUS;
+    const int r = u - s_step * SUS, w = r / (GPC * SB), o = r - w * (GPC * SB);
+    s_lane = (uint32_t)min(ctw + w, NTL - 1) * (uint32_t)(Gall * 16 * SB) + (uint32_t)o * 16u;
+    const int uz = min(lane, MBS * ZUS - 1);
+    z_step = uz / ZUS;
+    const int rz = uz - z_step * ZUS, wz = rz / (GPC * 2), oz = rz - wz * (GPC * 2);
+    z_lane = (uint32_t)min(ctw + wz, NTL - 1) * (uint32_t)(Gall * 8) + (uint32_t)oz * 4u;
   }
   const uint8_t *a_rows = reinterpret_cast<const uint8_t *>(p.A + (size_t)m0 * p.K);
 
   // copies of step j into stage st: the slice's activation tile (a quarter
-  // of it per column quarter), this wavefront's weight tiles, scales,
-  // zero-points and gamma.  Always the same instructions: steps past K
-  // re-read the last k tile, symmetric weights copy scale bytes into the
-  // (unread) zero-point area, and without RMSNorm activation bytes go into
-  // the (unread) gamma area.
+  // of it per column quarter); when step j opens a metadata block, first
+  // that block's scales and zero-points.  Steps past K re-read the last k
+  // tile; symmetric weights copy scale bytes into the (unread) zero-point
+  // area.
   auto issue = [&](int j, int st) __attribute__((always_inline)) {
+    if (j % MBS == 0) {
+      uint8_t *blk = mblk_of(j / MBS);
+      // k tile of step j + s_step (the lane's own step in the block)
+      const int kts = min(ktile(j + s_step), KC - 1), ktz = min(ktile(j + z_step), KC - 1);
+#pragma unroll
+      for (int i = 0; i < NW; ++i) {
+        const uint8_t *sb = reinterpret_cast<const uint8_t *>(p.scales[i]);
+        if (s_on) copy16_to_lds(sb + s_lane + (size_t)kts * GPC * 16 * SB, blk + i * BS);
+        const uint8_t *zb = has_zp ? p.zeros[i] + (size_t)ktz * GPC * 8 + z_lane
+                                   : sb + s_lane + (size_t)kts * GPC * 16 * SB;
+        if (z_on) copy4_to_lds(zb, blk + NW * BS + i * BZ);
+      }
+    }
     const int kt = min(ktile(j), KC - 1);
     uint8_t *abuf = abuf_of(st);
     const uint8_t *abase = a_rows + (size_t)kt * kTileK * 2;
 #pragma unroll
     for (int qi = 0; qi < AQ; ++qi) copy16_to_lds(abase + aoff[qi], abuf + (wc + NWC * qi) * 1024);
-    uint8_t *wslot = wslot_of(st);
+  };
+
+  // the weight tiles of step j, straight into registers
+  auto load_w = [&](int j, u32x4 (&wv)[NW][CT]) __attribute__((always_inline)) {
+    const int kt = min(ktile(j), KC - 1);
 #pragma unroll
     for (int i = 0; i < NW; ++i)
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
         const size_t tile = (size_t)min(ctw + ct, NTL - 1) * KC + kt;
-        copy16_to_lds(p.w[i] + tile * kTileBytes + lane * 16, wslot + (i * CT + ct) * kTileBytes);
+        wv[i][ct] = reinterpret_cast<const u32x4 *>(p.w[i] + tile * kTileBytes)[lane];
       }
-    uint8_t *slot = slot_of(st);
-#pragma unroll
-    for (int i = 0; i < NW; ++i) {
-      const uint8_t *sbase = reinterpret_cast<const uint8_t *>(p.scales[i]) + (size_t)kt * GPC * 16 * SB;
-#pragma unroll
-      for (int q = 0; q < SQ; ++q)
-        if (q * 64 + lane < CT * SU) copy16_to_lds(sbase + soff[q], slot + i * MS + q * 1024);
-      const uint8_t *zbase = has_zp ? p.zeros[i] + (size_t)kt * GPC * 8 : sbase;
-#pragma unroll
-      for (int q = 0; q < ZQ; ++q)
-        if (q * 64 + lane < CT * ZU) copy4_to_lds(zbase + zoff[q], slot + NW * MS + i * MZ + q * 256);
-    }
-    {
-      const f16 *gsrc = rms ? p.gamma + kt * kTileK + lane * 8 : p.A + lane * 8;
-      if (lane < 16) copy16_to_lds(gsrc, slot + NW * (MS + MZ));
-    }
   };
 
   f32x4 acc[NW][MT][CT];
@@ -198,12 +222,10 @@ tile_kernel(const GemmArgs p) {
   // l + 64i (i = 0..3), i.e. row 16*(w/2) + 4i + l/16, and keeps that row's
   // running sum of squares in ssq[i]
   float ssq[4] = {0.f, 0.f, 0.f, 0.f};
-  auto rms_pass = [&](int st) __attribute__((always_inline)) {
+  auto rms_pass = [&](int j, int st) __attribute__((always_inline)) {
     const int sl = wave & 1, h = wave >> 1;
     uint8_t *ab = smem + st * STAGE + sl * kTileABytes;
-    // gamma of slice sl's k tile sits in the slot of wavefront (0, sl)
-    const f16 *gm = reinterpret_cast<const f16 *>(smem + st * STAGE + NKS * kTileABytes +
-                                                 (sl * NWC) * SLOT + WB + NW * (MS + MZ));
+    const f16 *gm = p.gamma + (size_t)min(j * NKS + sl, KC - 1) * kTileK;  // slice sl's k tile
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int e = lane + 64 * i;
@@ -221,12 +243,12 @@ tile_kernel(const GemmArgs p) {
   };
 
   const int zshift = 4 * (c & 1);
-  auto compute = [&](int st) __attribute__((always_inline)) {
+  auto compute = [&](int j, int st, const u32x4 (&wreg)[NW][CT]) __attribute__((always_inline)) {
     // row 16mt + c, chunk 4d + kq sits at slot row * 16 + ((4d + kq) ^ c): the
     // 16 rows of one operand read land in 16 different chunk positions
     const uint8_t *abuf = abuf_of(st) + c * 256;
-    const uint8_t *slot = slot_of(st);
-    const u32x4 *wsl = reinterpret_cast<const u32x4 *>(wslot_of(st)) + lane;
+    const uint8_t *blk = mblk_of(j / MBS);
+    const int jb = j % MBS;  // step within the metadata block
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
     f16x8 a[4][MT];
 #pragma unroll
@@ -238,9 +260,9 @@ tile_kernel(const GemmArgs p) {
     for (int i = 0; i < NW; ++i) {
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
-        const u32x4 wv = wsl[(i * CT + ct) * 64];
-        const uint8_t *sp = slot + i * MS + ((ct * GPC) * 16 + c) * SB;  // scale of group 0
-        const uint8_t *zp = slot + NW * MS + i * MZ + (ct * GPC) * 8 + (c >> 1);
+        const u32x4 wv = wreg[i][ct];
+        const uint8_t *sp = blk + i * BS + jb * PSS + ((ct * GPC) * 16 + c) * SB;  // group 0
+        const uint8_t *zp = blk + NW * BS + i * BZ + jb * PSZ + (ct * GPC) * 8 + (c >> 1);
         auto scale = [&](int g2) __attribute__((always_inline)) {
           if constexpr (SF32)
             return *reinterpret_cast<const float *>(sp + g2 * 16 * SB);
@@ -297,22 +319,35 @@ tile_kernel(const GemmArgs p) {
     }
   };
 
-  // Pipeline: steps 0 .. ST-2 are issued up front; step j waits for its
-  // copies, meets the other wavefronts (which frees the stage read in step
-  // j - 1), issues step j + ST - 1 into that stage, and computes.
+  // Pipeline: the copies of steps 0 .. ST-2 and the weights of steps
+  // 0 .. D-1 are issued up front; step j waits for its copies, meets the
+  // other wavefronts (which frees the stage read in step j - 1), issues the
+  // copies of step j + ST - 1 into that stage and the weights of step j + D,
+  // and computes.
+  u32x4 wring[D + 1][NW][CT];
 #pragma unroll
   for (int u = 0; u < ST - 1; ++u) issue(u, u);
+#pragma unroll
+  for (int u = 0; u < D; ++u) load_w(u, wring[u]);
   int st = 0;
-  for (int j = 0; j < nsteps; ++j) {
+  auto step = [&](int j, auto uc) __attribute__((always_inline)) {
+    constexpr int u = decltype(uc)::value;  // j % (D + 1)
     wait_vmcnt<AFTER>();  // this wavefront's copies of step j have landed
     lds_only_barrier();   // everyone's have, and step j - 1's reads are done
     issue(j + ST - 1, st == 0 ? ST - 1 : st - 1);
+    load_w(j + D, wring[(u + D) % (D + 1)]);
     if (rms) {
-      rms_pass(st);
+      rms_pass(j, st);
       lds_only_barrier();
     }
-    if (ktile(j) < KC) compute(st);
+    if (ktile(j) < KC) compute(j, st, wring[u]);
     st = st == ST - 1 ? 0 : st + 1;
+  };
+  for (int j0 = 0; j0 < nsteps; j0 += D + 1) {
+    step(j0, std::integral_constant<int, 0>{});
+    if (j0 + 1 < nsteps) step(j0 + 1, std::integral_constant<int, 1>{});
+    if (j0 + 2 < nsteps) step(j0 + 2, std::integral_constant<int, 2>{});
+    if (j0 + 3 < nsteps) step(j0 + 3, std::integral_constant<int, 3>{});
   }
   __syncthreads();  // every step and every copy done: the stages become reduction scratch
 
@@ -419,9 +454,7 @@ int tile_ct(bool wide, bool gate_up) { return (wide && !gate_up) ? 2 : 1; }
 
 size_t tile_lds_bytes(int ct, int group, int scale_bytes, bool gate_up) {
   const int nw = gate_up ? 2 : 1;
-  return (size_t)tile_stages(ct, group, scale_bytes, nw) *
-             tile_stage_bytes(ct, group, scale_bytes, nw) +
-         tile_rms_bytes();
+  return (size_t)tile_lds(tile_stages(ct, group, scale_bytes, nw), ct, group, scale_bytes, nw);
 }
 
 int tile_columns(int ct) { return kTileNWC * ct * kTileN; }
