@@ -6,10 +6,13 @@ fused call (w4a16_gemm) over one resident input set; input sets rotate so the
 36.8 MB of packed weights per call come from HBM, not from the 256 MiB
 Infinity Cache.  `value` is algorithmic bytes per call / time per call.
 
-Also reported (stderr table and the JSON `m_sweep` field): the same shape for
-M = 2..128, with µs, TFLOP/s (2MNK / t, croqtile tutorial "TFLOPS"), GB/s and
-the fraction of the HBM and fp16-MFMA peaks; a streaming-read probe of the
-achievable HBM rate; and the CPU oracle timed on the host's cores.
+Also reported (stderr table and the JSON `m_sweep` / `extras` fields): the
+same shape for M = 2..128, with µs, TFLOP/s (2MNK / t, croqtile tutorial
+"TFLOPS"), GB/s and the fraction of the HBM and fp16-MFMA peaks; the group
+sweep at M=16 K=N=4096 with the fused bias+ReLU epilogue and RMSNorm prologue
+against their unfused chains (analytic bytes beside measured time); the fused
+gate_up SwiGLU at M=32; a streaming-read probe of the achievable HBM rate; and
+the CPU oracle timed on the host's cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
                        [--profile-kernel M [--eager]]
@@ -145,6 +148,139 @@ def time_calls(sets, steps, warmup, ws):
     return us, wall, n
 
 
+class DevProblem:
+    """R rotating device input sets of one W4A16 shape: packed weights (one or
+    two streams), A, bias and gamma, all drawn on the device with the
+    recipe's distributions (codes U{0..15}, scales U[0.001, 0.02], zero-points
+    U{0..15}, A ~ N(0,1), bias ~ N(0, 0.1), gamma ~ N(1, 0.1))."""
+
+    def __init__(self, M, K, N, group, R, n_weights=1, seed=100):
+        import torch
+        import decode_w4a16_repack_amd as w4
+        g = torch.Generator(device="cuda")
+        g.manual_seed(seed)
+        G = K // group
+        self.M, self.K, self.N, self.group = M, K, N, group
+        self.sets = []
+        for _ in range(R):
+            ws_ = []
+            for _ in range(n_weights):
+                q = torch.randint(0, 256, (N, K // 2), dtype=torch.uint8, device="cuda", generator=g)
+                sc = (torch.rand((N, G), device="cuda", generator=g) * 0.019 + 0.001).half()
+                z = torch.randint(0, 256, (N, (G + 1) // 2), dtype=torch.uint8, device="cuda", generator=g)
+                ws_.append(w4.repack(q, sc, z, K, N, group))
+                del q, sc, z
+            A = torch.randn((M, K), device="cuda", generator=g).half()
+            bias = (torch.randn((N,), device="cuda", generator=g) * 0.1).half()
+            gamma = (1.0 + 0.1 * torch.randn((K,), device="cuda", generator=g)).half()
+            out = torch.empty((M, N), dtype=torch.float16, device="cuda")
+            self.sets.append({"A": A, "w": ws_, "bias": bias, "gamma": gamma, "out": out})
+        # scratch of the unfused chains (shared: rewritten by every call)
+        self.tmp = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        self.tmp2 = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        self.an = torch.empty((M, K), dtype=torch.float16, device="cuda")
+        torch.cuda.synchronize()
+
+
+def time_graph(call, sets, steps=200, warmup=10):
+    """us per call of call(set) over the rotating sets, graph-replayed, HIP
+    events on the replay stream (as time_calls)."""
+    import torch
+    for i in range(max(warmup, len(sets))):
+        call(sets[i % len(sets)])
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(gr, stream=stream):
+            for st in sets:
+                call(st)
+    reps = max(1, steps // len(sets))
+    with torch.cuda.stream(stream):
+        gr.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            gr.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / (reps * len(sets))
+
+
+def extras(ws):
+    """The pages' other workloads: the group sweep at M=16 K=N=4096 with the
+    fused bias+ReLU epilogue and the fused RMSNorm prologue against their
+    unfused chains (analytic bytes beside measured time, "Fusion benchmark"
+    page), and the fused gate_up SwiGLU at M=32 K=5120 N=13824."""
+    import torch
+    import decode_w4a16_repack_amd as w4
+    res = {"group_sweep_m16_k4096_n4096": [], "gate_up_m32_k5120_n13824_g128": None}
+    M, K_, N_ = 16, 4096, 4096
+    for g in (16, 32, 64, 128):
+        byt = algorithmic_bytes(M, K_, N_, g)
+        R = max(2, math.ceil(2 * INFINITY_CACHE / byt))
+        pr = DevProblem(M, K_, N_, g, R, seed=200 + g)
+        sets = pr.sets
+        t_plain = time_graph(lambda st: w4.gemm(st["A"], st["w"][0], out=st["out"], workspace=ws), sets)
+        t_bias_fused = time_graph(lambda st: w4.gemm(st["A"], st["w"][0], epilogue="bias_relu",
+                                                     bias=st["bias"], out=st["out"], workspace=ws), sets)
+
+        def unfused_bias(st):
+            w4.gemm(st["A"], st["w"][0], out=pr.tmp, workspace=ws)
+            w4.add_bias(pr.tmp, st["bias"], out=pr.tmp2)
+            w4.relu(pr.tmp2, out=st["out"])
+        t_bias_unfused = time_graph(unfused_bias, sets)
+        t_rms_fused = time_graph(lambda st: w4.gemm(st["A"], st["w"][0], gamma=st["gamma"], eps=1e-6,
+                                                    out=st["out"], workspace=ws), sets)
+
+        def unfused_rms(st):
+            w4.rmsnorm(st["A"], st["gamma"], 1e-6, out=pr.an)
+            w4.gemm(pr.an, st["w"][0], out=st["out"], workspace=ws)
+        t_rms_unfused = time_graph(unfused_rms, sets)
+        row = {
+            "group": g, "rotating_sets": R, "level": "HBM (rotated inputs), graph replay",
+            "gemm_us": t_plain, "gemm_GBps": byt / t_plain / 1e3,
+            "gemm_pct_hbm_peak": 100 * byt / t_plain / 1e3 / HBM_PEAK_GBS,
+            "bias_relu_fused_us": t_bias_fused, "bias_relu_unfused_us": t_bias_unfused,
+            # output side, fp16: fused writes 2MN; the unfused chain writes the
+            # GEMM output, reads+writes it in the bias pass and again in ReLU
+            "bias_relu_analytic_output_bytes": {"fused": 2 * M * N_, "unfused": 10 * M * N_,
+                                                "saved": 8 * M * N_},
+            "rmsnorm_fused_us": t_rms_fused, "rmsnorm_unfused_us": t_rms_unfused,
+            # activation side, fp16: fused reads A once; unfused reads A,
+            # writes the normalized A and the GEMM reads it back
+            "rmsnorm_analytic_a_side_bytes": {"fused": 2 * M * K_, "unfused": 6 * M * K_,
+                                              "saved": 4 * M * K_},
+        }
+        res["group_sweep_m16_k4096_n4096"].append(row)
+        log(f"[bench] C4 g={g:3d}: gemm {t_plain:6.2f} us ({row['gemm_pct_hbm_peak']:4.1f}% HBM)  "
+            f"bias+relu fused {t_bias_fused:6.2f} / unfused {t_bias_unfused:6.2f} us  "
+            f"rmsnorm fused {t_rms_fused:6.2f} / unfused {t_rms_unfused:6.2f} us")
+        del pr, sets
+        torch.cuda.empty_cache()
+    # gate_up SwiGLU
+    M, g = 32, 128
+    byt = algorithmic_bytes(M, K, N, g, n_weights=2)
+    R = max(2, math.ceil(2 * INFINITY_CACHE / byt))
+    pr = DevProblem(M, K, N, g, R, n_weights=2, seed=300)
+    t_gu = time_graph(lambda st: w4.gemm_gate_up(st["A"], st["w"][0], st["w"][1], out=st["out"],
+                                                 workspace=ws), pr.sets)
+    t_two = time_graph(lambda st: (w4.gemm(st["A"], st["w"][0], out=pr.tmp, workspace=ws),
+                                   w4.gemm(st["A"], st["w"][1], out=pr.tmp2, workspace=ws)), pr.sets)
+    res["gate_up_m32_k5120_n13824_g128"] = {
+        "rotating_sets": R, "level": "HBM (rotated inputs), graph replay",
+        "us": t_gu, "GBps": byt / t_gu / 1e3, "pct_hbm_peak": 100 * byt / t_gu / 1e3 / HBM_PEAK_GBS,
+        "TFLOPs": flops(M, n_weights=2) / t_gu / 1e6, "algorithmic_bytes": byt,
+        "two_plain_gemms_us": t_two,
+    }
+    log(f"[bench] C5 gate_up M=32: {t_gu:.2f} us ({res['gate_up_m32_k5120_n13824_g128']['pct_hbm_peak']:.1f}% HBM); "
+        f"two plain GEMMs {t_two:.2f} us")
+    del pr
+    torch.cuda.empty_cache()
+    return res
+
+
 def self_check(sets, ws):
     """Cheap checks of the timed launch configuration that need no oracle:
     every output finite, and a repeated call bit-identical (fixed-order
@@ -268,6 +404,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--profile-kernel", type=int, default=0,
                     help="only launch the GEMM at this M (for rocprofv3)")
     ap.add_argument("--eager", action="store_true",
@@ -343,6 +480,7 @@ def main():
             del s2
             torch.cuda.empty_cache()
 
+    extra = None if args.no_extras else extras(ws)
     probe = hbm_probe()
     log(f"[bench] streaming-read probe: {probe:.1f} GB/s")
     cpu = None if args.no_cpu else cpu_baseline()
@@ -375,6 +513,7 @@ def main():
         "cpu_baseline": cpu,
         "self_check": parity,
         "m_sweep": sweep,
+        "extras": extra,
         "page_context": {"M1_us_H200": PAGE_M1_US, "note": "other hardware, context only"},
     }
     print(json.dumps(line), flush=True)
