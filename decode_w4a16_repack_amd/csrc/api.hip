@@ -64,10 +64,7 @@ void fill_workspace(GemmArgs &a, const Plan &pl, void *ws) {
   a.split = pl.split;
   a.cps = pl.cps;
   a.rows_pow2 = pl.rows_pow2;
-  a.lds_g = pl.lds_g;
   a.lds_s = pl.lds_s;
-  a.lds_z = pl.lds_z;
-  a.gr = pl.gr;
   a.lds_r = pl.lds_r;
   a.ws_part = pl.ws_total ? reinterpret_cast<float *>(b + pl.ws_part_off) : nullptr;
   a.ws_rms = pl.ws_total ? reinterpret_cast<float *>(b + pl.ws_rms_off) : nullptr;

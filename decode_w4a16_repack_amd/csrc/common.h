@@ -21,24 +21,6 @@ constexpr int kTileN = 16;       // columns of one packed weight tile
 constexpr int kTileBytes = 1024; // bytes of one packed tile (64 lanes x 16 B)
 constexpr int kMaxSplitBlocks = 1024;  // split-K only below this many workgroups
 
-// Tile configurations of the ring kernel: MT 16-row m tiles per wavefront,
-// NWC column tiles x NWK k slices of wavefronts per workgroup, DA packed k
-// tiles per round.
-struct RingCfg {
-  int mt, nwc, nwk, da;
-};
-constexpr int kNumRingCfgs = 5;
-extern const RingCfg kRingCfgs[kNumRingCfgs];
-
-// Tile configurations of the small-M one-shot kernel: NWC column tiles x NWK
-// k slices per workgroup, at most CW packed k tiles per wavefront, PD of
-// them in flight.
-struct OneshotCfg {
-  int mt, nwc, nwk, cw, pd;
-};
-constexpr int kNumOneshotCfgs = 3;
-extern const OneshotCfg kOneshotCfgs[kNumOneshotCfgs];
-
 // Tile configurations of the small-M stream kernel: CPW 16-column tiles per
 // wavefront, KPW 128-k tiles per wavefront (its activation fragments stay in
 // registers), NWK wavefronts (k slices) per workgroup, PD tiles in flight.
@@ -88,24 +70,21 @@ struct GemmArgs {
   uint32_t *ws_cnt;   // [blocks] arrival counters, zero between calls
   int split;          // number of K splits across workgroups
   int cps;            // 128-wide k tiles per split
-  int rows_pow2;      // staged activation rows: power of two >= min(M, 16*MT)
-  int lds_g;          // byte offset of the staged RMSNorm weight in LDS
-  int lds_s, lds_z;   // byte offsets of the staged scales / zero-points in LDS
-  int gr;             // staged groups per column tile
-  int lds_r;          // byte offset of the sum-of-squares scratch in LDS
+  int rows_pow2;      // stream kernel: activation rows staged in LDS (power of two >= M)
+  int lds_s;          // stream kernel: bytes of one wavefront's private LDS region
+  int lds_r;          // stream kernel: byte offset of the sum-of-squares scratch in LDS
 };
 
 // Launch plan of one GEMM call, a pure function of the shape.
-enum PlanKind { kKindRing = 0, kKindOneshot = 1, kKindStream = 2, kKindTile = 3 };
+enum PlanKind { kKindStream = 2, kKindTile = 3 };
 
 struct Plan {
-  int kind;     // PlanKind: ring.hip (kRingCfgs), oneshot.hip (kOneshotCfgs), stream.hip
-                // (kStreamCfgs), tile.hip
+  int kind;     // PlanKind: stream.hip (kStreamCfgs) or tile.hip
   int cfg;      // index into the kernel's configuration table
   int gx, gy, gz;
   int split, cps;
   int rows_pow2;
-  int lds_g, lds_s, lds_z, gr, lds_r;
+  int lds_s, lds_r;
   int alds;  // stream kernel: activation rows staged through LDS
   size_t lds_bytes;
   size_t ws_part_off, ws_rms_off, ws_cnt_off, ws_total;
@@ -116,9 +95,6 @@ struct Plan {
 Plan make_plan(int M, int K, int N, int group, int scale_bytes, bool gate_up,
                int force_kind = -1, int force_cfg = -1, int force_split = 0);
 
-hipError_t launch_oneshot(const GemmArgs &a, const Plan &p, int group, bool scale_f32,
-                          bool gate_up, hipStream_t stream);
-
 hipError_t launch_stream(const GemmArgs &a, const Plan &p, int group, bool scale_f32,
                          bool gate_up, hipStream_t stream);
 
@@ -128,9 +104,6 @@ int tile_ct(bool wide, bool gate_up);
 size_t tile_lds_bytes(int ct, int group, int scale_bytes, bool gate_up);
 int tile_columns(int ct);
 hipError_t launch_tile(const GemmArgs &a, const Plan &p, int group, bool scale_f32,
-                       bool gate_up, hipStream_t stream);
-
-hipError_t launch_ring(const GemmArgs &a, const Plan &p, int group, bool scale_f32,
                        bool gate_up, hipStream_t stream);
 
 hipError_t launch_gemm(const GemmArgs &a, const Plan &p, int group,

@@ -63,76 +63,6 @@ __device__ __forceinline__ f32x4 mfma16(f16x8 a, f16x8 b, f32x4 c) {
 
 __device__ __forceinline__ float silu(float v) { return v / (1.0f + expf(-v)); }
 
-// Contract one packed k tile (128 k, four 32-deep MFMA steps) of one 16-column
-// weight tile with MT 16-row m tiles of activations and add the scaled group
-// sums into acc.
-//  * a[d][t]: this lane's activation fragment of 32-k step d for m tile t
-//    (row l%16 of the tile, k slots 8*(l/16)..+7 of the step).
-//  * zp_of(gl) / scale_of(gl): zero-point (0..15) / scale of group gl
-//    (0 .. 128/G - 1) of the tile for this lane's column; each is asked for
-//    once per group.
-template <int MT, int G, class ZpOf, class ScaleOf>
-__device__ __forceinline__ void contract_tile(f32x4 (&acc)[MT], const u32x4 &w,
-                                              const f16x8 (&a)[4][MT], int kq, ZpOf zp_of,
-                                              ScaleOf scale_of) {
-  constexpr int GPC = 128 / G;
-  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
-  // zero-point constants of this lane's B slots (one group per 32-k step
-  // for G >= 32; for G = 16 the slot's group is 2d + kq/2)
-  f16x2 zlo[4], zhi[4];
-  if constexpr (G >= 32) {
-#pragma unroll
-    for (int gl = 0; gl < GPC; ++gl) {
-      f16x2 l, h;
-      zero_consts((uint32_t)zp_of(gl), l, h);
-#pragma unroll
-      for (int d = 0; d < 4; ++d)
-        if ((32 * d) / G == gl) { zlo[d] = l; zhi[d] = h; }
-    }
-  } else {
-#pragma unroll
-    for (int d = 0; d < 4; ++d) zero_consts((uint32_t)zp_of(2 * d + (kq >> 1)), zlo[d], zhi[d]);
-  }
-  if constexpr (G >= 32) {
-    constexpr int SPG = G / 32;  // MFMA steps per group
-    f32x4 accg[MT];
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      const f16x8 b = unpack8(w[d], zlo[d], zhi[d]);
-#pragma unroll
-      for (int t = 0; t < MT; ++t)
-        accg[t] = mfma16(a[d][t], b, (d % SPG == 0) ? zero4 : accg[t]);
-      if ((d + 1) % SPG == 0) {
-        const float s = scale_of((32 * d) / G);
-#pragma unroll
-        for (int t = 0; t < MT; ++t)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[t][e] = __builtin_fmaf(accg[t][e], s, acc[t][e]);
-      }
-    }
-  } else {
-    // group 16: k slots kq = 0, 1 belong to group 2d, kq = 2, 3 to 2d + 1;
-    // two MFMAs per step, each with the other group's B lanes zeroed
-    const f16x8 zero8 = {};
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      const f16x8 b = unpack8(w[d], zlo[d], zhi[d]);
-      const f16x8 blo = (kq < 2) ? b : zero8;
-      const f16x8 bhi = (kq < 2) ? zero8 : b;
-      const float s0 = scale_of(2 * d);
-      const float s1 = scale_of(2 * d + 1);
-#pragma unroll
-      for (int t = 0; t < MT; ++t) {
-        const f32x4 p0 = mfma16(a[d][t], blo, zero4);
-        const f32x4 p1 = mfma16(a[d][t], bhi, zero4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          acc[t][e] = __builtin_fmaf(p1[e], s1, __builtin_fmaf(p0[e], s0, acc[t][e]));
-      }
-    }
-  }
-}
-
 // ---------------------------------------------------------------------------
 // Contraction with the zero-point taken out of the weights.
 //
@@ -226,26 +156,6 @@ __device__ __forceinline__ void contract_tile_sub(f32x4 &acc, const u32x4 &w, co
       apply(p1, 2 * d + 1);
     }
   }
-}
-
-// contract_tile with the activation fragments read from LDS:
-//  * a_lane[t]: this lane's 16-byte activation slot of step 0 for m tile t;
-//    step d is d * dstride bytes further.  The tile is in fragment order
-//    (slot ((d * 4 + kq) * R + row)), so the 16 rows one MFMA operand reads
-//    are 16 consecutive slots.  Lanes whose row is beyond M point at a valid
-//    row instead: an A row only feeds its own output row, never written.
-template <int MT, int G, class ZpOf, class ScaleOf>
-__device__ __forceinline__ void contract_tile_frag(f32x4 (&acc)[MT], const u32x4 &w,
-                                                   const uint8_t *const (&a_lane)[MT],
-                                                   int dstride, int kq, ZpOf zp_of,
-                                                   ScaleOf scale_of) {
-  f16x8 a[4][MT];
-#pragma unroll
-  for (int d = 0; d < 4; ++d)
-#pragma unroll
-    for (int t = 0; t < MT; ++t)
-      a[d][t] = *reinterpret_cast<const f16x8 *>(a_lane[t] + d * dstride);
-  contract_tile<MT, G>(acc, w, a, kq, zp_of, scale_of);
 }
 
 // Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4):
