@@ -49,7 +49,7 @@ INFINITY_CACHE = 256 << 20
 PAGE_M1_US = 69.5  # the pages' M=1 time for this shape (H200, context only)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemv_m1.json")
 KERNEL_SOURCES = ["decode_w4a16_repack_amd/csrc/" + f for f in
-                  ("stream.hip", "oneshot.hip", "ring.hip", "device.h", "gemm.hip", "common.h")]
+                  ("stream.hip", "tile.hip", "device.h", "gemm.hip", "common.h")]
 COPY_PROBE_BYTES = 256 << 20  # plain copy of known size, counter calibration
 
 
@@ -278,7 +278,60 @@ def extras(ws):
         f"two plain GEMMs {t_two:.2f} us")
     del pr
     torch.cuda.empty_cache()
+    res["split_sweep_m8"] = split_sweep(ws)
     return res
+
+
+# The M=8 decode shapes the "Small-M split-K retune" update tunes: (name, K,
+# N per projection, gate_up).  The gate_up rows are paired projections of
+# N each (4096 x 2*13696 and 5120 x 2*13824 in the update's table).
+SPLIT_SWEEP_SHAPES = [("o_q_proj", 4096, 4096, False), ("down_proj", 13696, 4096, False),
+                      ("gate_up_glm", 4096, 13696, True), ("gate_up_qwen", 5120, 13824, True)]
+
+
+def split_sweep(ws, M=8, group=128):
+    """Each shape at M=8: the automatic plan's time and %HBM, beside every
+    forced split-K factor in {1, 2, 3, 4, 6, 8} the shape can run."""
+    import torch
+    import decode_w4a16_repack_amd as w4
+    rows = []
+    for name, K_, N_, gu in SPLIT_SWEEP_SHAPES:
+        nw = 2 if gu else 1
+        byt = algorithmic_bytes(M, K_, N_, group, n_weights=nw)
+        R = max(2, math.ceil(2 * INFINITY_CACHE / byt))
+        pr = DevProblem(M, K_, N_, group, R, n_weights=nw, seed=400)
+
+        def call(st, split):
+            if gu:
+                w4.gemm_gate_up(st["A"], st["w"][0], st["w"][1], out=st["out"], workspace=ws,
+                                split=split)
+            else:
+                w4.gemm(st["A"], st["w"][0], out=st["out"], workspace=ws, split=split)
+        auto = w4.plan(M, K_, N_, group, gate_up=gu)
+        t_auto = time_graph(lambda st: call(st, 0), pr.sets)
+        forced = {}
+        for sk in (1, 2, 3, 4, 6, 8):
+            try:
+                fp = w4.plan(M, K_, N_, group, gate_up=gu, split=sk)
+            except w4.W4A16Error:
+                continue
+            if fp.split in forced:
+                continue
+            forced[fp.split] = time_graph(lambda st: call(st, sk), pr.sets)
+        best = min(forced, key=forced.get) if forced else auto.split
+        row = {"shape": name, "M": M, "K": K_, "N": N_, "gate_up": gu, "group": group,
+               "rotating_sets": R, "algorithmic_bytes": byt,
+               "auto_kernel": auto.kernel, "auto_split": auto.split, "auto_us": t_auto,
+               "auto_pct_hbm_peak": 100 * byt / t_auto / 1e3 / HBM_PEAK_GBS,
+               "forced_split_us": {str(k): v for k, v in sorted(forced.items())},
+               "best_forced_split": best}
+        rows.append(row)
+        log(f"[bench] split sweep {name:12s} M={M} K={K_} N={N_}{' x2' if gu else ''}: auto sk{auto.split} "
+            f"{t_auto:6.2f} us ({row['auto_pct_hbm_peak']:4.1f}% HBM); forced "
+            + " ".join(f"sk{k}={v:.2f}" for k, v in sorted(forced.items())))
+        del pr
+        torch.cuda.empty_cache()
+    return rows
 
 
 def self_check(sets, ws):

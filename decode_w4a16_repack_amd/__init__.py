@@ -19,11 +19,12 @@ from typing import Optional
 import torch
 
 from . import _lib
+from ._lib import W4A16Error
 
 __all__ = [
     "PackedWeight", "repack", "gemm", "gemm_gate_up", "packed_bytes",
     "workspace_bytes", "layout_version", "add_bias", "relu", "rmsnorm",
-    "probe_read", "probe_copy", "Workspace",
+    "probe_read", "probe_copy", "Workspace", "plan", "Plan", "W4A16Error",
 ]
 
 
@@ -69,6 +70,29 @@ def packed_bytes(K: int, N: int, group: int, scale_dtype: int, has_zp: bool) -> 
 
 def workspace_bytes(M: int, K: int, N: int, group: int, gate_up: bool = False) -> int:
     return _lib.lib().w4a16_workspace_bytes(M, K, N, group, int(gate_up))
+
+
+@dataclass
+class Plan:
+    """The launch a call of one shape makes (w4a16_plan_info)."""
+    kernel: str          # "stream" (M <= 16) or "tile"
+    split: int           # workgroups along K per output tile
+    k_tiles_per_split: int
+    grid: tuple
+    block: int
+    lds_bytes: int
+    workspace_bytes: int
+
+
+def plan(M: int, K: int, N: int, group: int, scale_dtype: int = _lib.SCALE_F16,
+         gate_up: bool = False, split: int = 0) -> Plan:
+    """Host-only query of the plan; split > 0 forces that split-K factor."""
+    info = _lib.PlanInfo()
+    st = _lib.lib().w4a16_plan(M, K, N, group, scale_dtype, int(gate_up), split, info)
+    _lib.check(st, "w4a16_plan")
+    return Plan("stream" if info.kernel == _lib.KERNEL_STREAM else "tile", info.split,
+                info.k_tiles_per_split, tuple(info.grid), info.block, info.lds_bytes,
+                info.workspace_bytes)
 
 
 class Workspace:
@@ -123,8 +147,9 @@ def repack(qweight: torch.Tensor, scales: torch.Tensor, zeros: Optional[torch.Te
 def gemm(A: torch.Tensor, w: PackedWeight, *, epilogue: str = "none",
          bias: Optional[torch.Tensor] = None, gamma: Optional[torch.Tensor] = None,
          eps: float = 1e-6, out: Optional[torch.Tensor] = None,
-         workspace: Optional[Workspace] = None) -> torch.Tensor:
-    """fp16 [M][N] = epilogue(X . dequant(W)), X = A or RMSNorm(A; gamma, eps)."""
+         workspace: Optional[Workspace] = None, split: int = 0) -> torch.Tensor:
+    """fp16 [M][N] = epilogue(X . dequant(W)), X = A or RMSNorm(A; gamma, eps).
+    split > 0 forces that split-K factor (w4a16_gemm_split)."""
     _need_gpu(A, "A", torch.float16)
     M, K = A.shape
     if K != w.K:
@@ -135,11 +160,17 @@ def gemm(A: torch.Tensor, w: PackedWeight, *, epilogue: str = "none",
     if out is None:
         out = torch.empty((M, w.N), dtype=torch.float16, device=A.device)
     _need_gpu(out, "out", torch.float16)
-    ws_n = workspace_bytes(M, K, w.N, w.group, False)
+    if split:
+        ws_n = plan(M, K, w.N, w.group, w.scale_dtype, False, split).workspace_bytes
+    else:
+        ws_n = workspace_bytes(M, K, w.N, w.group, False)
     ws = (workspace or _default_ws).get(ws_n, A.device)
-    st = _lib.lib().w4a16_gemm(_ptr(A), M, K, w.N, w.group, w.scale_dtype, int(w.has_zp),
-                               _ptr(w.data), _lib.EPI[epilogue], _ptr(bias), _ptr(gamma),
-                               float(eps), _ptr(out), _ptr(ws), ws_n, _stream())
+    args = (_ptr(A), M, K, w.N, w.group, w.scale_dtype, int(w.has_zp), _ptr(w.data),
+            _lib.EPI[epilogue], _ptr(bias), _ptr(gamma), float(eps), _ptr(out), _ptr(ws), ws_n)
+    if split:
+        st = _lib.lib().w4a16_gemm_split(*args, split, _stream())
+    else:
+        st = _lib.lib().w4a16_gemm(*args, _stream())
     _lib.check(st, "w4a16_gemm")
     return out
 
@@ -147,8 +178,8 @@ def gemm(A: torch.Tensor, w: PackedWeight, *, epilogue: str = "none",
 def gemm_gate_up(A: torch.Tensor, w_gate: PackedWeight, w_up: PackedWeight, *,
                  gamma: Optional[torch.Tensor] = None, eps: float = 1e-6,
                  out: Optional[torch.Tensor] = None,
-                 workspace: Optional[Workspace] = None) -> torch.Tensor:
-    """fp16 [M][N] = silu(X . Wg) * (X . Wu)."""
+                 workspace: Optional[Workspace] = None, split: int = 0) -> torch.Tensor:
+    """fp16 [M][N] = silu(X . Wg) * (X . Wu); split as in gemm()."""
     _need_gpu(A, "A", torch.float16)
     M, K = A.shape
     for w in (w_gate, w_up):
@@ -162,12 +193,18 @@ def gemm_gate_up(A: torch.Tensor, w_gate: PackedWeight, w_up: PackedWeight, *,
     if out is None:
         out = torch.empty((M, w_gate.N), dtype=torch.float16, device=A.device)
     _need_gpu(out, "out", torch.float16)
-    ws_n = workspace_bytes(M, K, w_gate.N, w_gate.group, True)
+    if split:
+        ws_n = plan(M, K, w_gate.N, w_gate.group, w_gate.scale_dtype, True, split).workspace_bytes
+    else:
+        ws_n = workspace_bytes(M, K, w_gate.N, w_gate.group, True)
     ws = (workspace or _default_ws).get(ws_n, A.device)
-    st = _lib.lib().w4a16_gemm_gate_up(
-        _ptr(A), M, K, w_gate.N, w_gate.group, w_gate.scale_dtype, int(w_gate.has_zp),
-        _ptr(w_gate.data), _ptr(w_up.data), _ptr(gamma), float(eps), _ptr(out),
-        _ptr(ws), ws_n, _stream())
+    args = (_ptr(A), M, K, w_gate.N, w_gate.group, w_gate.scale_dtype, int(w_gate.has_zp),
+            _ptr(w_gate.data), _ptr(w_up.data), _ptr(gamma), float(eps), _ptr(out),
+            _ptr(ws), ws_n)
+    if split:
+        st = _lib.lib().w4a16_gemm_gate_up_split(*args, split, _stream())
+    else:
+        st = _lib.lib().w4a16_gemm_gate_up(*args, _stream())
     _lib.check(st, "w4a16_gemm_gate_up")
     return out
 

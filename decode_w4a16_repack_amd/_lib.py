@@ -25,6 +25,10 @@ ERR_EPILOGUE = -5
 ERR_WORKSPACE = -6
 ERR_ALIGN = -7
 ERR_LAUNCH = -8
+ERR_SPLIT = -9
+
+KERNEL_STREAM = 1
+KERNEL_TILE = 2
 
 SCALE_F16 = 0
 SCALE_F32 = 1
@@ -34,8 +38,16 @@ EXPORTS = [
     "w4a16_packed_bytes", "w4a16_repack", "w4a16_workspace_bytes", "w4a16_gemm",
     "w4a16_gemm_gate_up", "w4a16_status_string", "w4a16_layout_version",
     "w4a16_add_bias", "w4a16_relu", "w4a16_rmsnorm", "w4a16_probe_read",
-    "w4a16_probe_copy",
+    "w4a16_probe_copy", "w4a16_plan", "w4a16_gemm_split", "w4a16_gemm_gate_up_split",
 ]
+
+
+class PlanInfo(ctypes.Structure):
+    """w4a16_plan_info."""
+    _fields_ = [("kernel", ctypes.c_int), ("split", ctypes.c_int),
+                ("k_tiles_per_split", ctypes.c_int), ("grid", ctypes.c_int * 3),
+                ("block", ctypes.c_int), ("lds_bytes", ctypes.c_int),
+                ("workspace_bytes", ctypes.c_size_t)]
 
 
 class W4A16Error(RuntimeError):
@@ -70,6 +82,9 @@ def lib() -> ctypes.CDLL:
         "w4a16_rmsnorm": (I, [P, P, F, I, I, P, P]),
         "w4a16_probe_read": (I, [P, Z, P, P]),
         "w4a16_probe_copy": (I, [P, P, Z, P]),
+        "w4a16_plan": (I, [I, I, I, I, I, I, I, ctypes.POINTER(PlanInfo)]),
+        "w4a16_gemm_split": (I, [P, I, I, I, I, I, I, P, I, P, P, F, P, P, Z, I, P]),
+        "w4a16_gemm_gate_up_split": (I, [P, I, I, I, I, I, I, P, P, P, F, P, P, Z, I, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)

@@ -50,6 +50,19 @@ int check_workspace(const Plan &pl, const void *ws, size_t ws_bytes) {
   return W4A16_OK;
 }
 
+// The automatic plan (split <= 0) or the stream kernel with `split`
+// workgroups along K; W4A16_ERR_SPLIT when that split cannot run the shape.
+int plan_for(int M, int K, int N, int group, int scale_dtype, bool gate_up, int split,
+             Plan &pl) {
+  const int sb = scale_bytes_of(scale_dtype);
+  if (split <= 0) {
+    pl = make_plan(M, K, N, group, sb, gate_up);
+    return W4A16_OK;
+  }
+  pl = make_plan(M, K, N, group, sb, gate_up, kKindStream, -1, split);
+  return pl.kind == kKindStream ? W4A16_OK : W4A16_ERR_SPLIT;
+}
+
 void fill_packed(GemmArgs &a, int slot, const void *packed, int K, int N,
                  int group, int sbytes, bool has_zp) {
   const PackedOffsets off = packed_offsets(K, N, group, sbytes, has_zp);
@@ -110,10 +123,10 @@ size_t w4a16_workspace_bytes(int M, int K, int N, int group, int gate_up) {
   return a > b ? a : b;
 }
 
-int w4a16_gemm(const void *A, int M, int K, int N, int group, int scale_dtype,
-               int has_zp, const void *packed, int epilogue, const void *bias,
-               const void *rms_gamma, float rms_eps, void *out,
-               void *workspace, size_t workspace_bytes, w4a16_stream stream) {
+int w4a16_gemm_split(const void *A, int M, int K, int N, int group, int scale_dtype,
+                     int has_zp, const void *packed, int epilogue, const void *bias,
+                     const void *rms_gamma, float rms_eps, void *out, void *workspace,
+                     size_t workspace_bytes, int split, w4a16_stream stream) {
   const void *pk[1] = {packed};
   int st = check_gemm(A, M, K, N, group, scale_dtype, pk, 1, out);
   if (st != W4A16_OK) return st;
@@ -124,7 +137,9 @@ int w4a16_gemm(const void *A, int M, int K, int N, int group, int scale_dtype,
   if ((bias != nullptr && !aligned16(bias)) ||
       (rms_gamma != nullptr && !aligned16(rms_gamma)))
     return W4A16_ERR_ALIGN;
-  const Plan pl = make_plan(M, K, N, group, scale_bytes_of(scale_dtype), false);
+  Plan pl;
+  st = plan_for(M, K, N, group, scale_dtype, false, split, pl);
+  if (st != W4A16_OK) return st;
   st = check_workspace(pl, workspace, workspace_bytes);
   if (st != W4A16_OK) return st;
 
@@ -146,16 +161,18 @@ int w4a16_gemm(const void *A, int M, int K, int N, int group, int scale_dtype,
                               static_cast<hipStream_t>(stream)));
 }
 
-int w4a16_gemm_gate_up(const void *A, int M, int K, int N, int group,
-                       int scale_dtype, int has_zp, const void *packed_gate,
-                       const void *packed_up, const void *rms_gamma,
-                       float rms_eps, void *out, void *workspace,
-                       size_t workspace_bytes, w4a16_stream stream) {
+int w4a16_gemm_gate_up_split(const void *A, int M, int K, int N, int group,
+                             int scale_dtype, int has_zp, const void *packed_gate,
+                             const void *packed_up, const void *rms_gamma,
+                             float rms_eps, void *out, void *workspace,
+                             size_t workspace_bytes, int split, w4a16_stream stream) {
   const void *pk[2] = {packed_gate, packed_up};
   int st = check_gemm(A, M, K, N, group, scale_dtype, pk, 2, out);
   if (st != W4A16_OK) return st;
   if (rms_gamma != nullptr && !aligned16(rms_gamma)) return W4A16_ERR_ALIGN;
-  const Plan pl = make_plan(M, K, N, group, scale_bytes_of(scale_dtype), true);
+  Plan pl;
+  st = plan_for(M, K, N, group, scale_dtype, true, split, pl);
+  if (st != W4A16_OK) return st;
   st = check_workspace(pl, workspace, workspace_bytes);
   if (st != W4A16_OK) return st;
 
@@ -177,6 +194,46 @@ int w4a16_gemm_gate_up(const void *A, int M, int K, int N, int group,
                               static_cast<hipStream_t>(stream)));
 }
 
+int w4a16_gemm(const void *A, int M, int K, int N, int group, int scale_dtype,
+               int has_zp, const void *packed, int epilogue, const void *bias,
+               const void *rms_gamma, float rms_eps, void *out,
+               void *workspace, size_t workspace_bytes, w4a16_stream stream) {
+  return w4a16_gemm_split(A, M, K, N, group, scale_dtype, has_zp, packed, epilogue, bias,
+                          rms_gamma, rms_eps, out, workspace, workspace_bytes, 0, stream);
+}
+
+int w4a16_gemm_gate_up(const void *A, int M, int K, int N, int group,
+                       int scale_dtype, int has_zp, const void *packed_gate,
+                       const void *packed_up, const void *rms_gamma,
+                       float rms_eps, void *out, void *workspace,
+                       size_t workspace_bytes, w4a16_stream stream) {
+  return w4a16_gemm_gate_up_split(A, M, K, N, group, scale_dtype, has_zp, packed_gate,
+                                  packed_up, rms_gamma, rms_eps, out, workspace,
+                                  workspace_bytes, 0, stream);
+}
+
+int w4a16_plan(int M, int K, int N, int group, int scale_dtype, int gate_up, int split,
+               w4a16_plan_info *info) {
+  if (info == nullptr) return W4A16_ERR_NULL;
+  if (M < 1 || M > kMaxDim) return W4A16_ERR_SHAPE;
+  int st = check_kn(K, N, group);
+  if (st != W4A16_OK) return st;
+  if (scale_bytes_of(scale_dtype) == 0) return W4A16_ERR_DTYPE;
+  Plan pl;
+  st = plan_for(M, K, N, group, scale_dtype, gate_up != 0, split, pl);
+  if (st != W4A16_OK) return st;
+  info->kernel = pl.kind == kKindStream ? W4A16_KERNEL_STREAM : W4A16_KERNEL_TILE;
+  info->split = pl.split;
+  info->k_tiles_per_split = pl.cps;
+  info->grid[0] = pl.gx;
+  info->grid[1] = pl.gy;
+  info->grid[2] = pl.gz;
+  info->block = pl.block;
+  info->lds_bytes = (int)pl.lds_bytes;
+  info->workspace_bytes = pl.ws_total;
+  return W4A16_OK;
+}
+
 const char *w4a16_status_string(int status) {
   switch (status) {
     case W4A16_OK: return "ok";
@@ -188,6 +245,7 @@ const char *w4a16_status_string(int status) {
     case W4A16_ERR_WORKSPACE: return "workspace missing or too small";
     case W4A16_ERR_ALIGN: return "device pointer not 16-byte aligned";
     case W4A16_ERR_LAUNCH: return "kernel launch failed";
+    case W4A16_ERR_SPLIT: return "forced split-K factor not possible for this shape";
     default: return "unknown status";
   }
 }

@@ -82,6 +82,7 @@ struct Plan {
   int kind;     // PlanKind: stream.hip (kStreamCfgs) or tile.hip
   int cfg;      // index into the kernel's configuration table
   int gx, gy, gz;
+  int block;  // threads per workgroup
   int split, cps;
   int rows_pow2;
   int lds_s, lds_r;
@@ -103,6 +104,7 @@ hipError_t launch_stream(const GemmArgs &a, const Plan &p, int group, bool scale
 int tile_ct(bool wide, bool gate_up);
 size_t tile_lds_bytes(int ct, int group, int scale_bytes, bool gate_up);
 int tile_columns(int ct);
+int tile_threads();
 hipError_t launch_tile(const GemmArgs &a, const Plan &p, int group, bool scale_f32,
                        bool gate_up, hipStream_t stream);
 

@@ -57,9 +57,12 @@ bool plan_stream(Plan &p, int M, int K, int N, int group, int scale_bytes, bool 
   const int per_wg = c.nwk * c.kpw;  // k tiles one workgroup covers
   p.gx = (NTL + c.cpw - 1) / c.cpw;
   p.gz = 1;
+  p.block = 64 * c.nwk;
   const int base = p.gx * p.gz;
-  int S = choose_split(base, c.nwk, KC, force_split);
   const int s_min = (KC + per_wg - 1) / per_wg;
+  // a forced split must leave every workgroup at most its NWK x KPW tiles
+  if (force_split > 0 && (force_split < s_min || force_split > KC)) return false;
+  int S = choose_split(base, c.nwk, KC, force_split);
   if (S < s_min) S = s_min;
   if (S > KC) S = KC;
   if (S > 1 && NTL * p.gz > kMaxSplitBlocks) return false;  // one arrival counter per column tile
@@ -113,6 +116,7 @@ void plan_tile(Plan &p, int M, int K, int N, int group, int scale_bytes, bool ga
   const int ct = tile_ct(p.cfg == 1, gate_up);
   p.gx = (N + tile_columns(ct) - 1) / tile_columns(ct);
   p.gy = 1;
+  p.block = tile_threads();
   p.split = 1;
   p.cps = K / kTileK;
   p.lds_bytes = tile_lds_bytes(ct, group, scale_bytes, gate_up);

@@ -312,7 +312,13 @@ stream_kernel(const GemmArgs p) {
   // 8. k splits across workgroups (narrow grids and very deep k only): the
   //    finishing wavefronts store partials; the finishing wavefront of the
   //    last workgroup to arrive (counted per column tile) sums them in split
-  //    order
+  //    order.  Partials, sums of squares and counters are agent-scope atomic
+  //    accesses, coherent across the XCDs' separate L2 caches by themselves;
+  //    the only ordering needed is that a wavefront's partial stores have
+  //    completed before its arrival is counted (a wait on its own stores),
+  //    and the last arrival reads them only after its count returned.  A
+  //    device-wide fence instead would write back and invalidate the whole
+  //    L2 of the XCD once per finishing wavefront.
   if (S > 1) {
     const size_t cnt = (size_t)blockIdx.z * NTL + ct0 + wfin;  // per column tile
 #pragma unroll
@@ -321,16 +327,15 @@ stream_kernel(const GemmArgs p) {
       if (row < mrows) {
 #pragma unroll
         for (int i = 0; i < NW; ++i)
-          p.ws_part[(((size_t)s * NW + i) * p.M + m0 + row) * p.N + ncol] = fin[i][e];
-        if (rms && c == 0) p.ws_rms[(cnt * S + s) * 16 + row] = rs[e];
+          store_agent(&p.ws_part[(((size_t)s * NW + i) * p.M + m0 + row) * p.N + ncol], fin[i][e]);
+        if (rms && c == 0) store_agent(&p.ws_rms[(cnt * S + s) * 16 + row], rs[e]);
       }
     }
-    __threadfence();
+    wait_stores();
     int last = 0;
-    if (lane == 0) last = atomicAdd(&p.ws_cnt[cnt], 1u) == (unsigned)(S - 1);
+    if (lane == 0) last = count_arrival(&p.ws_cnt[cnt]) == (unsigned)(S - 1);
     last = __shfl(last, 0);
     if (!last) return;
-    __threadfence();
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int row = 4 * kq + e;
@@ -340,18 +345,18 @@ stream_kernel(const GemmArgs p) {
           float v = 0.f;
           for (int s2 = 0; s2 < S; ++s2)
             v += (s2 == s) ? fin[i][e]
-                           : p.ws_part[(((size_t)s2 * NW + i) * p.M + m0 + row) * p.N + ncol];
+                           : load_agent(&p.ws_part[(((size_t)s2 * NW + i) * p.M + m0 + row) * p.N + ncol]);
           fin[i][e] = v;
         }
         if (rms) {
           float v = 0.f;
           for (int s2 = 0; s2 < S; ++s2)
-            v += (s2 == s) ? rs[e] : p.ws_rms[(cnt * S + s2) * 16 + row];
+            v += (s2 == s) ? rs[e] : load_agent(&p.ws_rms[(cnt * S + s2) * 16 + row]);
           rs[e] = v;
         }
       }
     }
-    if (lane == 0) p.ws_cnt[cnt] = 0u;
+    if (lane == 0) reset_arrival(&p.ws_cnt[cnt]);
   }
 
   // 9. epilogue, one fp16 write per output

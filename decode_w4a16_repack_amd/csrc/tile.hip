@@ -459,6 +459,8 @@ size_t tile_lds_bytes(int ct, int group, int scale_bytes, bool gate_up) {
 
 int tile_columns(int ct) { return kTileNWC * ct * kTileN; }
 
+int tile_threads() { return 64 * kTileNWave; }
+
 hipError_t launch_tile(const GemmArgs &a, const Plan &pl, int group, bool scale_f32,
                        bool gate_up, hipStream_t stream) {
   switch (group) {

@@ -65,7 +65,8 @@ typedef enum {
   W4A16_ERR_EPILOGUE = -5,  /* unknown epilogue, or a bias epilogue without bias */
   W4A16_ERR_WORKSPACE = -6, /* workspace NULL or smaller than required */
   W4A16_ERR_ALIGN = -7,     /* a device pointer is not 16-byte aligned */
-  W4A16_ERR_LAUNCH = -8     /* the HIP launch failed (hipGetLastError) */
+  W4A16_ERR_LAUNCH = -8,    /* the HIP launch failed (hipGetLastError) */
+  W4A16_ERR_SPLIT = -9      /* a forced split-K factor the shape cannot use */
 } w4a16_status;
 
 enum { W4A16_SCALE_F16 = 0, W4A16_SCALE_F32 = 1 };
@@ -140,6 +141,50 @@ int w4a16_gemm_gate_up(const void *A, int M, int K, int N, int group,
                        const void *packed_up, const void *rms_gamma,
                        float rms_eps, void *out, void *workspace,
                        size_t workspace_bytes, w4a16_stream stream);
+
+/*
+ * Split-K control.  The "Small-M split-K retune" update on the onnx-genai
+ * pull request tunes how many workgroups share one output tile's k range
+ * for the small-M decode shapes (o/q 4096x4096, down 13696x4096, gate_up
+ * 4096x2*13696 and 5120x2*13824 at M=8).  The automatic choice (split = 0)
+ * keeps at least two wavefronts per compute unit in flight and splits
+ * further only when the k range exceeds what one workgroup covers.  A
+ * positive `split` forces the streaming kernel (M <= 16) with that many k
+ * slices; the actual factor may round down so that no slice is empty.
+ * W4A16_ERR_SPLIT when the shape cannot run with it: M > 16, split larger
+ * than K/128, or smaller than the k range one workgroup can cover.
+ */
+enum { W4A16_KERNEL_STREAM = 1, W4A16_KERNEL_TILE = 2 };
+
+typedef struct {
+  int kernel;             /* W4A16_KERNEL_STREAM (M <= 16) or W4A16_KERNEL_TILE */
+  int split;              /* workgroups along K per output tile (1 = no split-K) */
+  int k_tiles_per_split;  /* 128-wide k tiles one split covers */
+  int grid[3];            /* launch grid */
+  int block;              /* threads per workgroup */
+  int lds_bytes;          /* dynamic LDS per workgroup */
+  size_t workspace_bytes; /* workspace the call needs (see w4a16_workspace_bytes) */
+} w4a16_plan_info;
+
+/* Host-only: fill *info with the plan a call of this shape launches.
+ * Touches no device.  Returns W4A16_ERR_SPLIT as described above. */
+int w4a16_plan(int M, int K, int N, int group, int scale_dtype, int gate_up,
+               int split, w4a16_plan_info *info);
+
+/* w4a16_gemm / w4a16_gemm_gate_up with a split-K factor (0 = automatic,
+ * the same as the calls without it).  The workspace must hold
+ * w4a16_plan(...).workspace_bytes for the same split. */
+int w4a16_gemm_split(const void *A, int M, int K, int N, int group,
+                     int scale_dtype, int has_zp, const void *packed,
+                     int epilogue, const void *bias, const void *rms_gamma,
+                     float rms_eps, void *out, void *workspace,
+                     size_t workspace_bytes, int split, w4a16_stream stream);
+int w4a16_gemm_gate_up_split(const void *A, int M, int K, int N, int group,
+                             int scale_dtype, int has_zp,
+                             const void *packed_gate, const void *packed_up,
+                             const void *rms_gamma, float rms_eps, void *out,
+                             void *workspace, size_t workspace_bytes,
+                             int split, w4a16_stream stream);
 
 /* Static, human-readable text for a w4a16_status value. */
 const char *w4a16_status_string(int status);

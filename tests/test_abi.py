@@ -39,7 +39,8 @@ def test_header_enums_match_binding():
     for name, val in [("W4A16_ERR_NULL", -1), ("W4A16_ERR_SHAPE", -2),
                       ("W4A16_ERR_GROUP", -3), ("W4A16_ERR_DTYPE", -4),
                       ("W4A16_ERR_EPILOGUE", -5), ("W4A16_ERR_WORKSPACE", -6),
-                      ("W4A16_ERR_ALIGN", -7), ("W4A16_ERR_LAUNCH", -8)]:
+                      ("W4A16_ERR_ALIGN", -7), ("W4A16_ERR_LAUNCH", -8),
+                      ("W4A16_ERR_SPLIT", -9)]:
         assert re.search(rf"{name}\s*=\s*{val}\b", text), name
         assert getattr(_lib, name[6:]) == val
     assert re.search(r"W4A16_EPI_BIAS_RELU\s*=\s*2", text)
@@ -48,7 +49,7 @@ def test_header_enums_match_binding():
 
 def test_layout_version_and_status_strings(L):
     assert L.w4a16_layout_version() == 1
-    for st in range(-8, 1):
+    for st in range(-9, 1):
         assert len(L.w4a16_status_string(st)) > 0
     assert L.w4a16_status_string(-99) == b"unknown status"
 
@@ -139,3 +140,63 @@ def test_single_hip_runtime_after_load(L):
     maps = open("/proc/self/maps").read()
     libs = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
     assert len(libs) <= 1, libs
+
+
+def plan(L, M, K, N, g=128, sdt=0, gu=0, split=0):
+    info = _lib.PlanInfo()
+    st = L.w4a16_plan(M, K, N, g, sdt, gu, split, ctypes.byref(info))
+    return st, info
+
+
+def test_plan_query_matches_workspace_and_kernel_choice(L):
+    """Stream kernel for M <= 16, tile kernel above; the plan's workspace is
+    what w4a16_workspace_bytes reports; the grid covers every column tile."""
+    for M, K, N, gu in [(1, 5120, 13824, 0), (8, 13696, 4096, 0), (16, 4096, 4096, 0),
+                        (8, 4096, 13696, 1), (17, 5120, 13824, 0), (128, 1024, 384, 1),
+                        (1, 1024, 384, 0)]:
+        st, info = plan(L, M, K, N, gu=gu)
+        assert st == _lib.OK
+        assert info.kernel == (_lib.KERNEL_STREAM if M <= 16 else _lib.KERNEL_TILE)
+        assert info.block in (256, 512)
+        assert info.k_tiles_per_split * info.split >= K // 128
+        assert info.k_tiles_per_split * (info.split - 1) < K // 128  # no empty split
+        assert info.grid[1] == info.split
+        ws = max(plan(L, M, K, N, sdt=s, gu=gu)[1].workspace_bytes for s in (0, 1))
+        assert ws == L.w4a16_workspace_bytes(M, K, N, 128, gu)
+        assert (info.workspace_bytes > 0) == (info.split > 1)
+
+
+def test_plan_deep_k_splits_and_forced_splits(L):
+    """K = 13696 (107 k tiles) is deeper than one workgroup covers: the
+    automatic plan splits it; a forced split below that minimum, above the
+    tile count, or for M > 16 is rejected; a forced split rounds so that no
+    slice is empty."""
+    st, auto = plan(L, 8, 13696, 4096)
+    assert st == _lib.OK and auto.split >= 3
+    for sk in (1, 2):
+        assert plan(L, 8, 13696, 4096, split=sk)[0] == _lib.ERR_SPLIT
+    assert plan(L, 8, 1024, 384, split=9)[0] == _lib.ERR_SPLIT    # 8 k tiles
+    assert plan(L, 17, 4096, 4096, split=2)[0] == _lib.ERR_SPLIT  # tile kernel
+    st, f = plan(L, 8, 5120, 13824, split=9)   # 40 tiles: 5 per split -> 8 splits
+    assert st == _lib.OK and (f.split, f.k_tiles_per_split) == (8, 5)
+    for sk in (3, 4, 8, 16):
+        st, f = plan(L, 8, 13696, 4096, split=sk)
+        assert st == _lib.OK and f.split <= sk and f.workspace_bytes > 0
+    st, f = plan(L, 8, 4096, 4096, split=1)
+    assert st == _lib.OK and f.split == 1 and f.workspace_bytes == 0
+    assert L.w4a16_plan(8, 4096, 4096, 128, 0, 0, 0, None) == _lib.ERR_NULL
+    assert plan(L, 8, 4000, 4096)[0] == _lib.ERR_SHAPE
+
+
+def test_forced_split_workspace_checked_before_launch(L):
+    """A forced split needs its own workspace size; a smaller one is refused
+    on the host (FAKE pointers are never dereferenced)."""
+    FAKE = 1 << 20
+    st, f = plan(L, 8, 13696, 4096, split=8)
+    assert f.workspace_bytes > 0
+    assert L.w4a16_gemm_split(FAKE, 8, 13696, 4096, 128, 0, 1, FAKE, 0, None, None, 1e-6,
+                              FAKE, FAKE, f.workspace_bytes - 1, 8, None) == _lib.ERR_WORKSPACE
+    assert L.w4a16_gemm_split(FAKE, 8, 13696, 4096, 128, 0, 1, FAKE, 0, None, None, 1e-6,
+                              FAKE, FAKE, 1 << 30, 2, None) == _lib.ERR_SPLIT
+    assert L.w4a16_gemm_gate_up_split(FAKE, 20, 4096, 4096, 128, 0, 1, FAKE, FAKE, None, 1e-6,
+                                      FAKE, FAKE, 1 << 30, 4, None) == _lib.ERR_SPLIT

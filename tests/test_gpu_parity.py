@@ -268,6 +268,65 @@ def test_gate_up_small_all_outputs(M, g, rms):
     check_close(run_gate_up(p, rms), ref_gate_up(p, rms=rms), f"gate_up M={M} g={g} rms={rms}")
 
 
+# ------------------------------------- M=8 decode shapes and split-K control
+
+# The shapes the "Small-M split-K retune" update tunes at M=8: o/q
+# 4096x4096, down 13696x4096 (107 k tiles: deeper than one workgroup
+# covers, so always split), gate_up 4096 x 2*13696 and 5120 x 2*13824.
+
+
+@pytest.mark.parametrize("K,N", [(4096, 4096), (13696, 4096)])
+def test_split_sweep_gemm_shapes_sampled(K, N):
+    p = synth.make_problem(8, K, N, 128, seed=K + N, gamma=True, bias=True)
+    cols = sample_cols(N, 96, seed=K)
+    got = run_gemm(p)
+    check_close(got[:, cols], ref_gemm(p, cols=cols), f"M=8 K={K} N={N}")
+    got = run_gemm(p, rms=True, epilogue="bias_relu")
+    check_close(got[:, cols], ref_gemm(p, cols=cols, rms=True, epilogue="bias_relu"),
+                f"M=8 K={K} N={N} rms+bias_relu")
+
+
+@pytest.mark.parametrize("K,N", [(4096, 13696), (5120, 13824)])
+def test_split_sweep_gate_up_shapes_sampled(K, N):
+    p = synth.make_problem(8, K, N, 128, seed=K, gate_up=True)
+    got = run_gate_up(p)
+    cols = sample_cols(N, 96, seed=N)
+    check_close(got[:, cols], ref_gate_up(p, cols=cols), f"gate_up M=8 K={K} N={N}")
+
+
+def test_forced_splits_match_oracle_and_repeat():
+    """Every forced split of the deep down_proj shape (with the RMSNorm
+    prologue, whose sums of squares are also split) meets the oracle on
+    sampled columns, and repeats bit-identically."""
+    K, N, M = 13696, 4096, 8
+    p = synth.make_problem(M, K, N, 128, seed=11, gamma=True)
+    w = repack_dev(p.w)
+    A, gm = to_dev(p.A), to_dev(p.gamma)
+    cols = sample_cols(N, 64, seed=3)
+    ref = ref_gemm(p, cols=cols, rms=True)
+    for sk in (3, 4, 8, 16, 107):
+        y1 = w4.gemm(A, w, gamma=gm, out=nan_out(M, N), split=sk)
+        y2 = w4.gemm(A, w, gamma=gm, out=nan_out(M, N), split=sk)
+        torch.cuda.synchronize()
+        assert torch.equal(y1, y2), f"split {sk} not repeatable"
+        check_close(y1.cpu().numpy()[:, cols], ref, f"down_proj split={sk}")
+
+
+@pytest.mark.parametrize("M", [1, 8, 16])
+def test_forced_splits_all_outputs_small(M):
+    """Small shape, every output, every feasible split (1 .. 8 k tiles)."""
+    p = synth.make_problem(M, 1024, 384, 32, seed=M, gate_up=True, gamma=True)
+    ref = ref_gemm(p, rms=True)
+    ref_gu = ref_gate_up(p, rms=True)
+    w, wu = repack_dev(p.w), repack_dev(p.w_up)
+    A, gm = to_dev(p.A), to_dev(p.gamma)
+    for sk in range(1, 9):
+        y = w4.gemm(A, w, gamma=gm, out=nan_out(M, p.N), split=sk)
+        check_close(y.cpu().numpy(), ref, f"M={M} split={sk}")
+        y = w4.gemm_gate_up(A, w, wu, gamma=gm, out=nan_out(M, p.N), split=sk)
+        check_close(y.cpu().numpy(), ref_gu, f"gate_up M={M} split={sk}")
+
+
 # --------------------------------------------------------------------- probes
 
 
