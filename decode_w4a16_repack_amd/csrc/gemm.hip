@@ -3,10 +3,10 @@
 //
 // The plan is a pure function of the shape: it picks the kernel
 // configuration, the grid and, only where a workgroup's k range cannot hold
-// the whole K or the grid is short of wavefronts, a k split across
-// workgroups (the onnx-genai pull request "Marlin-style fused fp16xint4
-// tensor-core GEMM", "P2 - widen the win: split-K": split only when the grid
-// is short of waves).
+// the whole K or the grid is short of one workgroup per compute unit, a k
+// split across workgroups (the onnx-genai pull request "Marlin-style fused
+// fp16xint4 tensor-core GEMM", "P2 - widen the win: split-K": split only
+// when the grid is short of waves).
 #include "common.h"
 
 namespace w4a16 {
@@ -21,15 +21,16 @@ int pow2_at_least(int v) {
 
 size_t align16(size_t v) { return (v + 15) / 16 * 16; }
 
-// k splits across workgroups only when the grid has fewer than 512
-// wavefronts; every split keeps at least one k tile.
-int choose_split(int base, int nwave, int KC, int force_split) {
-  int S = 1;
-  if (force_split > 0) {
-    S = force_split;
-  } else {
-    while (base * S * nwave < 512 && S + 1 <= KC) ++S;
-  }
+// Workgroups of the stream kernel resident at once: one per compute unit
+// (its register use leaves room for one 8-wavefront workgroup per CU).
+constexpr int kStreamSlots = 256;
+
+// Automatic split: as many k splits as keep every workgroup of the grid
+// resident at once, since a second round of workgroups costs a whole
+// workgroup lifetime; a forced split is taken as given.
+int choose_split(int base, int KC, int force_split) {
+  int S = force_split > 0 ? force_split : kStreamSlots / base;
+  if (S < 1) S = 1;
   return S > KC ? KC : S;
 }
 
@@ -62,7 +63,7 @@ bool plan_stream(Plan &p, int M, int K, int N, int group, int scale_bytes, bool 
   const int s_min = (KC + per_wg - 1) / per_wg;
   // a forced split must leave every workgroup at most its NWK x KPW tiles
   if (force_split > 0 && (force_split < s_min || force_split > KC)) return false;
-  int S = choose_split(base, c.nwk, KC, force_split);
+  int S = choose_split(base, KC, force_split);
   if (S < s_min) S = s_min;
   if (S > KC) S = KC;
   if (S > 1 && NTL * p.gz > kMaxSplitBlocks) return false;  // one arrival counter per column tile
