@@ -54,9 +54,11 @@ constexpr int kLdsMax = 160 * 1024;
 // ring of tile_nbuf() blocks.
 constexpr int tile_step_scale_bytes(int ct, int group, int sb) { return ct * (kTileK / group) * 16 * sb; }
 constexpr int tile_step_zp_bytes(int ct, int group) { return ct * (kTileK / group) * 8; }
+// (a divisor of the main loop's unroll of 4, so a block opens at a fixed
+// position of the unrolled body)
 constexpr int tile_mbs(int ct, int group, int sb) {
-  return 1024 / tile_step_scale_bytes(ct, group, sb) >= 8 ? 8
-         : 1024 / tile_step_scale_bytes(ct, group, sb) >= 1 ? 1024 / tile_step_scale_bytes(ct, group, sb)
+  return 1024 / tile_step_scale_bytes(ct, group, sb) >= 4   ? 4
+         : 1024 / tile_step_scale_bytes(ct, group, sb) >= 2 ? 2
                                                              : 1;
 }
 constexpr int tile_meta_block_bytes(int ct, int group, int sb, int nw) {
@@ -177,8 +179,8 @@ tile_kernel(const GemmArgs p) {
   // that block's scales and zero-points.  Steps past K re-read the last k
   // tile; symmetric weights copy scale bytes into the (unread) zero-point
   // area.
-  auto issue = [&](int j, int st) __attribute__((always_inline)) {
-    if (j % MBS == 0) {
+  auto issue = [&](int j, int st, bool opens_block) __attribute__((always_inline)) {
+    if (opens_block) {
       uint8_t *blk = mblk_of(j / MBS);
       // k tile of step j + s_step (the lane's own step in the block)
       const int kts = min(ktile(j + s_step), KC - 1), ktz = min(ktile(j + z_step), KC - 1);
@@ -226,6 +228,8 @@ tile_kernel(const GemmArgs p) {
     const int sl = wave & 1, h = wave >> 1;
     uint8_t *ab = smem + st * STAGE + sl * kTileABytes;
     const f16 *gm = p.gamma + (size_t)min(j * NKS + sl, KC - 1) * kTileK;  // slice sl's k tile
+    // a step past K holds a re-read of the last k tile: it adds no squares
+    const float on = j * NKS + sl < KC ? 1.0f : 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int e = lane + 64 * i;
@@ -236,7 +240,7 @@ tile_kernel(const GemmArgs p) {
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         const float xf = (float)x[q];
-        ssq[i] = __builtin_fmaf(xf, xf, ssq[i]);
+        ssq[i] = __builtin_fmaf(xf * on, xf, ssq[i]);
       }
       *px = x * g;
     }
@@ -250,6 +254,9 @@ tile_kernel(const GemmArgs p) {
     const uint8_t *blk = mblk_of(j / MBS);
     const int jb = j % MBS;  // step within the metadata block
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+    // a step past K (its copies and loads re-read the last k tile) runs the
+    // same instructions with every scale zero, so it adds exactly nothing
+    const float on = ktile(j) < KC ? 1.0f : 0.0f;
     f16x8 a[4][MT];
 #pragma unroll
     for (int d = 0; d < 4; ++d)
@@ -265,9 +272,9 @@ tile_kernel(const GemmArgs p) {
         const uint8_t *zp = blk + NW * BS + i * BZ + jb * PSZ + (ct * GPC) * 8 + (c >> 1);
         auto scale = [&](int g2) __attribute__((always_inline)) {
           if constexpr (SF32)
-            return *reinterpret_cast<const float *>(sp + g2 * 16 * SB);
+            return on * *reinterpret_cast<const float *>(sp + g2 * 16 * SB);
           else
-            return (float)*reinterpret_cast<const f16 *>(sp + g2 * 16 * SB);
+            return on * (float)*reinterpret_cast<const f16 *>(sp + g2 * 16 * SB);
         };
         auto zconst = [&](int g2, f16x2 &zlo, f16x2 &zhi) __attribute__((always_inline)) {
           const uint32_t z = has_zp ? (uint32_t)((zp[g2 * 8] >> zshift) & 15) : 8u;
@@ -326,28 +333,40 @@ tile_kernel(const GemmArgs p) {
   // and computes.
   u32x4 wring[D + 1][NW][CT];
 #pragma unroll
-  for (int u = 0; u < ST - 1; ++u) issue(u, u);
+  for (int u = 0; u < ST - 1; ++u) issue(u, u, u % MBS == 0);
 #pragma unroll
   for (int u = 0; u < D; ++u) load_w(u, wring[u]);
   int st = 0;
+  // Step j = j0 + u (j0 a multiple of D + 1 = 4, so u, the ring slot and
+  // whether a metadata block opens are known at compile time).  Every step
+  // issues the same copies and loads and runs the same contraction (a step
+  // past K with zero scales), so every load has a consumer on every path
+  // and the compiler never has to drain the loads in flight.  Where the
+  // register file allows it (one column tile per wavefront, one weight
+  // stream, groups of 64 or 128) the trip count is padded to a multiple of
+  // 4 and the body has no branch at all; elsewhere the steps past the last
+  // group of 4 are skipped, since the compiler would otherwise interleave
+  // the four steps past what the register file holds.
   auto step = [&](int j, auto uc) __attribute__((always_inline)) {
-    constexpr int u = decltype(uc)::value;  // j % (D + 1)
+    constexpr int u = decltype(uc)::value;
     wait_vmcnt<AFTER>();  // this wavefront's copies of step j have landed
     lds_only_barrier();   // everyone's have, and step j - 1's reads are done
-    issue(j + ST - 1, st == 0 ? ST - 1 : st - 1);
+    issue(j + ST - 1, st == 0 ? ST - 1 : st - 1, (u + ST - 1) % MBS == 0);
     load_w(j + D, wring[(u + D) % (D + 1)]);
     if (rms) {
       rms_pass(j, st);
       lds_only_barrier();
     }
-    if (ktile(j) < KC) compute(j, st, wring[u]);
+    compute(j, st, wring[u]);
     st = st == ST - 1 ? 0 : st + 1;
   };
+  static_assert(D + 1 == 4 && 4 % MBS == 0, "unroll and metadata blocks");
+  constexpr bool FLAT = CT == 1 && !GU && (G == 128 || (G == 64 && !SF32));
   for (int j0 = 0; j0 < nsteps; j0 += D + 1) {
     step(j0, std::integral_constant<int, 0>{});
-    if (j0 + 1 < nsteps) step(j0 + 1, std::integral_constant<int, 1>{});
-    if (j0 + 2 < nsteps) step(j0 + 2, std::integral_constant<int, 2>{});
-    if (j0 + 3 < nsteps) step(j0 + 3, std::integral_constant<int, 3>{});
+    if (FLAT || j0 + 1 < nsteps) step(j0 + 1, std::integral_constant<int, 1>{});
+    if (FLAT || j0 + 2 < nsteps) step(j0 + 2, std::integral_constant<int, 2>{});
+    if (FLAT || j0 + 3 < nsteps) step(j0 + 3, std::integral_constant<int, 3>{});
   }
   __syncthreads();  // every step and every copy done: the stages become reduction scratch
 

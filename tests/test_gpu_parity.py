@@ -209,6 +209,20 @@ def test_rmsnorm_prologue_small(M):
     check_close(run_gemm(p, rms=True), ref_gemm(p, rms=True), f"rmsnorm M={M}")
 
 
+@pytest.mark.parametrize("M,g,gu", [(5, 64, False), (20, 64, False), (70, 128, False),
+                                    (130, 32, False), (40, 16, True), (9, 128, True)])
+def test_rmsnorm_odd_k_tile_count(M, g, gu):
+    """K = 1152 is 9 k tiles: the two k slices of a workgroup get 5 and 4, so
+    one slice runs a step past K.  That step must add nothing, neither to
+    the product nor to the sums of squares of the RMSNorm prologue."""
+    p = synth.make_problem(M, 1152, 256, g, seed=M + g, gamma=True, gate_up=gu)
+    if gu:
+        check_close(run_gate_up(p, rms=True), ref_gate_up(p, rms=True), f"odd-k gate_up M={M}")
+    else:
+        check_close(run_gemm(p, rms=True), ref_gemm(p, rms=True), f"odd-k rmsnorm M={M} g={g}")
+        check_close(run_gemm(p), ref_gemm(p), f"odd-k M={M} g={g}")
+
+
 def test_unfused_chain_matches_fused():
     """FUSED=0 chain (GEMM -> bias pass -> ReLU pass; RMSNorm pass -> GEMM)
     computes the same as the fused kernels, within the tolerance."""
