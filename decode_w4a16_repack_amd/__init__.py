@@ -147,16 +147,22 @@ def repack(qweight: torch.Tensor, scales: torch.Tensor, zeros: Optional[torch.Te
 def gemm(A: torch.Tensor, w: PackedWeight, *, epilogue: str = "none",
          bias: Optional[torch.Tensor] = None, gamma: Optional[torch.Tensor] = None,
          eps: float = 1e-6, out: Optional[torch.Tensor] = None,
-         workspace: Optional[Workspace] = None, split: int = 0) -> torch.Tensor:
-    """fp16 [M][N] = epilogue(X . dequant(W)), X = A or RMSNorm(A; gamma, eps).
-    split > 0 forces that split-K factor (w4a16_gemm_split)."""
+         workspace: Optional[Workspace] = None, split: int = 0,
+         residual: Optional[torch.Tensor] = None,
+         residual_out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """fp16 [M][N] = epilogue(X . dequant(W)), X = A or RMSNorm(A; gamma, eps),
+    or with ``residual`` X = RMSNorm(A + residual) (w4a16_gemm_skip_rmsnorm;
+    the sum is written to ``residual_out`` when given).  split > 0 forces
+    that split-K factor (w4a16_gemm_split)."""
     _need_gpu(A, "A", torch.float16)
     M, K = A.shape
     if K != w.K:
         raise ValueError(f"A has K={K}, weight has K={w.K}")
-    for t, n in ((bias, "bias"), (gamma, "gamma")):
+    for t, n in ((bias, "bias"), (gamma, "gamma"), (residual, "residual"),
+                 (residual_out, "residual_out")):
         if t is not None:
             _need_gpu(t, n, torch.float16)
+    _check_residual(A, gamma, residual, residual_out, split)
     if out is None:
         out = torch.empty((M, w.N), dtype=torch.float16, device=A.device)
     _need_gpu(out, "out", torch.float16)
@@ -167,7 +173,10 @@ def gemm(A: torch.Tensor, w: PackedWeight, *, epilogue: str = "none",
     ws = (workspace or _default_ws).get(ws_n, A.device)
     args = (_ptr(A), M, K, w.N, w.group, w.scale_dtype, int(w.has_zp), _ptr(w.data),
             _lib.EPI[epilogue], _ptr(bias), _ptr(gamma), float(eps), _ptr(out), _ptr(ws), ws_n)
-    if split:
+    if residual is not None:
+        st = _lib.lib().w4a16_gemm_skip_rmsnorm(_ptr(A), _ptr(residual), _ptr(residual_out),
+                                                *args[1:], _stream())
+    elif split:
         st = _lib.lib().w4a16_gemm_split(*args, split, _stream())
     else:
         st = _lib.lib().w4a16_gemm(*args, _stream())
@@ -175,13 +184,33 @@ def gemm(A: torch.Tensor, w: PackedWeight, *, epilogue: str = "none",
     return out
 
 
+def _check_residual(A, gamma, residual, residual_out, split):
+    if residual is None:
+        if residual_out is not None:
+            raise ValueError("residual_out needs residual")
+        return
+    if gamma is None:
+        raise ValueError("the residual (skip) prologue needs gamma")
+    if split:
+        raise ValueError("split is not available with the residual prologue")
+    if residual.shape != A.shape or (residual_out is not None and residual_out.shape != A.shape):
+        raise ValueError("residual and residual_out must have A's shape")
+
+
 def gemm_gate_up(A: torch.Tensor, w_gate: PackedWeight, w_up: PackedWeight, *,
                  gamma: Optional[torch.Tensor] = None, eps: float = 1e-6,
                  out: Optional[torch.Tensor] = None,
-                 workspace: Optional[Workspace] = None, split: int = 0) -> torch.Tensor:
-    """fp16 [M][N] = silu(X . Wg) * (X . Wu); split as in gemm()."""
+                 workspace: Optional[Workspace] = None, split: int = 0,
+                 residual: Optional[torch.Tensor] = None,
+                 residual_out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """fp16 [M][N] = silu(X . Wg) * (X . Wu); split, residual and
+    residual_out as in gemm()."""
     _need_gpu(A, "A", torch.float16)
     M, K = A.shape
+    for t, n in ((residual, "residual"), (residual_out, "residual_out")):
+        if t is not None:
+            _need_gpu(t, n, torch.float16)
+    _check_residual(A, gamma, residual, residual_out, split)
     for w in (w_gate, w_up):
         if (w.K, w.N, w.group, w.scale_dtype, w.has_zp) != (
                 w_gate.K, w_gate.N, w_gate.group, w_gate.scale_dtype, w_gate.has_zp):
@@ -201,7 +230,10 @@ def gemm_gate_up(A: torch.Tensor, w_gate: PackedWeight, w_up: PackedWeight, *,
     args = (_ptr(A), M, K, w_gate.N, w_gate.group, w_gate.scale_dtype, int(w_gate.has_zp),
             _ptr(w_gate.data), _ptr(w_up.data), _ptr(gamma), float(eps), _ptr(out),
             _ptr(ws), ws_n)
-    if split:
+    if residual is not None:
+        st = _lib.lib().w4a16_gemm_gate_up_skip_rmsnorm(_ptr(A), _ptr(residual),
+                                                        _ptr(residual_out), *args[1:], _stream())
+    elif split:
         st = _lib.lib().w4a16_gemm_gate_up_split(*args, split, _stream())
     else:
         st = _lib.lib().w4a16_gemm_gate_up(*args, _stream())

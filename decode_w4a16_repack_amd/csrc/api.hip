@@ -123,12 +123,25 @@ size_t w4a16_workspace_bytes(int M, int K, int N, int group, int gate_up) {
   return a > b ? a : b;
 }
 
-int w4a16_gemm_split(const void *A, int M, int K, int N, int group, int scale_dtype,
-                     int has_zp, const void *packed, int epilogue, const void *bias,
-                     const void *rms_gamma, float rms_eps, void *out, void *workspace,
-                     size_t workspace_bytes, int split, w4a16_stream stream) {
+namespace {
+
+// Residual (skip + RMSNorm) arguments: the residual needs the norm; both
+// device buffers 16-byte aligned.
+int check_residual(const void *resid, const void *resid_out, const void *gamma) {
+  if (resid == nullptr) return resid_out == nullptr ? W4A16_OK : W4A16_ERR_NULL;
+  if (gamma == nullptr) return W4A16_ERR_NULL;
+  if (!aligned16(resid) || (resid_out != nullptr && !aligned16(resid_out))) return W4A16_ERR_ALIGN;
+  return W4A16_OK;
+}
+
+int gemm_impl(const void *A, const void *resid, void *resid_out, int M, int K, int N,
+              int group, int scale_dtype, int has_zp, const void *packed, int epilogue,
+              const void *bias, const void *rms_gamma, float rms_eps, void *out,
+              void *workspace, size_t workspace_bytes, int split, w4a16_stream stream) {
   const void *pk[1] = {packed};
   int st = check_gemm(A, M, K, N, group, scale_dtype, pk, 1, out);
+  if (st != W4A16_OK) return st;
+  st = check_residual(resid, resid_out, rms_gamma);
   if (st != W4A16_OK) return st;
   if (epilogue != W4A16_EPI_NONE && epilogue != W4A16_EPI_BIAS &&
       epilogue != W4A16_EPI_BIAS_RELU)
@@ -154,6 +167,8 @@ int w4a16_gemm_split(const void *A, int M, int K, int N, int group, int scale_dt
   a.epilogue = epilogue;
   a.bias = static_cast<const f16 *>(bias);
   a.gamma = static_cast<const f16 *>(rms_gamma);
+  a.resid = static_cast<const f16 *>(resid);
+  a.resid_out = static_cast<f16 *>(resid_out);
   a.eps = rms_eps;
   a.out = static_cast<f16 *>(out);
   fill_workspace(a, pl, workspace);
@@ -161,13 +176,14 @@ int w4a16_gemm_split(const void *A, int M, int K, int N, int group, int scale_dt
                               static_cast<hipStream_t>(stream)));
 }
 
-int w4a16_gemm_gate_up_split(const void *A, int M, int K, int N, int group,
-                             int scale_dtype, int has_zp, const void *packed_gate,
-                             const void *packed_up, const void *rms_gamma,
-                             float rms_eps, void *out, void *workspace,
-                             size_t workspace_bytes, int split, w4a16_stream stream) {
+int gate_up_impl(const void *A, const void *resid, void *resid_out, int M, int K, int N,
+                 int group, int scale_dtype, int has_zp, const void *packed_gate,
+                 const void *packed_up, const void *rms_gamma, float rms_eps, void *out,
+                 void *workspace, size_t workspace_bytes, int split, w4a16_stream stream) {
   const void *pk[2] = {packed_gate, packed_up};
   int st = check_gemm(A, M, K, N, group, scale_dtype, pk, 2, out);
+  if (st != W4A16_OK) return st;
+  st = check_residual(resid, resid_out, rms_gamma);
   if (st != W4A16_OK) return st;
   if (rms_gamma != nullptr && !aligned16(rms_gamma)) return W4A16_ERR_ALIGN;
   Plan pl;
@@ -187,11 +203,56 @@ int w4a16_gemm_gate_up_split(const void *A, int M, int K, int N, int group,
   a.has_zp = has_zp != 0;
   a.epilogue = W4A16_EPI_NONE;
   a.gamma = static_cast<const f16 *>(rms_gamma);
+  a.resid = static_cast<const f16 *>(resid);
+  a.resid_out = static_cast<f16 *>(resid_out);
   a.eps = rms_eps;
   a.out = static_cast<f16 *>(out);
   fill_workspace(a, pl, workspace);
   return launched(launch_gemm(a, pl, group, sb == 4, true,
                               static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+int w4a16_gemm_split(const void *A, int M, int K, int N, int group, int scale_dtype,
+                     int has_zp, const void *packed, int epilogue, const void *bias,
+                     const void *rms_gamma, float rms_eps, void *out, void *workspace,
+                     size_t workspace_bytes, int split, w4a16_stream stream) {
+  return gemm_impl(A, nullptr, nullptr, M, K, N, group, scale_dtype, has_zp, packed, epilogue,
+                   bias, rms_gamma, rms_eps, out, workspace, workspace_bytes, split, stream);
+}
+
+int w4a16_gemm_gate_up_split(const void *A, int M, int K, int N, int group,
+                             int scale_dtype, int has_zp, const void *packed_gate,
+                             const void *packed_up, const void *rms_gamma,
+                             float rms_eps, void *out, void *workspace,
+                             size_t workspace_bytes, int split, w4a16_stream stream) {
+  return gate_up_impl(A, nullptr, nullptr, M, K, N, group, scale_dtype, has_zp, packed_gate,
+                      packed_up, rms_gamma, rms_eps, out, workspace, workspace_bytes, split,
+                      stream);
+}
+
+int w4a16_gemm_skip_rmsnorm(const void *A, const void *residual, void *residual_out, int M,
+                            int K, int N, int group, int scale_dtype, int has_zp,
+                            const void *packed, int epilogue, const void *bias,
+                            const void *rms_gamma, float rms_eps, void *out, void *workspace,
+                            size_t workspace_bytes, w4a16_stream stream) {
+  if (residual == nullptr || rms_gamma == nullptr) return W4A16_ERR_NULL;
+  return gemm_impl(A, residual, residual_out, M, K, N, group, scale_dtype, has_zp, packed,
+                   epilogue, bias, rms_gamma, rms_eps, out, workspace, workspace_bytes, 0,
+                   stream);
+}
+
+int w4a16_gemm_gate_up_skip_rmsnorm(const void *A, const void *residual, void *residual_out,
+                                    int M, int K, int N, int group, int scale_dtype,
+                                    int has_zp, const void *packed_gate,
+                                    const void *packed_up, const void *rms_gamma,
+                                    float rms_eps, void *out, void *workspace,
+                                    size_t workspace_bytes, w4a16_stream stream) {
+  if (residual == nullptr || rms_gamma == nullptr) return W4A16_ERR_NULL;
+  return gate_up_impl(A, residual, residual_out, M, K, N, group, scale_dtype, has_zp,
+                      packed_gate, packed_up, rms_gamma, rms_eps, out, workspace,
+                      workspace_bytes, 0, stream);
 }
 
 int w4a16_gemm(const void *A, int M, int K, int N, int group, int scale_dtype,

@@ -63,6 +63,8 @@ struct GemmArgs {
   int epilogue;
   const f16 *bias;
   const f16 *gamma;  // null: no RMSNorm prologue
+  const f16 *resid;  // with gamma: residual added before the norm (null: none)
+  f16 *resid_out;    // with resid: the sum A + resid written here (null: not written)
   float eps;
   f16 *out;
   float *ws_part;     // [S][2 if gate_up][M][N] fp32 partial sums

@@ -189,6 +189,36 @@ stream_kernel(const GemmArgs p) {
   //    factor 1/sqrt(mean + eps) is applied in the epilogue.
   float ss = 0.f;
   if (rms) {
+    if (p.resid != nullptr) {
+      // residual add first (skip + RMSNorm): s = A + resid rounded once to
+      // fp16; the workgroups of column block 0 write s out, each (row, k)
+      // once
+      f16x8 rr[KPW][4];
+      const f16 *rrow = p.resid + (size_t)(m0 + arow) * p.K + 8 * kq;
+#pragma unroll
+      for (int t = 0; t < KPW; ++t) {
+        const int kc = min(my_kb + min(t, max(my_n - 1, 0)), KC - 1);
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+          rr[t][d] = *reinterpret_cast<const f16x8 *>(rrow + kc * kTileK + 32 * d);
+      }
+      wait_vmcnt<0>();
+      read_slots();
+#pragma unroll
+      for (int t = 0; t < KPW; ++t)
+#pragma unroll
+        for (int d = 0; d < 4; ++d) a[t][d][0] = a[t][d][0] + rr[t][d];
+      zero_tail();
+      if (p.resid_out != nullptr && blockIdx.x == 0 && c < mrows) {
+        f16 *orow = p.resid_out + (size_t)(m0 + c) * p.K + 8 * kq;
+#pragma unroll
+        for (int t = 0; t < KPW; ++t)
+          if (t < my_n)
+#pragma unroll
+            for (int d = 0; d < 4; ++d)
+              *reinterpret_cast<f16x8 *>(orow + (my_kb + t) * kTileK + 32 * d) = a[t][d][0];
+      }
+    }
     f16x8 gam[KPW][4];
 #pragma unroll
     for (int t = 0; t < KPW; ++t) {
@@ -198,8 +228,10 @@ stream_kernel(const GemmArgs p) {
         gam[t][d] = *reinterpret_cast<const f16x8 *>(p.gamma + kc * kTileK + 32 * d + 8 * kq);
     }
     wait_vmcnt<0>();
-    read_slots();
-    zero_tail();
+    if (p.resid == nullptr) {
+      read_slots();
+      zero_tail();
+    }
 #pragma unroll
     for (int t = 0; t < KPW; ++t)
 #pragma unroll

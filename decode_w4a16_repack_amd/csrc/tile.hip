@@ -222,27 +222,54 @@ tile_kernel(const GemmArgs p) {
   // RMSNorm prologue, in place on the stage: wavefront w normalizes rows
   // 16*(w/2) .. +15 of slice w%2's activation tile; lane l takes chunks
   // l + 64i (i = 0..3), i.e. row 16*(w/2) + 4i + l/16, and keeps that row's
-  // running sum of squares in ssq[i]
+  // running sum of squares in ssq[i].  With a residual (skip + RMSNorm) the
+  // chunk is first replaced by A + resid rounded once to fp16, which the
+  // workgroups of column block 0 also write out.  The gamma and residual
+  // chunks of a step are loaded one step ahead, into registers.
   float ssq[4] = {0.f, 0.f, 0.f, 0.f};
+  const bool has_res = p.resid != nullptr;
+  const bool write_res = has_res && p.resid_out != nullptr && blockIdx.x == 0;
+  const int rsl = wave & 1, rh = wave >> 1;
+  f16x8 rgam[4], rres[4];
+  auto rms_chunk_k = [&](int i) __attribute__((always_inline)) {
+    const int e = lane + 64 * i, r = 16 * rh + (e >> 4), pos = e & 15;
+    return 8 * (pos ^ (r & 15));  // k offset of the chunk within its tile
+  };
+  auto rms_row = [&](int i) __attribute__((always_inline)) { return 16 * rh + 4 * i + (lane >> 4); };
+  auto rms_load = [&](int j) __attribute__((always_inline)) {
+    const size_t k0 = (size_t)min(j * NKS + rsl, KC - 1) * kTileK;  // slice rsl's k tile
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      rgam[i] = *reinterpret_cast<const f16x8 *>(p.gamma + k0 + rms_chunk_k(i));
+      if (has_res)
+        rres[i] = *reinterpret_cast<const f16x8 *>(
+            p.resid + (size_t)(m0 + min(rms_row(i), mrows - 1)) * p.K + k0 + rms_chunk_k(i));
+    }
+  };
   auto rms_pass = [&](int j, int st) __attribute__((always_inline)) {
-    const int sl = wave & 1, h = wave >> 1;
-    uint8_t *ab = smem + st * STAGE + sl * kTileABytes;
-    const f16 *gm = p.gamma + (size_t)min(j * NKS + sl, KC - 1) * kTileK;  // slice sl's k tile
+    uint8_t *ab = smem + st * STAGE + rsl * kTileABytes;
     // a step past K holds a re-read of the last k tile: it adds no squares
-    const float on = j * NKS + sl < KC ? 1.0f : 0.0f;
+    // and writes nothing
+    const bool valid = j * NKS + rsl < KC;
+    const float on = valid ? 1.0f : 0.0f;
+    const size_t k0 = (size_t)(j * NKS + rsl) * kTileK;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int e = lane + 64 * i;
-      const int r = 16 * h + (e >> 4), pos = e & 15;
+      const int r = 16 * rh + (e >> 4), pos = e & 15;
       f16x8 *px = reinterpret_cast<f16x8 *>(ab + (r * 16 + pos) * 16);
-      const f16x8 g = *reinterpret_cast<const f16x8 *>(gm + 8 * (pos ^ (r & 15)));
       f16x8 x = *px;
+      if (has_res) {
+        x = x + rres[i];
+        if (write_res && valid && r < mrows)
+          *reinterpret_cast<f16x8 *>(p.resid_out + (size_t)(m0 + r) * p.K + k0 + rms_chunk_k(i)) = x;
+      }
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         const float xf = (float)x[q];
         ssq[i] = __builtin_fmaf(xf * on, xf, ssq[i]);
       }
-      *px = x * g;
+      *px = x * rgam[i];
     }
   };
 
@@ -332,6 +359,7 @@ tile_kernel(const GemmArgs p) {
   // copies of step j + ST - 1 into that stage and the weights of step j + D,
   // and computes.
   u32x4 wring[D + 1][NW][CT];
+  if (rms) rms_load(0);
 #pragma unroll
   for (int u = 0; u < ST - 1; ++u) issue(u, u, u % MBS == 0);
 #pragma unroll
@@ -355,6 +383,7 @@ tile_kernel(const GemmArgs p) {
     load_w(j + D, wring[(u + D) % (D + 1)]);
     if (rms) {
       rms_pass(j, st);
+      rms_load(j + 1);
       lds_only_barrier();
     }
     compute(j, st, wring[u]);

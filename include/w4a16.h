@@ -186,6 +186,36 @@ int w4a16_gemm_gate_up_split(const void *A, int M, int K, int N, int group,
                              void *workspace, size_t workspace_bytes,
                              int split, w4a16_stream stream);
 
+/*
+ * Skip + RMSNorm prologue (SkipSimplifiedLayerNormalization, the residual
+ * step before the projections of a decoder block; named in the "Stage 2 of
+ * spec-capture" update on the onnx-genai pull request, which makes it
+ * capture-safe).  The normalized input is the residual sum:
+ *   S = A + residual        (fp16 [M][K], each element rounded once)
+ *   X = S * gamma / sqrt(mean_k S^2 + eps)
+ * and the product, epilogue and gate_up pairing are those of w4a16_gemm /
+ * w4a16_gemm_gate_up with X in place of RMSNorm(A).  residual: fp16 [M][K],
+ * required, as is rms_gamma.  residual_out: fp16 [M][K] or NULL; when given,
+ * S is written there (every element exactly once), the updated residual
+ * stream for the next layer.  residual_out must not overlap A or residual.
+ */
+int w4a16_gemm_skip_rmsnorm(const void *A, const void *residual,
+                            void *residual_out, int M, int K, int N, int group,
+                            int scale_dtype, int has_zp, const void *packed,
+                            int epilogue, const void *bias,
+                            const void *rms_gamma, float rms_eps, void *out,
+                            void *workspace, size_t workspace_bytes,
+                            w4a16_stream stream);
+int w4a16_gemm_gate_up_skip_rmsnorm(const void *A, const void *residual,
+                                    void *residual_out, int M, int K, int N,
+                                    int group, int scale_dtype, int has_zp,
+                                    const void *packed_gate,
+                                    const void *packed_up,
+                                    const void *rms_gamma, float rms_eps,
+                                    void *out, void *workspace,
+                                    size_t workspace_bytes,
+                                    w4a16_stream stream);
+
 /* Static, human-readable text for a w4a16_status value. */
 const char *w4a16_status_string(int status);
 

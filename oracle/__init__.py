@@ -10,7 +10,9 @@ fp16xint4 tensor-core GEMM": the dequantized weight is (q - zp) * scale per
 dequant -> GEMM oracle ("Validation"); the RMSNorm prologue ("fused RMS-norm
 epilogue" update) and the paired gate/up SwiGLU ("gate_up SwiGLU MLP fusion"
 update).  The bias + ReLU epilogue and the fused/unfused byte model follow the
-"Fusion benchmark" page.
+"Fusion benchmark" page; the skip + RMSNorm residual sum (``skip_sum``)
+follows the SkipSimplifiedLayerNormalization op named in the "Stage 2 of
+spec-capture" update.
 
 Every value is computed in IEEE double by ``w4a16_oracle.c`` and
 ``repack_oracle.c``; this module only widens inputs to double (exact for fp16
@@ -181,6 +183,15 @@ def unrepack(packed, K: int, N: int, group: int, scale_dtype, has_zp: bool):
                              _ptr(q), _ptr(s.view(np.uint8)), _ptr(z))
     _check(rc, "unrepack")
     return q, s, z
+
+
+def skip_sum(A, residual) -> np.ndarray:
+    """fp16 residual sum S = A + residual of the skip + RMSNorm prologue
+    (SkipSimplifiedLayerNormalization, named in the "Stage 2 of
+    spec-capture" update): the exact sum of two fp16 values, rounded once
+    to fp16 (nearest-even).  The norm and the product then take S as the
+    activation: ``gemm(skip_sum(A, R), ..., gamma=gamma)``."""
+    return (np.asarray(A, dtype=np.float64) + np.asarray(residual, dtype=np.float64)).astype(np.float16)
 
 
 def to_fp16(y: np.ndarray) -> np.ndarray:

@@ -200,3 +200,36 @@ def test_forced_split_workspace_checked_before_launch(L):
                               FAKE, FAKE, 1 << 30, 2, None) == _lib.ERR_SPLIT
     assert L.w4a16_gemm_gate_up_split(FAKE, 20, 4096, 4096, 128, 0, 1, FAKE, FAKE, None, 1e-6,
                                       FAKE, FAKE, 1 << 30, 4, None) == _lib.ERR_SPLIT
+
+
+def test_library_sources_never_allocate_sync_or_memset():
+    """Capture safety by construction: no allocation, free, host
+    synchronization, copy or memset call anywhere in the library sources
+    (a memset node in a captured graph is also avoided this way)."""
+    csrc = os.path.join(ROOT, "decode_w4a16_repack_amd", "csrc")
+    banned = re.compile(r"\b(hipMalloc\w*|hipFree\w*|hipHostMalloc|hipMemset\w*|hipMemcpy\w*|"
+                        r"hipDeviceSynchronize|hipStreamSynchronize|hipEventSynchronize)\s*\(")
+    for name in sorted(os.listdir(csrc)):
+        text = re.sub(r"//[^\n]*|/\*.*?\*/", "", open(os.path.join(csrc, name)).read(), flags=re.S)
+        hits = banned.findall(text)
+        assert not hits, (name, hits)
+
+
+def test_skip_rmsnorm_validation(L):
+    """The skip prologue needs residual and gamma; 16-byte aligned buffers."""
+    FAKE = 1 << 20
+    args = (8, 1024, 256, 128, 0, 1, FAKE, 0, None)
+    assert L.w4a16_gemm_skip_rmsnorm(FAKE, None, None, *args, FAKE, 1e-6, FAKE, FAKE,
+                                     1 << 30, None) == _lib.ERR_NULL
+    assert L.w4a16_gemm_skip_rmsnorm(FAKE, FAKE, None, *args, None, 1e-6, FAKE, FAKE,
+                                     1 << 30, None) == _lib.ERR_NULL
+    assert L.w4a16_gemm_skip_rmsnorm(FAKE, FAKE + 8, None, *args, FAKE, 1e-6, FAKE, FAKE,
+                                     1 << 30, None) == _lib.ERR_ALIGN
+    assert L.w4a16_gemm_skip_rmsnorm(FAKE, FAKE, FAKE + 4, *args, FAKE, 1e-6, FAKE, FAKE,
+                                     1 << 30, None) == _lib.ERR_ALIGN
+    assert L.w4a16_gemm_gate_up_skip_rmsnorm(FAKE, None, None, 8, 1024, 256, 128, 0, 1, FAKE,
+                                             FAKE, FAKE, 1e-6, FAKE, FAKE, 1 << 30,
+                                             None) == _lib.ERR_NULL
+    assert L.w4a16_gemm_gate_up_skip_rmsnorm(FAKE, FAKE, None, 8, 1000, 256, 128, 0, 1, FAKE,
+                                             FAKE, FAKE, 1e-6, FAKE, FAKE, 1 << 30,
+                                             None) == _lib.ERR_SHAPE

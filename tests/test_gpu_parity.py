@@ -282,6 +282,56 @@ def test_gate_up_small_all_outputs(M, g, rms):
     check_close(run_gate_up(p, rms), ref_gate_up(p, rms=rms), f"gate_up M={M} g={g} rms={rms}")
 
 
+# ------------------------------------------------- skip + RMSNorm prologue
+
+
+@pytest.mark.parametrize("M,K,N,g,gu", [(1, 1024, 384, 128, False), (8, 1152, 256, 32, False),
+                                        (16, 1024, 512, 64, True), (20, 1152, 256, 64, False),
+                                        (64, 2048, 512, 16, False), (130, 1024, 256, 128, True),
+                                        (3, 1024, 256, 128, True)])
+def test_skip_rmsnorm_prologue_all_outputs(M, K, N, g, gu):
+    """X = RMSNorm(A + residual): every output against the oracle, and the
+    residual sum written out bit-exactly (one fp16 rounding per element)."""
+    p = synth.make_problem(M, K, N, g, seed=M * 3 + K, gamma=True, gate_up=gu)
+    R = np.random.default_rng(M + K).standard_normal((M, K)).astype(F16)
+    S = oracle.skip_sum(p.A, R)
+    A, Rd, gm = to_dev(p.A), to_dev(R), to_dev(p.gamma)
+    w = repack_dev(p.w)
+    s_out = torch.full((M, K), float("nan"), dtype=torch.float16, device="cuda")
+    if gu:
+        wu = repack_dev(p.w_up)
+        y = w4.gemm_gate_up(A, w, wu, gamma=gm, residual=Rd, residual_out=s_out, out=nan_out(M, N))
+        ref = oracle.gate_up(S, (p.w.qweight, p.w.scales, p.w.zeros),
+                             (p.w_up.qweight, p.w_up.scales, p.w_up.zeros), g, N, gamma=p.gamma)
+    else:
+        y = w4.gemm(A, w, gamma=gm, residual=Rd, residual_out=s_out, out=nan_out(M, N))
+        ref = oracle.gemm(S, p.w.qweight, p.w.scales, p.w.zeros, g, N, gamma=p.gamma)
+    torch.cuda.synchronize()
+    check_close(y.cpu().numpy(), ref, f"skip rmsnorm M={M} K={K} gu={gu}")
+    assert np.array_equal(s_out.cpu().numpy().view(np.uint16), S.view(np.uint16))
+    # the same without writing the sum
+    y2 = (w4.gemm_gate_up(A, w, wu, gamma=gm, residual=Rd) if gu
+          else w4.gemm(A, w, gamma=gm, residual=Rd))
+    assert torch.equal(y2, y)
+
+
+@pytest.mark.parametrize("M", [1, 32])
+def test_skip_rmsnorm_decode_shape_sampled(M):
+    K, N, g = 5120, 13824, 128
+    p = synth.make_problem(M, K, N, g, seed=40 + M, gamma=True, bias=True)
+    R = np.random.default_rng(M).standard_normal((M, K)).astype(F16)
+    S = oracle.skip_sum(p.A, R)
+    s_out = torch.full((M, K), float("nan"), dtype=torch.float16, device="cuda")
+    y = w4.gemm(to_dev(p.A), repack_dev(p.w), gamma=to_dev(p.gamma), residual=to_dev(R),
+                residual_out=s_out, epilogue="bias", bias=to_dev(p.bias), out=nan_out(M, N))
+    cols = sample_cols(N, 96, seed=M)
+    ref = oracle.gemm(S, p.w.qweight, p.w.scales, p.w.zeros, g, N, gamma=p.gamma,
+                      epilogue="bias", bias=p.bias, cols=cols)
+    torch.cuda.synchronize()
+    check_close(y.cpu().numpy()[:, cols], ref, f"skip rmsnorm decode M={M}")
+    assert np.array_equal(s_out.cpu().numpy().view(np.uint16), S.view(np.uint16))
+
+
 # ------------------------------------- M=8 decode shapes and split-K control
 
 # The shapes the "Small-M split-K retune" update tunes at M=8: o/q

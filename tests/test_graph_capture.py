@@ -1,0 +1,134 @@
+"""Capture contract ("Stage 2 of spec-capture" and "What's landed" updates on
+the onnx-genai pull request: a warmed call is capture-safe when its launch
+grid is static, nothing is allocated on replay and nothing is read back to
+the host).
+
+A warm call of each entry point is captured into a HIP graph (through
+torch.cuda.CUDAGraph) and replayed several times, with eager work of the
+program (other library calls on other inputs, torch ops, synchronizations)
+between the replays; every replay must reproduce the eager result
+bit-for-bit.  The shapes include the split-K path, whose arrival counters
+must be back at zero after every replay.  Expected values are the eager
+calls of the same library (the property under test is replay == eager);
+the eager results themselves are pinned to the oracle by the parity tests.
+"""
+import numpy as np
+import pytest
+import torch
+
+import decode_w4a16_repack_amd as w4
+from decode_w4a16_repack_amd import synth
+
+from gpu_cases import repack_dev, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _capture(fn):
+    """Warm fn eagerly, then capture one call of it on a side stream."""
+    fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            fn()
+    torch.cuda.synchronize()
+    return g
+
+
+# (M, K, N, group, kind): stream kernel without and with split-K, tile
+# kernel with one and two 64-row blocks, gate_up, RMSNorm and bias epilogues
+CASES = [
+    (1, 5120, 13824, 128, "gemm"),
+    (1, 5120, 256, 128, "gemm"),          # split-K across workgroups
+    (8, 13696, 4096, 128, "gemm"),        # deep k: split-K
+    (16, 1024, 384, 32, "rms"),
+    (64, 1024, 512, 64, "bias_relu"),
+    (130, 2048, 512, 128, "gemm"),
+    (8, 1024, 256, 128, "gate_up"),       # split-K gate_up with RMSNorm
+    (40, 1024, 256, 16, "gate_up"),
+]
+
+
+@pytest.mark.parametrize("M,K,N,g,kind", CASES)
+def test_graph_replay_is_bit_identical_to_eager(M, K, N, g, kind):
+    p = synth.make_problem(M, K, N, g, seed=M + N, gamma=True, bias=True, gate_up=(kind == "gate_up"))
+    w = repack_dev(p.w)
+    wu = repack_dev(p.w_up) if kind == "gate_up" else None
+    A, gm, b = to_dev(p.A), to_dev(p.gamma), to_dev(p.bias)
+    ws = w4.Workspace()
+    ws.get(8 << 20, "cuda")  # sized once: no reallocation can move it after capture
+    out = torch.empty((M, N), dtype=torch.float16, device="cuda")
+
+    def call():
+        if kind == "gate_up":
+            w4.gemm_gate_up(A, w, wu, gamma=gm, out=out, workspace=ws)
+        elif kind == "rms":
+            w4.gemm(A, w, gamma=gm, out=out, workspace=ws)
+        elif kind == "bias_relu":
+            w4.gemm(A, w, epilogue="bias_relu", bias=b, out=out, workspace=ws)
+        else:
+            w4.gemm(A, w, out=out, workspace=ws)
+
+    call()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    g_ = _capture(call)
+    # other eager work on the same workspace between replays: a different
+    # shape that also splits k (its counters share the workspace)
+    q = synth.make_problem(2, 1024, 512, 128, seed=99)
+    wq, Aq = repack_dev(q.w), to_dev(q.A)
+    ref_q = w4.gemm(Aq, wq, workspace=ws).clone()
+    for r in range(4):
+        out.fill_(float("nan"))
+        g_.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {r} differs from the eager call"
+        assert torch.equal(w4.gemm(Aq, wq, workspace=ws), ref_q)
+        torch.cuda.synchronize()
+
+
+def test_replay_reads_current_inputs():
+    """The graph holds pointers, not values: new input data written into the
+    captured buffers is what the next replay computes on."""
+    p1 = synth.make_problem(4, 1024, 256, 64, seed=1)
+    p2 = synth.make_problem(4, 1024, 256, 64, seed=2)
+    w = repack_dev(p1.w)
+    A = to_dev(p1.A)
+    ws = w4.Workspace()
+    ws.get(1 << 20, "cuda")
+    out = torch.empty((4, 256), dtype=torch.float16, device="cuda")
+    g_ = _capture(lambda: w4.gemm(A, w, out=out, workspace=ws))
+    ref2 = w4.gemm(to_dev(p2.A), w, workspace=ws).clone()
+    A.copy_(to_dev(p2.A))
+    g_.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref2)
+
+
+def test_replay_allocates_nothing():
+    """No device memory is taken on replay (the library never allocates; the
+    workspace is the caller's)."""
+    p = synth.make_problem(1, 5120, 256, 128, seed=5)
+    w = repack_dev(p.w)
+    A = to_dev(p.A)
+    ws = w4.Workspace()
+    ws.get(1 << 20, "cuda")
+    out = torch.empty((1, 256), dtype=torch.float16, device="cuda")
+    g_ = _capture(lambda: w4.gemm(A, w, out=out, workspace=ws))
+    torch.cuda.synchronize()
+    before = torch.cuda.memory_stats()
+    for _ in range(8):
+        g_.replay()
+    torch.cuda.synchronize()
+    after = torch.cuda.memory_stats()
+    assert after["allocation.all.allocated"] == before["allocation.all.allocated"]
+    assert after["allocated_bytes.all.current"] == before["allocated_bytes.all.current"]
+    assert np.all(np.isfinite(out.float().cpu().numpy()))

@@ -355,3 +355,23 @@ def test_output_magnitude_matches_page_tolerance_scale(oracle_lib):
     cols = np.arange(0, 13824, 3)
     y = oracle.gemm(p.A, p.w.qweight, p.w.scales, p.w.zeros, 128, 13824, cols=cols)
     assert 15.0 < np.abs(y).max() < 60.0
+
+
+def test_skip_sum_rounds_once_to_nearest_even():
+    """S = A + R in fp16 (IEEE 754 binary16, round to nearest, ties to even):
+    exact when representable; 2048 + 1 and 2050 + 1 are ties between
+    neighbours 2 apart and go to the even significand (2048, 2052); a sum
+    past the largest finite value 65504 by half an ulp or more overflows."""
+    import oracle
+    f = np.float16
+    A = np.array([3, -7.5, 2048, 2050, 0.25, 65504, 1e-7], dtype=f)
+    R = np.array([5, 7.5, 1, 1, 0.125, 16, 0], dtype=f)
+    S = oracle.skip_sum(A, R)
+    assert S.dtype == np.float16
+    assert list(S[:5]) == [8, 0, 2048, 2052, 0.375]
+    assert np.isinf(S[5])                      # 65520 is the tie with 2^16: rounds up
+    assert S[6] == A[6]                        # adding zero is the identity
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal((4, 64)).astype(f)
+    y = rng.standard_normal((4, 64)).astype(f)
+    assert np.array_equal(oracle.skip_sum(x, y), oracle.skip_sum(y, x))
