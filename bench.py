@@ -49,7 +49,7 @@ INFINITY_CACHE = 256 << 20
 PAGE_M1_US = 69.5  # the pages' M=1 time for this shape (H200, context only)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemv_m1.json")
 KERNEL_SOURCES = ["decode_w4a16_repack_amd/csrc/" + f for f in
-                  ("stream.hip", "tile.hip", "device.h", "gemm.hip", "common.h")]
+                  ("stream.hip", "panel.hip", "tile.hip", "device.h", "gemm.hip", "common.h")]
 COPY_PROBE_BYTES = 256 << 20  # plain copy of known size, counter calibration
 
 

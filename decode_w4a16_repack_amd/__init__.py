@@ -90,7 +90,8 @@ def plan(M: int, K: int, N: int, group: int, scale_dtype: int = _lib.SCALE_F16,
     info = _lib.PlanInfo()
     st = _lib.lib().w4a16_plan(M, K, N, group, scale_dtype, int(gate_up), split, info)
     _lib.check(st, "w4a16_plan")
-    return Plan("stream" if info.kernel == _lib.KERNEL_STREAM else "tile", info.split,
+    kind = {_lib.KERNEL_STREAM: "stream", _lib.KERNEL_PANEL: "panel"}.get(info.kernel, "tile")
+    return Plan(kind, info.split,
                 info.k_tiles_per_split, tuple(info.grid), info.block, info.lds_bytes,
                 info.workspace_bytes)
 

@@ -29,6 +29,7 @@ ERR_SPLIT = -9
 
 KERNEL_STREAM = 1
 KERNEL_TILE = 2
+KERNEL_PANEL = 3
 
 SCALE_F16 = 0
 SCALE_F32 = 1

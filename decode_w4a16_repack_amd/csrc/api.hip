@@ -50,7 +50,7 @@ int check_workspace(const Plan &pl, const void *ws, size_t ws_bytes) {
   return W4A16_OK;
 }
 
-// The automatic plan (split <= 0) or the stream kernel with `split`
+// The automatic plan (split <= 0) or the stream / panel kernel with `split`
 // workgroups along K; W4A16_ERR_SPLIT when that split cannot run the shape.
 int plan_for(int M, int K, int N, int group, int scale_dtype, bool gate_up, int split,
              Plan &pl) {
@@ -59,8 +59,8 @@ int plan_for(int M, int K, int N, int group, int scale_dtype, bool gate_up, int 
     pl = make_plan(M, K, N, group, sb, gate_up);
     return W4A16_OK;
   }
-  pl = make_plan(M, K, N, group, sb, gate_up, kKindStream, -1, split);
-  return pl.kind == kKindStream ? W4A16_OK : W4A16_ERR_SPLIT;
+  pl = make_plan(M, K, N, group, sb, gate_up, -1, -1, split);
+  return pl.kind != kKindTile ? W4A16_OK : W4A16_ERR_SPLIT;
 }
 
 void fill_packed(GemmArgs &a, int slot, const void *packed, int K, int N,
@@ -283,7 +283,9 @@ int w4a16_plan(int M, int K, int N, int group, int scale_dtype, int gate_up, int
   Plan pl;
   st = plan_for(M, K, N, group, scale_dtype, gate_up != 0, split, pl);
   if (st != W4A16_OK) return st;
-  info->kernel = pl.kind == kKindStream ? W4A16_KERNEL_STREAM : W4A16_KERNEL_TILE;
+  info->kernel = pl.kind == kKindStream  ? W4A16_KERNEL_STREAM
+                 : pl.kind == kKindPanel ? W4A16_KERNEL_PANEL
+                                         : W4A16_KERNEL_TILE;
   info->split = pl.split;
   info->k_tiles_per_split = pl.cps;
   info->grid[0] = pl.gx;

@@ -30,6 +30,14 @@ struct StreamCfg {
 constexpr int kNumStreamCfgs = 3;
 extern const StreamCfg kStreamCfgs[kNumStreamCfgs];
 
+// Tile configurations of the panel kernel (16 < M <= 32): MT 16-row tiles
+// per workgroup, and CPW, KPW, NWK, PD as for the stream kernel.
+struct PanelCfg {
+  int mt, cpw, kpw, nwk, pd;
+};
+constexpr int kNumPanelCfgs = 1;
+extern const PanelCfg kPanelCfgs[kNumPanelCfgs];
+
 inline size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 
 // Byte offsets of the packed regions (layout version 1).
@@ -78,10 +86,10 @@ struct GemmArgs {
 };
 
 // Launch plan of one GEMM call, a pure function of the shape.
-enum PlanKind { kKindStream = 2, kKindTile = 3 };
+enum PlanKind { kKindStream = 2, kKindTile = 3, kKindPanel = 4 };
 
 struct Plan {
-  int kind;     // PlanKind: stream.hip (kStreamCfgs) or tile.hip
+  int kind;     // PlanKind: stream.hip (kStreamCfgs), panel.hip (kPanelCfgs) or tile.hip
   int cfg;      // index into the kernel's configuration table
   int gx, gy, gz;
   int block;  // threads per workgroup
@@ -100,6 +108,9 @@ Plan make_plan(int M, int K, int N, int group, int scale_bytes, bool gate_up,
 
 hipError_t launch_stream(const GemmArgs &a, const Plan &p, int group, bool scale_f32,
                          bool gate_up, hipStream_t stream);
+
+hipError_t launch_panel(const GemmArgs &a, const Plan &p, int group, bool scale_f32,
+                        bool gate_up, hipStream_t stream);
 
 // tile.hip (M > 16): column tiles per wavefront and weight stream (wide:
 // several 64-row blocks), LDS bytes, output columns per workgroup

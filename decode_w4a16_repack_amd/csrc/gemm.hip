@@ -1,5 +1,6 @@
 // Launch planning for the fused W4A16 GEMM: stream.hip for M <= 16 (the
-// HBM-bound decode regime), tile.hip above.
+// HBM-bound decode regime), panel.hip above (tile.hip for what neither
+// takes).
 //
 // The plan is a pure function of the shape: it picks the kernel
 // configuration, the grid and, only where a workgroup's k range cannot hold
@@ -107,8 +108,72 @@ bool plan_stream(Plan &p, int M, int K, int N, int group, int scale_bytes, bool 
   return true;
 }
 
-// Tile kernel plan (M > 16, and M <= 16 shapes the stream kernel cannot
-// take): 64-row blocks x tile_columns() per workgroup over the whole K; wide
+// Panel kernel plan (16 < M <= 32): one 32-row block, 4 column tiles per
+// workgroup; k split across workgroups as for the stream kernel (deep K, or
+// a grid short of one workgroup per compute unit).  Above 32 rows the
+// activation fragments each wavefront loads from L2 grow with M while the
+// weight stream does not, and the tile kernel (activations shared through
+// LDS) is faster (K=5120 N=13824: M=64 28.3 vs 23.9 us).  Each
+// wavefront's private LDS region holds its slice's scales and zero-points
+// and, at the end, one weight stream's partial sums.
+bool plan_panel(Plan &p, int M, int K, int N, int group, int scale_bytes, bool gate_up,
+                int force_split) {
+  const int NTL = N / kTileN;
+  const int KC = K / kTileK;
+  const int NW = gate_up ? 2 : 1;
+  if (M <= 16 || M > 32) return false;
+  const int mt = 2;
+  p.kind = kKindPanel;
+  p.gz = (M + 16 * mt - 1) / (16 * mt);
+  p.cfg = -1;
+  for (int i = 0; i < kNumPanelCfgs; ++i)
+    if (kPanelCfgs[i].mt == mt) p.cfg = i;
+  if (p.cfg < 0) return false;
+  const PanelCfg c = kPanelCfgs[p.cfg];
+  const int per_wg = c.nwk * c.kpw;  // k tiles one workgroup covers
+  p.gx = (NTL + c.cpw - 1) / c.cpw;
+  p.block = 64 * c.nwk;
+  const int base = p.gx * p.gz;
+  const int s_min = (KC + per_wg - 1) / per_wg;
+  if (force_split > 0 && (force_split < s_min || force_split > KC)) return false;
+  int S = choose_split(base, KC, force_split);
+  if (S < s_min) S = s_min;
+  if (S > KC) S = KC;
+  p.cps = (KC + S - 1) / S;
+  p.split = (KC + p.cps - 1) / p.cps;
+  p.gy = p.split;
+  const int gpw = c.kpw * (kTileK / group);
+  const size_t meta = NW * ((size_t)c.cpw * gpw * 16 * scale_bytes + align16((size_t)c.cpw * gpw * 8));
+  const size_t red = (size_t)c.cpw * c.mt * 1024;  // one weight stream's partial sums
+  const size_t region = align16(meta > red ? meta : red);
+  p.lds_s = (int)region;
+  p.lds_r = (int)(c.nwk * region);
+  // (+ one int: the workgroup's "last to arrive" flag of the split path)
+  p.lds_bytes = (size_t)p.lds_r + (size_t)c.nwk * 16 * c.mt * 4 + 16;
+  if (p.lds_bytes > 160 * 1024) return false;
+  p.rows_pow2 = 0;
+  p.alds = 0;
+  // workspace: arrival counters (one per output tile of a workgroup, in the
+  // same fixed region as every other plan's, so that all plans leave the
+  // same words at zero), row sums of squares [tile][S][16 * MT], partial
+  // sums [S][NW][M][N]
+  size_t off = 0;
+  if (p.split > 1) {
+    const size_t tiles = (size_t)p.gx * p.gz;
+    if (tiles > (size_t)kMaxSplitBlocks) return false;
+    p.ws_cnt_off = 0;
+    off = align256((size_t)kMaxSplitBlocks * 4);
+    p.ws_rms_off = off;
+    off = align256(off + tiles * p.split * 16 * c.mt * 4);
+    p.ws_part_off = off;
+    off = align256(off + (size_t)p.split * NW * M * N * 4);
+  }
+  p.ws_total = off;
+  return true;
+}
+
+// Tile kernel plan (M > 16 shapes the panel kernel cannot take, and M <= 16
+// shapes the stream kernel cannot take): 64-row blocks x tile_columns() per workgroup over the whole K; wide
 // column blocks only when several row blocks keep the grid full.
 void plan_tile(Plan &p, int M, int K, int N, int group, int scale_bytes, bool gate_up) {
   p.kind = kKindTile;
@@ -129,10 +194,13 @@ void plan_tile(Plan &p, int M, int K, int N, int group, int scale_bytes, bool ga
 Plan make_plan(int M, int K, int N, int group, int scale_bytes, bool gate_up, int force_kind,
                int force_cfg, int force_split) {
   Plan p{};
-  if (force_kind != kKindTile &&
+  if ((force_kind < 0 || force_kind == kKindStream) &&
       plan_stream(p, M, K, N, group, scale_bytes, gate_up,
-                  force_kind == kKindStream ? force_cfg : -1,
-                  force_kind == kKindStream ? force_split : 0))
+                  force_kind == kKindStream ? force_cfg : -1, force_split))
+    return p;
+  p = Plan{};
+  if ((force_kind < 0 || force_kind == kKindPanel) &&
+      plan_panel(p, M, K, N, group, scale_bytes, gate_up, force_split))
     return p;
   p = Plan{};
   plan_tile(p, M, K, N, group, scale_bytes, gate_up);
@@ -142,6 +210,7 @@ Plan make_plan(int M, int K, int N, int group, int scale_bytes, bool gate_up, in
 hipError_t launch_gemm(const GemmArgs &a, const Plan &pl, int group, bool scale_f32,
                        bool gate_up, hipStream_t stream) {
   if (pl.kind == kKindStream) return launch_stream(a, pl, group, scale_f32, gate_up, stream);
+  if (pl.kind == kKindPanel) return launch_panel(a, pl, group, scale_f32, gate_up, stream);
   return launch_tile(a, pl, group, scale_f32, gate_up, stream);
 }
 

@@ -257,7 +257,7 @@ stream_kernel(const GemmArgs p) {
     const size_t tile = (size_t)min(ct0 + w, NTL - 1) * KC + kc;
 #pragma unroll
     for (int i = 0; i < NW; ++i)
-      wv[i][f] = reinterpret_cast<const u32x4 *>(p.w[i] + tile * kTileBytes)[lane];
+      wv[i][f] = load_weights(p.w[i] + tile * kTileBytes, lane);
   };
 #pragma unroll
   for (int f = 0; f < PDE; ++f) issue_tile(f);

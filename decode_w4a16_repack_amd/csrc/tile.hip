@@ -208,7 +208,7 @@ tile_kernel(const GemmArgs p) {
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
         const size_t tile = (size_t)min(ctw + ct, NTL - 1) * KC + kt;
-        wv[i][ct] = reinterpret_cast<const u32x4 *>(p.w[i] + tile * kTileBytes)[lane];
+        wv[i][ct] = load_weights<CT == 1>(p.w[i] + tile * kTileBytes, lane);  // CT > 1: several row blocks
       }
   };
 

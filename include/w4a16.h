@@ -149,15 +149,18 @@ int w4a16_gemm_gate_up(const void *A, int M, int K, int N, int group,
  * 4096x2*13696 and 5120x2*13824 at M=8).  The automatic choice (split = 0)
  * keeps at least two wavefronts per compute unit in flight and splits
  * further only when the k range exceeds what one workgroup covers.  A
- * positive `split` forces the streaming kernel (M <= 16) with that many k
- * slices; the actual factor may round down so that no slice is empty.
- * W4A16_ERR_SPLIT when the shape cannot run with it: M > 16, split larger
- * than K/128, or smaller than the k range one workgroup can cover.
+ * positive `split` forces that many k slices on the streaming kernel
+ * (M <= 16) or the panel kernel (16 < M <= 32); the actual factor may round down
+ * so that no slice is empty.  W4A16_ERR_SPLIT when the shape cannot run
+ * with it: split larger than K/128, smaller than the k range one workgroup
+ * can cover, or a shape only the tile kernel takes.
  */
-enum { W4A16_KERNEL_STREAM = 1, W4A16_KERNEL_TILE = 2 };
+enum { W4A16_KERNEL_STREAM = 1, W4A16_KERNEL_TILE = 2, W4A16_KERNEL_PANEL = 3 };
 
 typedef struct {
-  int kernel;             /* W4A16_KERNEL_STREAM (M <= 16) or W4A16_KERNEL_TILE */
+  int kernel;             /* W4A16_KERNEL_STREAM (M <= 16), W4A16_KERNEL_PANEL
+                             (16 < M <= 32) or W4A16_KERNEL_TILE (above, and shapes
+                             the others cannot take) */
   int split;              /* workgroups along K per output tile (1 = no split-K) */
   int k_tiles_per_split;  /* 128-wide k tiles one split covers */
   int grid[3];            /* launch grid */

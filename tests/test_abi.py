@@ -149,14 +149,15 @@ def plan(L, M, K, N, g=128, sdt=0, gu=0, split=0):
 
 
 def test_plan_query_matches_workspace_and_kernel_choice(L):
-    """Stream kernel for M <= 16, tile kernel above; the plan's workspace is
+    """Stream kernel for M <= 16, panel kernel to M = 32, tile kernel above; the plan's workspace is
     what w4a16_workspace_bytes reports; the grid covers every column tile."""
     for M, K, N, gu in [(1, 5120, 13824, 0), (8, 13696, 4096, 0), (16, 4096, 4096, 0),
                         (8, 4096, 13696, 1), (17, 5120, 13824, 0), (128, 1024, 384, 1),
                         (1, 1024, 384, 0)]:
         st, info = plan(L, M, K, N, gu=gu)
         assert st == _lib.OK
-        assert info.kernel == (_lib.KERNEL_STREAM if M <= 16 else _lib.KERNEL_TILE)
+        assert info.kernel == (_lib.KERNEL_STREAM if M <= 16 else
+                               _lib.KERNEL_PANEL if M <= 32 else _lib.KERNEL_TILE)
         assert info.block in (256, 512)
         assert info.k_tiles_per_split * info.split >= K // 128
         assert info.k_tiles_per_split * (info.split - 1) < K // 128  # no empty split
@@ -169,14 +170,17 @@ def test_plan_query_matches_workspace_and_kernel_choice(L):
 def test_plan_deep_k_splits_and_forced_splits(L):
     """K = 13696 (107 k tiles) is deeper than one workgroup covers: the
     automatic plan splits it; a forced split below that minimum, above the
-    tile count, or for M > 16 is rejected; a forced split rounds so that no
-    slice is empty."""
+    tile count, or on the tile kernel (M > 32) is rejected; a forced split
+    rounds so that no slice is empty."""
     st, auto = plan(L, 8, 13696, 4096)
     assert st == _lib.OK and auto.split >= 3
     for sk in (1, 2):
         assert plan(L, 8, 13696, 4096, split=sk)[0] == _lib.ERR_SPLIT
     assert plan(L, 8, 1024, 384, split=9)[0] == _lib.ERR_SPLIT    # 8 k tiles
-    assert plan(L, 17, 4096, 4096, split=2)[0] == _lib.ERR_SPLIT  # tile kernel
+    st, f = plan(L, 17, 4096, 4096, split=2)                      # panel kernel, M > 16
+    assert st == _lib.OK and f.kernel == _lib.KERNEL_PANEL and f.split == 2
+    assert plan(L, 17, 4096, 4096, split=33)[0] == _lib.ERR_SPLIT  # 32 k tiles
+    assert plan(L, 33, 4096, 4096, split=2)[0] == _lib.ERR_SPLIT   # tile kernel
     st, f = plan(L, 8, 5120, 13824, split=9)   # 40 tiles: 5 per split -> 8 splits
     assert st == _lib.OK and (f.split, f.k_tiles_per_split) == (8, 5)
     for sk in (3, 4, 8, 16):
@@ -199,7 +203,7 @@ def test_forced_split_workspace_checked_before_launch(L):
     assert L.w4a16_gemm_split(FAKE, 8, 13696, 4096, 128, 0, 1, FAKE, 0, None, None, 1e-6,
                               FAKE, FAKE, 1 << 30, 2, None) == _lib.ERR_SPLIT
     assert L.w4a16_gemm_gate_up_split(FAKE, 20, 4096, 4096, 128, 0, 1, FAKE, FAKE, None, 1e-6,
-                                      FAKE, FAKE, 1 << 30, 4, None) == _lib.ERR_SPLIT
+                                      FAKE, FAKE, 1 << 30, 33, None) == _lib.ERR_SPLIT
 
 
 def test_library_sources_never_allocate_sync_or_memset():

@@ -72,7 +72,7 @@ def test_tiny_config_full_output():
     check_close(run_gemm(p), ref_gemm(p), "tiny")
 
 
-SMALL_M = [1, 2, 3, 7, 16, 17, 33, 64, 65, 128, 130]
+SMALL_M = [1, 2, 3, 7, 16, 17, 24, 32, 33, 64, 65, 128, 130]
 
 
 @pytest.mark.parametrize("M", SMALL_M)
@@ -87,7 +87,7 @@ def test_small_shapes_all_outputs(M, g):
 
 @pytest.mark.parametrize("sdt", [F16, F32])
 @pytest.mark.parametrize("asym", [True, False])
-@pytest.mark.parametrize("M", [1, 16, 40])
+@pytest.mark.parametrize("M", [1, 16, 29, 40])
 def test_scale_dtype_and_zp_variants(sdt, asym, M):
     p = synth.make_problem(M, 2048, 256, 64, seed=3, scale_dtype=sdt, asym=asym)
     check_close(run_gemm(p), ref_gemm(p), f"M={M} {sdt.__name__} asym={asym}")
@@ -276,7 +276,8 @@ def test_gate_up_config_sampled():
     check_close(got[:, cols], ref_gate_up(p, cols=cols), "gate_up M=32")
 
 
-@pytest.mark.parametrize("M,g,rms", [(1, 128, False), (8, 16, True), (3, 32, False), (70, 64, True)])
+@pytest.mark.parametrize("M,g,rms", [(1, 128, False), (8, 16, True), (3, 32, False), (70, 64, True),
+                                     (25, 16, True), (32, 128, False)])
 def test_gate_up_small_all_outputs(M, g, rms):
     p = synth.make_problem(M, 1024, 256, g, seed=M + g, gate_up=True, gamma=rms)
     check_close(run_gate_up(p, rms), ref_gate_up(p, rms=rms), f"gate_up M={M} g={g} rms={rms}")
@@ -287,6 +288,7 @@ def test_gate_up_small_all_outputs(M, g, rms):
 
 @pytest.mark.parametrize("M,K,N,g,gu", [(1, 1024, 384, 128, False), (8, 1152, 256, 32, False),
                                         (16, 1024, 512, 64, True), (20, 1152, 256, 64, False),
+                                        (27, 1024, 256, 32, True),
                                         (64, 2048, 512, 16, False), (130, 1024, 256, 128, True),
                                         (3, 1024, 256, 128, True)])
 def test_skip_rmsnorm_prologue_all_outputs(M, K, N, g, gu):
@@ -376,7 +378,7 @@ def test_forced_splits_match_oracle_and_repeat():
         check_close(y1.cpu().numpy()[:, cols], ref, f"down_proj split={sk}")
 
 
-@pytest.mark.parametrize("M", [1, 8, 16])
+@pytest.mark.parametrize("M", [1, 8, 16, 17, 32])
 def test_forced_splits_all_outputs_small(M):
     """Small shape, every output, every feasible split (1 .. 8 k tiles)."""
     p = synth.make_problem(M, 1024, 384, 32, seed=M, gate_up=True, gamma=True)
