@@ -85,9 +85,22 @@ def test_small_shapes_all_outputs(M, g):
     check_close(run_gemm(p), ref_gemm(p), f"M={M} g={g} {sdt.__name__} asym={asym}")
 
 
+@pytest.mark.parametrize("M,g,epi", [(65, 32, "none"), (100, 64, "bias"), (128, 128, "bias_relu"),
+                                     (129, 128, "none"), (256, 64, "bias_relu"), (300, 32, "bias")])
+def test_large_m_all_outputs(M, g, epi):
+    """Several 64-row blocks with ragged rows (M % 64) and ragged column
+    blocks (N = 400 is 25 column tiles), every output against the oracle,
+    and the result repeats bit-identically."""
+    sdt = F32 if M % 2 else F16
+    p = synth.make_problem(M, 1536, 400, g, seed=M + g, scale_dtype=sdt, asym=M != 129, bias=True)
+    got = run_gemm(p, epilogue=epi)
+    check_close(got, ref_gemm(p, epilogue=epi), f"M={M} g={g} {epi}")
+    assert np.array_equal(got, run_gemm(p, epilogue=epi)), "not repeatable"
+
+
 @pytest.mark.parametrize("sdt", [F16, F32])
 @pytest.mark.parametrize("asym", [True, False])
-@pytest.mark.parametrize("M", [1, 16, 29, 40])
+@pytest.mark.parametrize("M", [1, 16, 29, 40, 90])
 def test_scale_dtype_and_zp_variants(sdt, asym, M):
     p = synth.make_problem(M, 2048, 256, 64, seed=3, scale_dtype=sdt, asym=asym)
     check_close(run_gemm(p), ref_gemm(p), f"M={M} {sdt.__name__} asym={asym}")
