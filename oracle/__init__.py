@@ -197,3 +197,16 @@ def skip_sum(A, residual) -> np.ndarray:
 def to_fp16(y: np.ndarray) -> np.ndarray:
     """Round the f64 result to fp16, nearest-even (IEEE default)."""
     return np.asarray(y, dtype=np.float64).astype(np.float16)
+
+
+def mlp(A, gate, up, down, group: int, I: int, H: int, *, gamma=None,
+        eps: float = 1e-6, cols=None) -> np.ndarray:
+    """f64 output [M][len(cols) or H] of the MLP block that the "gate_up
+    SwiGLU MLP fusion" update names as the bulk of the decode cost: the
+    paired gate/up projection (K = A's width, N = I, optional RMSNorm
+    prologue), its result rounded once to fp16 (the intermediate is an fp16
+    tensor handed from one projection to the next), then the plain down
+    projection of that intermediate (K = I, N = H).  ``gate``, ``up`` and
+    ``down`` are (qweight, scales, zeros); all three share ``group``."""
+    h = to_fp16(gate_up(A, gate, up, group, I, gamma=gamma, eps=eps))
+    return gemm(h, down[0], down[1], down[2], group, H, cols=cols)

@@ -252,6 +252,59 @@ def test_gate_up_rmsnorm_matches_prenormalized(oracle_lib):
     assert np.allclose(a, b, rtol=1e-12, atol=1e-12)
 
 
+# ------------------------------------------------------------------ MLP chain
+
+
+def test_mlp_permutation_down_returns_rounded_intermediate(oracle_lib):
+    """A down projection whose dequantized weight is a permutation matrix
+    (code 9 on one entry per row, 8 elsewhere, zero-point 8, scale 1) moves
+    intermediate column i to output column perm[i] unchanged: the chain's
+    output is then exactly the fp16-rounded gate_up result, permuted.  The
+    permutation is not an involution, so a transposed down operand fails."""
+    p = synth.make_problem(2, 256, 128, 32, seed=41, gate_up=True)
+    g, u = (p.w.qweight, p.w.scales, p.w.zeros), (p.w_up.qweight, p.w_up.scales, p.w_up.zeros)
+    I = H = 128
+    perm = np.roll(np.arange(H), 5)
+    codes = np.full((I, H), 8, np.uint8)
+    codes[np.arange(I), perm] = 9
+    G = I // p.group
+    d = synth.weight_from_codes(codes, np.ones((H, G), np.float16), None, p.group)
+    y = oracle.mlp(p.A, g, u, (d.qweight, d.scales, None), p.group, I, H)
+    h = oracle.gate_up(p.A, g, u, p.group, I).astype(np.float16).astype(np.float64)
+    ref = np.empty_like(h)
+    ref[:, perm] = h
+    assert np.array_equal(y, ref)
+
+
+@pytest.mark.parametrize("asym", [True, False])
+def test_mlp_tiny_vs_numpy_from_raw_draws(oracle_lib, asym):
+    """Dense gate, up and down weights rebuilt from the raw draws; silu from
+    scipy; the intermediate rounded to fp16 by numpy; numpy's matmul."""
+    from scipy.special import expit
+    rng = np.random.default_rng(43)
+    M, K, I, H, group = 3, 256, 128, 48, 32
+    A = rng.standard_normal((M, K)).astype(np.float16)
+    ws = [synth.draw_weight(rng, K, I, group, asym=asym),
+          synth.draw_weight(rng, K, I, group, asym=asym),
+          synth.draw_weight(rng, I, H, group, asym=asym)]
+
+    def dense(w):
+        kg = np.arange(w.K) // group
+        zp = w.zp if asym else np.full((w.N, w.K // group), 8, np.uint8)
+        return (w.codes.astype(np.float64) - zp.T[kg, :]) * w.scales.astype(np.float64).T[kg, :]
+    Wg, Wu, Wd = (dense(w) for w in ws)
+    a = A.astype(np.float64)
+    yg, yu = a @ Wg, a @ Wu
+    h = (yg * expit(yg) * yu).astype(np.float16).astype(np.float64)
+    ref = h @ Wd
+    t = [(w.qweight, w.scales, w.zeros) for w in ws]
+    y = oracle.mlp(A, t[0], t[1], t[2], group, I, H)
+    assert np.allclose(y, ref, rtol=0, atol=1e-12 * np.abs(ref).max())
+    cols = np.array([47, 0, 16, 31])
+    ys = oracle.mlp(A, t[0], t[1], t[2], group, I, H, cols=cols)
+    assert np.array_equal(ys, y[:, cols])
+
+
 # ------------------------------------------------------------------ byte model
 
 
