@@ -11,7 +11,8 @@ same shape for M = 2..128, with µs, TFLOP/s (2MNK / t, croqtile tutorial
 "TFLOPS"), GB/s and the fraction of the HBM and fp16-MFMA peaks; the group
 sweep at M=16 K=N=4096 with the fused bias+ReLU epilogue and RMSNorm prologue
 against their unfused chains (analytic bytes beside measured time); the fused
-gate_up SwiGLU at M=32; a streaming-read probe of the achievable HBM rate; and
+gate_up SwiGLU at M=32; the MLP block (gate_up, fp16 intermediate, down
+projection) at the decode MLP shapes; a streaming-read probe of the achievable HBM rate; and
 the CPU oracle timed on the host's cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
@@ -279,6 +280,7 @@ def extras(ws):
     del pr
     torch.cuda.empty_cache()
     res["split_sweep_m8"] = split_sweep(ws)
+    res["mlp_chain"] = mlp_chain(ws)
     return res
 
 
@@ -330,6 +332,63 @@ def split_sweep(ws, M=8, group=128):
             f"{t_auto:6.2f} us ({row['auto_pct_hbm_peak']:4.1f}% HBM); forced "
             + " ".join(f"sk{k}={v:.2f}" for k, v in sorted(forced.items())))
         del pr
+        torch.cuda.empty_cache()
+    return rows
+
+
+# The decode MLP blocks of the "Small-M split-K retune" update's shapes:
+# (name, hidden H, intermediate I).  gate_up is H x 2*I, down is I x H.
+MLP_SHAPES = [("mlp_4096x13696", 4096, 13696), ("mlp_5120x13824", 5120, 13824)]
+
+
+def mlp_chain(ws, Ms=(1, 8, 32), group=128):
+    """w4a16_mlp (gate_up with the RMSNorm prologue, fp16 intermediate, down
+    projection) at the decode MLP shapes, beside its two projections timed
+    alone.  Bytes: the three packed weights, A, the intermediate written and
+    read back, and the output."""
+    import torch
+    import decode_w4a16_repack_amd as w4
+    rows = []
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(500)
+
+    def packed(K_, N_):
+        G = K_ // group
+        q = torch.randint(0, 256, (N_, K_ // 2), dtype=torch.uint8, device="cuda", generator=gen)
+        sc = (torch.rand((N_, G), device="cuda", generator=gen) * 0.019 + 0.001).half()
+        z = torch.randint(0, 256, (N_, (G + 1) // 2), dtype=torch.uint8, device="cuda", generator=gen)
+        return w4.repack(q, sc, z, K_, N_, group)
+    for name, H, I in MLP_SHAPES:
+        wbytes = 2 * algorithmic_bytes(0, H, I, group) + algorithmic_bytes(0, I, H, group)
+        R = max(2, math.ceil(2 * INFINITY_CACHE / wbytes))
+        sets = [{"w": [packed(H, I), packed(H, I), packed(I, H)],
+                 "gamma": (1.0 + 0.1 * torch.randn((H,), device="cuda", generator=gen)).half()}
+                for _ in range(R)]
+        for M in Ms:
+            for st in sets:
+                st["A"] = torch.randn((M, H), device="cuda", generator=gen).half()
+                st["inter"] = torch.empty((M, I), dtype=torch.float16, device="cuda")
+                st["out"] = torch.empty((M, H), dtype=torch.float16, device="cuda")
+            byt = wbytes + 2 * M * H + 2 * 2 * M * I + 2 * M * H
+            t_mlp = time_graph(lambda st: w4.mlp(st["A"], *st["w"], gamma=st["gamma"],
+                                                 inter=st["inter"], out=st["out"], workspace=ws),
+                               sets)
+            t_gu = time_graph(lambda st: w4.gemm_gate_up(st["A"], st["w"][0], st["w"][1],
+                                                         gamma=st["gamma"], out=st["inter"],
+                                                         workspace=ws), sets)
+            t_dn = time_graph(lambda st: w4.gemm(st["inter"], st["w"][2], out=st["out"],
+                                                 workspace=ws), sets)
+            row = {"shape": name, "M": M, "H": H, "I": I, "group": group, "rotating_sets": R,
+                   "algorithmic_bytes": byt, "mlp_us": t_mlp,
+                   "mlp_GBps": byt / t_mlp / 1e3,
+                   "mlp_pct_hbm_peak": 100 * byt / t_mlp / 1e3 / HBM_PEAK_GBS,
+                   "gate_up_alone_us": t_gu, "down_alone_us": t_dn,
+                   "gate_up_plan": w4.plan(M, H, I, group, gate_up=True).__dict__,
+                   "down_plan": w4.plan(M, I, H, group).__dict__}
+            rows.append(row)
+            log(f"[bench] {name} M={M:2d}: mlp {t_mlp:6.2f} us ({row['mlp_pct_hbm_peak']:4.1f}% HBM); "
+                f"gate_up alone {t_gu:6.2f} + down alone {t_dn:6.2f} us")
+        del sets
         torch.cuda.empty_cache()
     return rows
 

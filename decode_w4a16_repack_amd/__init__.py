@@ -10,6 +10,7 @@ without the built library or without a GPU raises.
     y = gemm(A, pw, epilogue="bias_relu", bias=b)
     y = gemm(A, pw, gamma=g, eps=1e-6)                  # RMSNorm prologue
     y = gemm_gate_up(A, pw_gate, pw_up)                 # silu(A.Wg) * (A.Wu)
+    y = mlp(A, pw_gate, pw_up, pw_down)                 # (silu(A.Wg) * (A.Wu)) . Wd
 """
 from __future__ import annotations
 
@@ -25,6 +26,7 @@ __all__ = [
     "PackedWeight", "repack", "gemm", "gemm_gate_up", "packed_bytes",
     "workspace_bytes", "layout_version", "add_bias", "relu", "rmsnorm",
     "probe_read", "probe_copy", "Workspace", "plan", "Plan", "W4A16Error",
+    "mlp", "mlp_workspace_bytes",
 ]
 
 
@@ -75,7 +77,7 @@ def workspace_bytes(M: int, K: int, N: int, group: int, gate_up: bool = False) -
 @dataclass
 class Plan:
     """The launch a call of one shape makes (w4a16_plan_info)."""
-    kernel: str          # "stream" (M <= 16) or "tile"
+    kernel: str          # "stream" (M <= 16), "panel" (M <= 32) or "tile"
     split: int           # workgroups along K per output tile
     k_tiles_per_split: int
     grid: tuple
@@ -239,6 +241,55 @@ def gemm_gate_up(A: torch.Tensor, w_gate: PackedWeight, w_up: PackedWeight, *,
     else:
         st = _lib.lib().w4a16_gemm_gate_up(*args, _stream())
     _lib.check(st, "w4a16_gemm_gate_up")
+    return out
+
+
+def mlp_workspace_bytes(M: int, H: int, I: int, group: int) -> int:
+    return _lib.lib().w4a16_mlp_workspace_bytes(M, H, I, group)
+
+
+def mlp(A: torch.Tensor, w_gate: PackedWeight, w_up: PackedWeight, w_down: PackedWeight, *,
+        gamma: Optional[torch.Tensor] = None, eps: float = 1e-6,
+        inter: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+        workspace: Optional[Workspace] = None,
+        residual: Optional[torch.Tensor] = None,
+        residual_out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """MLP block (w4a16_mlp): inter = fp16 silu(X . Wg) * (X . Wu) [M][I],
+    then fp16 [M][H] = inter . Wd.  A is [M][H]; w_gate and w_up have K = H,
+    N = I; w_down has K = I, N = H.  X, gamma, residual and residual_out as
+    in gemm_gate_up().  ``inter`` receives the intermediate when given."""
+    _need_gpu(A, "A", torch.float16)
+    M, H = A.shape
+    for t, n in ((residual, "residual"), (residual_out, "residual_out")):
+        if t is not None:
+            _need_gpu(t, n, torch.float16)
+    _check_residual(A, gamma, residual, residual_out, 0)
+    key = (w_gate.group, w_gate.scale_dtype, w_gate.has_zp)
+    for w in (w_up, w_down):
+        if (w.group, w.scale_dtype, w.has_zp) != key:
+            raise ValueError("gate, up and down weights must share group, scale dtype, zp")
+    I = w_gate.N
+    if (w_gate.K, w_up.K, w_up.N, w_down.K, w_down.N) != (H, H, I, I, H):
+        raise ValueError(f"weights do not chain: A has H={H}; gate {w_gate.K}x{w_gate.N}, "
+                         f"up {w_up.K}x{w_up.N}, down {w_down.K}x{w_down.N}")
+    if gamma is not None:
+        _need_gpu(gamma, "gamma", torch.float16)
+    if inter is None:
+        inter = torch.empty((M, I), dtype=torch.float16, device=A.device)
+    if out is None:
+        out = torch.empty((M, H), dtype=torch.float16, device=A.device)
+    _need_gpu(inter, "inter", torch.float16)
+    _need_gpu(out, "out", torch.float16)
+    if tuple(inter.shape) != (M, I) or tuple(out.shape) != (M, H):
+        raise ValueError("inter must be [M][I] and out [M][H]")
+    ws_n = mlp_workspace_bytes(M, H, I, w_gate.group)
+    ws = (workspace or _default_ws).get(ws_n, A.device)
+    st = _lib.lib().w4a16_mlp(_ptr(A), _ptr(residual), _ptr(residual_out), M, H, I,
+                              w_gate.group, w_gate.scale_dtype, int(w_gate.has_zp),
+                              _ptr(w_gate.data), _ptr(w_up.data), _ptr(w_down.data),
+                              _ptr(gamma), float(eps), _ptr(inter), _ptr(out), _ptr(ws), ws_n,
+                              _stream())
+    _lib.check(st, "w4a16_mlp")
     return out
 
 

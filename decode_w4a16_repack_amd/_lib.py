@@ -41,6 +41,7 @@ EXPORTS = [
     "w4a16_add_bias", "w4a16_relu", "w4a16_rmsnorm", "w4a16_probe_read",
     "w4a16_probe_copy", "w4a16_plan", "w4a16_gemm_split", "w4a16_gemm_gate_up_split",
     "w4a16_gemm_skip_rmsnorm", "w4a16_gemm_gate_up_skip_rmsnorm",
+    "w4a16_mlp_workspace_bytes", "w4a16_mlp",
 ]
 
 
@@ -89,6 +90,8 @@ def lib() -> ctypes.CDLL:
         "w4a16_gemm_gate_up_split": (I, [P, I, I, I, I, I, I, P, P, P, F, P, P, Z, I, P]),
         "w4a16_gemm_skip_rmsnorm": (I, [P, P, P, I, I, I, I, I, I, P, I, P, P, F, P, P, Z, P]),
         "w4a16_gemm_gate_up_skip_rmsnorm": (I, [P, P, P, I, I, I, I, I, I, P, P, P, F, P, P, Z, P]),
+        "w4a16_mlp_workspace_bytes": (Z, [I, I, I, I]),
+        "w4a16_mlp": (I, [P, P, P, I, I, I, I, I, I, P, P, P, P, F, P, P, P, Z, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)

@@ -42,10 +42,12 @@ int check_gemm(const void *A, int M, int K, int N, int group, int scale_dtype,
   return W4A16_OK;
 }
 
-int check_workspace(const Plan &pl, const void *ws, size_t ws_bytes) {
-  if (pl.ws_total == 0) return W4A16_OK;
+// A call with the RMSNorm prologue needs the plan's staging buffers too.
+int check_workspace(const Plan &pl, bool rms, const void *ws, size_t ws_bytes) {
+  const size_t need = rms ? pl.ws_total_rms : pl.ws_total;
+  if (need == 0) return W4A16_OK;
   if (ws == nullptr) return W4A16_ERR_WORKSPACE;
-  if (ws_bytes < pl.ws_total) return W4A16_ERR_WORKSPACE;
+  if (ws_bytes < need) return W4A16_ERR_WORKSPACE;
   if (!aligned16(ws)) return W4A16_ERR_ALIGN;
   return W4A16_OK;
 }
@@ -82,6 +84,9 @@ void fill_workspace(GemmArgs &a, const Plan &pl, void *ws) {
   a.ws_part = pl.ws_total ? reinterpret_cast<float *>(b + pl.ws_part_off) : nullptr;
   a.ws_rms = pl.ws_total ? reinterpret_cast<float *>(b + pl.ws_rms_off) : nullptr;
   a.ws_cnt = pl.ws_total ? reinterpret_cast<uint32_t *>(b + pl.ws_cnt_off) : nullptr;
+  const bool staged = b != nullptr && pl.kind != kKindStream;
+  a.ws_x = staged ? reinterpret_cast<f16 *>(b + pl.ws_x_off) : nullptr;
+  a.ws_ss = staged ? reinterpret_cast<float *>(b + pl.ws_ss_off) : nullptr;
 }
 
 int launched(hipError_t e) { return e == hipSuccess ? W4A16_OK : W4A16_ERR_LAUNCH; }
@@ -118,8 +123,8 @@ size_t w4a16_workspace_bytes(int M, int K, int N, int group, int gate_up) {
   if (M < 1 || M > kMaxDim || check_kn(K, N, group) != W4A16_OK) return 0;
   // the plan (and so the workspace) may differ with the scale width: take
   // the larger of fp16 and fp32 scales
-  const size_t a = make_plan(M, K, N, group, 2, gate_up != 0).ws_total;
-  const size_t b = make_plan(M, K, N, group, 4, gate_up != 0).ws_total;
+  const size_t a = make_plan(M, K, N, group, 2, gate_up != 0).ws_total_rms;
+  const size_t b = make_plan(M, K, N, group, 4, gate_up != 0).ws_total_rms;
   return a > b ? a : b;
 }
 
@@ -134,10 +139,25 @@ int check_residual(const void *resid, const void *resid_out, const void *gamma) 
   return W4A16_OK;
 }
 
-int gemm_impl(const void *A, const void *resid, void *resid_out, int M, int K, int N,
+// A validated launch: arguments, plan and kernel selection of one call.
+struct Call {
+  GemmArgs a{};
+  Plan pl{};
+  int group = 0;
+  bool sf32 = false;
+  bool gate_up = false;
+};
+
+int run(const Call &c, w4a16_stream stream) {
+  return launched(launch_gemm(c.a, c.pl, c.group, c.sf32, c.gate_up,
+                              static_cast<hipStream_t>(stream)));
+}
+
+// Validates a plain GEMM call and fills `c`; touches no device.
+int prep_gemm(const void *A, const void *resid, void *resid_out, int M, int K, int N,
               int group, int scale_dtype, int has_zp, const void *packed, int epilogue,
               const void *bias, const void *rms_gamma, float rms_eps, void *out,
-              void *workspace, size_t workspace_bytes, int split, w4a16_stream stream) {
+              void *workspace, size_t workspace_bytes, int split, Call &c) {
   const void *pk[1] = {packed};
   int st = check_gemm(A, M, K, N, group, scale_dtype, pk, 1, out);
   if (st != W4A16_OK) return st;
@@ -150,14 +170,14 @@ int gemm_impl(const void *A, const void *resid, void *resid_out, int M, int K, i
   if ((bias != nullptr && !aligned16(bias)) ||
       (rms_gamma != nullptr && !aligned16(rms_gamma)))
     return W4A16_ERR_ALIGN;
-  Plan pl;
-  st = plan_for(M, K, N, group, scale_dtype, false, split, pl);
+  st = plan_for(M, K, N, group, scale_dtype, false, split, c.pl);
   if (st != W4A16_OK) return st;
-  st = check_workspace(pl, workspace, workspace_bytes);
+  st = check_workspace(c.pl, rms_gamma != nullptr, workspace, workspace_bytes);
   if (st != W4A16_OK) return st;
 
   const int sb = scale_bytes_of(scale_dtype);
-  GemmArgs a{};
+  GemmArgs &a = c.a;
+  a = GemmArgs{};
   a.A = static_cast<const f16 *>(A);
   a.M = M;
   a.K = K;
@@ -171,29 +191,32 @@ int gemm_impl(const void *A, const void *resid, void *resid_out, int M, int K, i
   a.resid_out = static_cast<f16 *>(resid_out);
   a.eps = rms_eps;
   a.out = static_cast<f16 *>(out);
-  fill_workspace(a, pl, workspace);
-  return launched(launch_gemm(a, pl, group, sb == 4, false,
-                              static_cast<hipStream_t>(stream)));
+  fill_workspace(a, c.pl, workspace);
+  c.group = group;
+  c.sf32 = sb == 4;
+  c.gate_up = false;
+  return W4A16_OK;
 }
 
-int gate_up_impl(const void *A, const void *resid, void *resid_out, int M, int K, int N,
+// Validates a gate_up call and fills `c`; touches no device.
+int prep_gate_up(const void *A, const void *resid, void *resid_out, int M, int K, int N,
                  int group, int scale_dtype, int has_zp, const void *packed_gate,
                  const void *packed_up, const void *rms_gamma, float rms_eps, void *out,
-                 void *workspace, size_t workspace_bytes, int split, w4a16_stream stream) {
+                 void *workspace, size_t workspace_bytes, int split, Call &c) {
   const void *pk[2] = {packed_gate, packed_up};
   int st = check_gemm(A, M, K, N, group, scale_dtype, pk, 2, out);
   if (st != W4A16_OK) return st;
   st = check_residual(resid, resid_out, rms_gamma);
   if (st != W4A16_OK) return st;
   if (rms_gamma != nullptr && !aligned16(rms_gamma)) return W4A16_ERR_ALIGN;
-  Plan pl;
-  st = plan_for(M, K, N, group, scale_dtype, true, split, pl);
+  st = plan_for(M, K, N, group, scale_dtype, true, split, c.pl);
   if (st != W4A16_OK) return st;
-  st = check_workspace(pl, workspace, workspace_bytes);
+  st = check_workspace(c.pl, rms_gamma != nullptr, workspace, workspace_bytes);
   if (st != W4A16_OK) return st;
 
   const int sb = scale_bytes_of(scale_dtype);
-  GemmArgs a{};
+  GemmArgs &a = c.a;
+  a = GemmArgs{};
   a.A = static_cast<const f16 *>(A);
   a.M = M;
   a.K = K;
@@ -207,9 +230,33 @@ int gate_up_impl(const void *A, const void *resid, void *resid_out, int M, int K
   a.resid_out = static_cast<f16 *>(resid_out);
   a.eps = rms_eps;
   a.out = static_cast<f16 *>(out);
-  fill_workspace(a, pl, workspace);
-  return launched(launch_gemm(a, pl, group, sb == 4, true,
-                              static_cast<hipStream_t>(stream)));
+  fill_workspace(a, c.pl, workspace);
+  c.group = group;
+  c.sf32 = sb == 4;
+  c.gate_up = true;
+  return W4A16_OK;
+}
+
+int gemm_impl(const void *A, const void *resid, void *resid_out, int M, int K, int N,
+              int group, int scale_dtype, int has_zp, const void *packed, int epilogue,
+              const void *bias, const void *rms_gamma, float rms_eps, void *out,
+              void *workspace, size_t workspace_bytes, int split, w4a16_stream stream) {
+  Call c;
+  const int st = prep_gemm(A, resid, resid_out, M, K, N, group, scale_dtype, has_zp, packed,
+                           epilogue, bias, rms_gamma, rms_eps, out, workspace,
+                           workspace_bytes, split, c);
+  return st != W4A16_OK ? st : run(c, stream);
+}
+
+int gate_up_impl(const void *A, const void *resid, void *resid_out, int M, int K, int N,
+                 int group, int scale_dtype, int has_zp, const void *packed_gate,
+                 const void *packed_up, const void *rms_gamma, float rms_eps, void *out,
+                 void *workspace, size_t workspace_bytes, int split, w4a16_stream stream) {
+  Call c;
+  const int st = prep_gate_up(A, resid, resid_out, M, K, N, group, scale_dtype, has_zp,
+                              packed_gate, packed_up, rms_gamma, rms_eps, out, workspace,
+                              workspace_bytes, split, c);
+  return st != W4A16_OK ? st : run(c, stream);
 }
 
 }  // namespace
@@ -273,6 +320,31 @@ int w4a16_gemm_gate_up(const void *A, int M, int K, int N, int group,
                                   workspace_bytes, 0, stream);
 }
 
+size_t w4a16_mlp_workspace_bytes(int M, int H, int I, int group) {
+  const size_t a = w4a16_workspace_bytes(M, H, I, group, 1);
+  const size_t b = w4a16_workspace_bytes(M, I, H, group, 0);
+  return a > b ? a : b;
+}
+
+int w4a16_mlp(const void *A, const void *residual, void *residual_out, int M, int H, int I,
+              int group, int scale_dtype, int has_zp, const void *packed_gate,
+              const void *packed_up, const void *packed_down, const void *rms_gamma,
+              float rms_eps, void *inter, void *out, void *workspace,
+              size_t workspace_bytes, w4a16_stream stream) {
+  // both projections are validated before either is enqueued
+  Call up, down;
+  int st = prep_gate_up(A, residual, residual_out, M, H, I, group, scale_dtype, has_zp,
+                        packed_gate, packed_up, rms_gamma, rms_eps, inter, workspace,
+                        workspace_bytes, 0, up);
+  if (st != W4A16_OK) return st;
+  st = prep_gemm(inter, nullptr, nullptr, M, I, H, group, scale_dtype, has_zp, packed_down,
+                 W4A16_EPI_NONE, nullptr, nullptr, 0.0f, out, workspace, workspace_bytes, 0,
+                 down);
+  if (st != W4A16_OK) return st;
+  st = run(up, stream);
+  return st != W4A16_OK ? st : run(down, stream);
+}
+
 int w4a16_plan(int M, int K, int N, int group, int scale_dtype, int gate_up, int split,
                w4a16_plan_info *info) {
   if (info == nullptr) return W4A16_ERR_NULL;
@@ -293,7 +365,7 @@ int w4a16_plan(int M, int K, int N, int group, int scale_dtype, int gate_up, int
   info->grid[2] = pl.gz;
   info->block = pl.block;
   info->lds_bytes = (int)pl.lds_bytes;
-  info->workspace_bytes = pl.ws_total;
+  info->workspace_bytes = pl.ws_total_rms;
   return W4A16_OK;
 }
 

@@ -74,7 +74,13 @@ struct GemmArgs {
   const f16 *resid;  // with gamma: residual added before the norm (null: none)
   f16 *resid_out;    // with resid: the sum A + resid written here (null: not written)
   float eps;
+  // panel / tile kernels: fp32 [M] sums of squares of the staged rows (the
+  // RMSNorm prologue, done by the staging pass); the epilogue multiplies row
+  // m by 1 / sqrt(row_ss[m] / K + eps).  Null: no row scale.
+  const float *row_ss;
   f16 *out;
+  f16 *ws_x;          // staging: fp16 [M][K] x * gamma (panel / tile prologue)
+  float *ws_ss;       // staging: fp32 [M] row sums of squares
   float *ws_part;     // [S][2 if gate_up][M][N] fp32 partial sums
   float *ws_rms;      // [blocks][S][64] fp32 partial sums of squares
   uint32_t *ws_cnt;   // [blocks] arrival counters, zero between calls
@@ -99,6 +105,10 @@ struct Plan {
   int alds;  // stream kernel: activation rows staged through LDS
   size_t lds_bytes;
   size_t ws_part_off, ws_rms_off, ws_cnt_off, ws_total;
+  // panel / tile plans: the RMSNorm staging buffers follow the split-K
+  // region; a call with the prologue needs ws_total_rms bytes, one without
+  // it ws_total (stream plans: the two are equal)
+  size_t ws_x_off, ws_ss_off, ws_total_rms;
 };
 
 // force_kind: -1 automatic, else a PlanKind; force_cfg < 0 /
@@ -123,6 +133,11 @@ hipError_t launch_tile(const GemmArgs &a, const Plan &p, int group, bool scale_f
 
 hipError_t launch_gemm(const GemmArgs &a, const Plan &p, int group,
                        bool scale_f32, bool gate_up, hipStream_t stream);
+
+// stage.hip: S = A (+ resid, written to resid_out when not null), x_out =
+// fp16(S * gamma), ss_out[m] = sum_k S[m][k]^2 in fp32; one workgroup per row.
+hipError_t launch_rms_stage(const f16 *A, const f16 *resid, f16 *resid_out, const f16 *gamma,
+                            int M, int K, f16 *x_out, float *ss_out, hipStream_t stream);
 
 hipError_t launch_repack(const uint8_t *qweight, const void *scales,
                          const uint8_t *zeros, int K, int N, int group,

@@ -168,28 +168,27 @@ bool plan_panel(Plan &p, int M, int K, int N, int group, int scale_bytes, bool g
   p.split = (KC + p.cps - 1) / p.cps;
   p.gy = p.split;
   const int gpw = c.kpw * (kTileK / group);
+  // per wavefront: its slice's scales and zero-points per weight stream
   const size_t meta = NW * ((size_t)c.cpw * gpw * 16 * scale_bytes + align16((size_t)c.cpw * gpw * 8));
   const size_t red = (size_t)c.cpw * c.mt * 1024;  // one weight stream's partial sums
   const size_t region = align16(meta > red ? meta : red);
   p.lds_s = (int)region;
   p.lds_r = (int)(c.nwk * region);
   // (+ one int: the workgroup's "last to arrive" flag of the split path)
-  p.lds_bytes = (size_t)p.lds_r + (size_t)c.nwk * 16 * c.mt * 4 + 16;
+  p.lds_bytes = (size_t)p.lds_r + 16;
   if (p.lds_bytes > 160 * 1024) return false;
   p.rows_pow2 = 0;
   p.alds = 0;
   // workspace: arrival counters (one per output tile of a workgroup, in the
   // same fixed region as every other plan's, so that all plans leave the
-  // same words at zero), row sums of squares [tile][S][16 * MT], partial
-  // sums [S][NW][M][N]
+  // same words at zero), partial sums [S][NW][M][N]
   size_t off = 0;
   if (p.split > 1) {
     const size_t tiles = (size_t)p.gx * p.gz;
     if (tiles > (size_t)kMaxSplitBlocks) return false;
     p.ws_cnt_off = 0;
     off = align256((size_t)kMaxSplitBlocks * 4);
-    p.ws_rms_off = off;
-    off = align256(off + tiles * p.split * 16 * c.mt * 4);
+    p.ws_rms_off = 0;
     p.ws_part_off = off;
     off = align256(off + (size_t)p.split * NW * M * N * 4);
   }
@@ -214,6 +213,21 @@ void plan_tile(Plan &p, int M, int K, int N, int group, int scale_bytes, bool ga
   p.ws_total = 0;
 }
 
+// Panel and tile plans: the RMSNorm staging buffers after the plan's own
+// workspace (fp16 [M][K] staged rows, fp32 [M] sums of squares), and never
+// inside the arrival counters at its start, which every plan shares and
+// leaves at zero (a plan without split-K has no workspace of its own).
+void add_staging(Plan &p, int M, int K) {
+  if (p.kind == kKindStream) {
+    p.ws_total_rms = p.ws_total;
+    return;
+  }
+  const size_t counters = align256((size_t)kMaxSplitBlocks * 4);
+  p.ws_x_off = align256(p.ws_total > counters ? p.ws_total : counters);
+  p.ws_ss_off = align256(p.ws_x_off + (size_t)M * K * 2);
+  p.ws_total_rms = align256(p.ws_ss_off + (size_t)M * 4);
+}
+
 }  // namespace
 
 Plan make_plan(int M, int K, int N, int group, int scale_bytes, bool gate_up, int force_kind,
@@ -221,20 +235,39 @@ Plan make_plan(int M, int K, int N, int group, int scale_bytes, bool gate_up, in
   Plan p{};
   if ((force_kind < 0 || force_kind == kKindStream) &&
       plan_stream(p, M, K, N, group, scale_bytes, gate_up,
-                  force_kind == kKindStream ? force_cfg : -1, force_split))
+                  force_kind == kKindStream ? force_cfg : -1, force_split)) {
+    add_staging(p, M, K);
     return p;
+  }
   p = Plan{};
   if ((force_kind < 0 || force_kind == kKindPanel) &&
-      plan_panel(p, M, K, N, group, scale_bytes, gate_up, force_split))
+      plan_panel(p, M, K, N, group, scale_bytes, gate_up, force_split)) {
+    add_staging(p, M, K);
     return p;
+  }
   p = Plan{};
   plan_tile(p, M, K, N, group, scale_bytes, gate_up);
+  add_staging(p, M, K);
   return p;
 }
 
 hipError_t launch_gemm(const GemmArgs &a, const Plan &pl, int group, bool scale_f32,
                        bool gate_up, hipStream_t stream) {
   if (pl.kind == kKindStream) return launch_stream(a, pl, group, scale_f32, gate_up, stream);
+  if (a.gamma != nullptr) {
+    // RMSNorm prologue of the panel / tile kernels: stage the rows, then the
+    // plain product on them with the row scale in the epilogue
+    const hipError_t e = launch_rms_stage(a.A, a.resid, a.resid_out, a.gamma, a.M, a.K,
+                                          a.ws_x, a.ws_ss, stream);
+    if (e != hipSuccess) return e;
+    GemmArgs b = a;
+    b.A = a.ws_x;
+    b.gamma = nullptr;
+    b.resid = nullptr;
+    b.resid_out = nullptr;
+    b.row_ss = a.ws_ss;
+    return launch_gemm(b, pl, group, scale_f32, gate_up, stream);
+  }
   if (pl.kind == kKindPanel) return launch_panel(a, pl, group, scale_f32, gate_up, stream);
   return launch_tile(a, pl, group, scale_f32, gate_up, stream);
 }

@@ -27,8 +27,8 @@
 //    region per wavefront; no barrier sits in the loop, only the one before
 //    the slice reduction;
 //  * the (row tile, column tile) output blocks are shared out over the
-//    wavefronts for the final sum: slice sum in slice order, RMSNorm factor,
-//    epilogue, one fp16 write.  Wide reductions (gate_up) go in one pass per
+//    wavefronts for the final sum: slice sum in slice order, the RMSNorm
+//    row scale (rows staged by stage.hip), epilogue, one fp16 write.  Wide reductions (gate_up) go in one pass per
 //    weight stream so the LDS need not hold both at once.
 #include "device.h"
 
@@ -36,8 +36,7 @@ namespace w4a16 {
 
 namespace {
 
-template <int MT, int CPW, int KPW, int NWK, int PD, bool ADB, int G, bool SF32, bool GU,
-          bool RMS>
+template <int MT, int CPW, int KPW, int NWK, int PD, bool ADB, int G, bool SF32, bool GU>
 __global__ void __launch_bounds__(64 * NWK)
 panel_kernel(const GemmArgs p) {
   constexpr int NW = GU ? 2 : 1;
@@ -54,10 +53,11 @@ panel_kernel(const GemmArgs p) {
   constexpr int NPAIR = MT * CPW;                   // output blocks of the workgroup
   constexpr int PPW = (NPAIR + NWK - 1) / NWK;      // output blocks finished per wavefront
   constexpr int NAB = ADB ? 2 : 1;                  // activation buffers
+  constexpr bool A1_EARLY = ADB && KPW > 1;  // second k tile's activations before the loop
   // loads issued after the metadata copies that may still be in flight when
-  // the copies are waited for: the first k tile's activations (and, with
-  // ADB, the second's) and the first PDE tiles of each stream
-  constexpr int AFTER_COPIES = MT * 4 * NAB + PDE * NW;
+  // the copies are waited for: the first k tile's activations (and the
+  // second's) and the first PDE tiles of each stream
+  constexpr int AFTER_COPIES = MT * 4 * (A1_EARLY ? 2 : 1) + PDE * NW;
   static_assert(PDE >= 1 && PDE <= NTILE, "prefetch depth");
 
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -77,9 +77,6 @@ panel_kernel(const GemmArgs p) {
   const int nkc = min(KC, kb + p.cps) - kb;
   const int my_kb = kb + wk * KPW;
   const int my_n = max(0, min(KPW, nkc - wk * KPW));  // valid k tiles of this slice
-  // the RMSNorm prologue is a separate instantiation: its registers would
-  // otherwise count against the plain kernel's loop
-  constexpr bool rms = RMS;
   const bool has_zp = p.has_zp != 0;
   const int kq = lane >> 4;
   const int c = lane & 15;
@@ -87,7 +84,6 @@ panel_kernel(const GemmArgs p) {
   uint8_t *region = smem + wk * p.lds_s;
   uint8_t *ms = region;                  // [NW] x MS_BYTES
   uint8_t *mz = region + NW * MS_BYTES;  // [NW] x MZ_PAD
-  float *lRms = reinterpret_cast<float *>(smem + p.lds_r);  // [NWK][16 * MT]
 
   // 1. this slice's scales and zero-points of the CPW column tiles, copied
   //    straight into the private region (reads clamped to the column tile's
@@ -140,66 +136,13 @@ panel_kernel(const GemmArgs p) {
     const int kc = kc_of(t);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const int row = min(16 * mt + c, mrows - 1);
-      const f16 *src = p.A + (size_t)(m0 + row) * p.K + kc * kTileK + 8 * kq;
+      const size_t off = (size_t)(m0 + min(16 * mt + c, mrows - 1)) * p.K + kc * kTileK + 8 * kq;
 #pragma unroll
-      for (int d = 0; d < 4; ++d) ab[mt][d] = *reinterpret_cast<const f16x8 *>(src + 32 * d);
+      for (int d = 0; d < 4; ++d) ab[mt][d] = *reinterpret_cast<const f16x8 *>(p.A + off + 32 * d);
     }
   };
 
-  // 3. RMSNorm prologue of one k tile, in registers: per-lane sums of
-  //    squares (row 16*mt + l%16, this lane's k slots; products of fp16
-  //    values are exact in fp32, summed in fp32 by v_dot2_f32_f16), and
-  //    x * gamma rounded once to fp16 (the packed fp16 multiply rounds the
-  //    exact product once, as an fp32 product rounded to fp16 would);
-  //    1/sqrt(mean + eps) is applied in the epilogue.  With a residual
-  //    (skip + RMSNorm) the fragment is first replaced by A + resid rounded
-  //    once to fp16, which the workgroups of column block 0 write out, each
-  //    (row, k) once.
-  float ss[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) ss[mt] = 0.f;
-  const bool write_res = p.resid != nullptr && p.resid_out != nullptr && blockIdx.x == 0;
-  auto prep_a = [&](int t, f16x8 (&ab)[MT][4]) __attribute__((always_inline)) {
-    const int kc = kc_of(t);
-    const bool valid = t < my_n;
-    const float on = valid ? 1.0f : 0.0f;
-    f16x8 gam[4];
-#pragma unroll
-    for (int d = 0; d < 4; ++d)
-      gam[d] = *reinterpret_cast<const f16x8 *>(p.gamma + kc * kTileK + 32 * d + 8 * kq);
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const int row = 16 * mt + c;
-      if (p.resid != nullptr) {
-        const f16 *rsrc = p.resid + (size_t)(m0 + min(row, mrows - 1)) * p.K + kc * kTileK + 8 * kq;
-        f16x8 rr[4];
-#pragma unroll
-        for (int d = 0; d < 4; ++d) rr[d] = *reinterpret_cast<const f16x8 *>(rsrc + 32 * d);
-#pragma unroll
-        for (int d = 0; d < 4; ++d) ab[mt][d] = ab[mt][d] + rr[d];
-        if (write_res && valid && row < mrows) {
-          f16 *dst = p.resid_out + (size_t)(m0 + row) * p.K + kc * kTileK + 8 * kq;
-#pragma unroll
-          for (int d = 0; d < 4; ++d) *reinterpret_cast<f16x8 *>(dst + 32 * d) = ab[mt][d];
-        }
-      }
-      float sq = 0.f;
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const f16x8 x = ab[mt][d];
-#pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          const f16x2 x2 = {x[2 * h], x[2 * h + 1]};
-          sq = __builtin_amdgcn_fdot2(x2, x2, sq, false);
-        }
-        ab[mt][d] = x * gam[d];
-      }
-      ss[mt] = __builtin_fmaf(on, sq, ss[mt]);
-    }
-  };
-
-  // 4. weight tiles: tile f = t * CPW + w (k tile position t, column tile
+  // 3. weight tiles: tile f = t * CPW + w (k tile position t, column tile
   //    w), issued PDE tiles before it is contracted; tiles past the slice or
   //    past N re-read a valid tile
   u32x4 wv[NW][NTILE];
@@ -217,14 +160,12 @@ panel_kernel(const GemmArgs p) {
   load_a(0, a[0]);
 #pragma unroll
   for (int f = 0; f < PDE; ++f) issue_tile(f);
-  if constexpr (ADB) {
-    if (KPW > 1) load_a(1, a[1 % NAB]);
-  }
-  // 5. this wavefront's metadata copies have landed (completion is in issue
+  if constexpr (A1_EARLY) load_a(1, a[1 % NAB]);
+  // 4. this wavefront's metadata copies have landed (completion is in issue
   //    order); no other wavefront reads its region before the reduction
   wait_vmcnt<(AFTER_COPIES < 63 ? AFTER_COPIES : 63)>();
 
-  // 6. contraction, k tile outer, column tile inner: each unpacked word of
+  // 5. contraction, k tile outer, column tile inner: each unpacked word of
   //    codes feeds MT MFMAs, each activation fragment CPW
   f32x4 acc[NW][CPW][MT];
 #pragma unroll
@@ -243,18 +184,14 @@ panel_kernel(const GemmArgs p) {
     // unpack or loads up into this one (the registers would run out)
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (w == 0) {
-      if constexpr (t > 0) {
-        if constexpr (ADB) {
-          if constexpr (t + 1 < KPW) load_a(t + 1, a[(t + 1) % NAB]);
-        } else {
-          // (no earlier: the single activation buffer is still being read
-          // by the previous k tile, and hoisting the loads above that would
-          // need a second buffer's registers)
-          __builtin_amdgcn_sched_barrier(0);
-          load_a(t, at);
-        }
+      if constexpr (!ADB && t > 0) {
+        // (no earlier: the single activation buffer is still being read
+        // by the previous k tile, and hoisting the loads above that would
+        // need a second buffer's registers)
+        __builtin_amdgcn_sched_barrier(0);
+        load_a(t, at);
       }
-      if constexpr (RMS) prep_a(t, at);
+      if constexpr (ADB && t > 0 && t + 1 < KPW) load_a(t + 1, a[(t + 1) % NAB]);
     }
     if constexpr (f + PDE < NTILE) issue_tile(f + PDE);
     const float on = t < my_n ? 1.0f : 0.0f;
@@ -318,19 +255,9 @@ panel_kernel(const GemmArgs p) {
     }
   });
 
-  // 7. row sums of squares of the slice (row 16*mt + l%16 is spread over
-  //    lanes l%16 + 16j), then the slice partial sums, one weight stream per
-  //    pass, through the private regions; wavefront wk finishes output blocks
-  //    wk, wk + NWK, ... (block = mt * CPW + w) in slice order
-  if (rms) {
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      float v = ss[mt];
-      v += __shfl_xor(v, 16);
-      v += __shfl_xor(v, 32);
-      if (lane < 16) lRms[wk * 16 * MT + 16 * mt + lane] = v;
-    }
-  }
+  // 6. the slice partial sums, one weight stream per pass, through the
+  //    private regions; wavefront wk finishes output blocks wk, wk + NWK, ...
+  //    (block = mt * CPW + w) in slice order
   f32x4 fin[NW][PPW];
   f32x4 *red = reinterpret_cast<f32x4 *>(region);
 #pragma unroll
@@ -351,20 +278,10 @@ panel_kernel(const GemmArgs p) {
       fin[i][j] = v;
     }
   }
-  // sums of squares of this lane's output rows 16*mt + 4*(l/16) + e
-  f32x4 rs[PPW];
-#pragma unroll
-  for (int j = 0; j < PPW; ++j) {
-    const int mt = min(wk + NWK * j, NPAIR - 1) / CPW;
-    rs[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (rms)
-      for (int w2 = 0; w2 < NWK; ++w2)
-        rs[j] += reinterpret_cast<const f32x4 *>(lRms + w2 * 16 * MT + 16 * mt)[kq];
-  }
 
-  // 8. k splits across workgroups (deep K, or a grid short of one
+  // 7. k splits across workgroups (deep K, or a grid short of one
   //    workgroup per compute unit): every workgroup stores its partial sums
-  //    (and row sums of squares); the last workgroup to arrive at this
+  //    and the last workgroup to arrive at this
   //    output tile (one counter per tile) sums them in split order.
   //    Agent-scope atomic accesses keep the exchange coherent across the
   //    XCDs' L2 caches without a device-wide fence; every wavefront waits
@@ -372,7 +289,6 @@ panel_kernel(const GemmArgs p) {
   //    count.
   if (S > 1) {
     const size_t tile_id = (size_t)blockIdx.z * gridDim.x + blockIdx.x;
-    float *wrms = p.ws_rms + tile_id * S * 16 * MT;  // [S][16 * MT rows]
 #pragma unroll
     for (int j = 0; j < PPW; ++j) {
       const int pr = wk + NWK * j;
@@ -387,11 +303,10 @@ panel_kernel(const GemmArgs p) {
           for (int i = 0; i < NW; ++i)
             store_agent(&p.ws_part[(((size_t)s * NW + i) * p.M + m0 + row) * p.N + ncol], fin[i][j][e]);
         }
-        if (rms && w == 0 && c == 0) store_agent(&wrms[s * 16 * MT + row], rs[j][e]);
       }
     }
     wait_stores();
-    int *flag = reinterpret_cast<int *>(lRms + NWK * 16 * MT);
+    int *flag = reinterpret_cast<int *>(smem + p.lds_r);
     __syncthreads();
     if (tid == 0) *flag = count_arrival(&p.ws_cnt[tile_id]) == (unsigned)(S - 1);
     __syncthreads();
@@ -415,18 +330,13 @@ panel_kernel(const GemmArgs p) {
             fin[i][j][e] = v;
           }
         }
-        if (rms) {
-          float v = 0.f;
-          for (int s2 = 0; s2 < S; ++s2)
-            v += (s2 == s) ? rs[j][e] : load_agent(&wrms[s2 * 16 * MT + row]);
-          rs[j][e] = v;
-        }
       }
     }
     if (tid == 0) reset_arrival(&p.ws_cnt[tile_id]);
   }
 
-  // 9. epilogue, one fp16 write per output
+  // 8. epilogue (row scale of the RMSNorm prologue, SwiGLU or bias / ReLU),
+  //    one fp16 write per output
 #pragma unroll
   for (int j = 0; j < PPW; ++j) {
     const int pr = wk + NWK * j;
@@ -439,7 +349,7 @@ panel_kernel(const GemmArgs p) {
       const int row = 16 * mt + 4 * kq + e;
       if (row < mrows) {
         float rsc = 1.0f;
-        if (rms) rsc = 1.0f / sqrtf(rs[j][e] / (float)p.K + p.eps);
+        if (p.row_ss != nullptr) rsc = 1.0f / sqrtf(p.row_ss[m0 + row] / (float)p.K + p.eps);
         float y;
         if constexpr (GU) {
           y = silu(fin[0][j][e] * rsc) * (fin[1][j][e] * rsc);
@@ -454,10 +364,9 @@ panel_kernel(const GemmArgs p) {
   }
 }
 
-template <int MT, int CPW, int KPW, int NWK, int PD, bool ADB, int G, bool SF32, bool GU,
-          bool RMS>
+template <int MT, int CPW, int KPW, int NWK, int PD, bool ADB, int G, bool SF32, bool GU>
 hipError_t launch_t(const GemmArgs &a, const Plan &pl, hipStream_t stream) {
-  auto kern = panel_kernel<MT, CPW, KPW, NWK, PD, ADB, G, SF32, GU, RMS>;
+  auto kern = panel_kernel<MT, CPW, KPW, NWK, PD, ADB, G, SF32, GU>;
   // Raise the kernel's dynamic-LDS limit above the default 64 KiB once; later
   // launches (also under stream capture) make no attribute call.
   static size_t lds_limit = 64 * 1024;
@@ -475,19 +384,13 @@ hipError_t launch_t(const GemmArgs &a, const Plan &pl, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int MT, int CPW, int KPW, int NWK, int PD, bool ADB, int G, bool SF32>
-hipError_t launch_r(const GemmArgs &a, const Plan &pl, bool gu, hipStream_t st) {
-  const bool rms = a.gamma != nullptr;
-  if (gu) return rms ? launch_t<MT, CPW, KPW, NWK, PD, ADB, G, SF32, true, true>(a, pl, st)
-                     : launch_t<MT, CPW, KPW, NWK, PD, ADB, G, SF32, true, false>(a, pl, st);
-  return rms ? launch_t<MT, CPW, KPW, NWK, PD, ADB, G, SF32, false, true>(a, pl, st)
-             : launch_t<MT, CPW, KPW, NWK, PD, ADB, G, SF32, false, false>(a, pl, st);
-}
-
 template <int MT, int CPW, int KPW, int NWK, int PD, bool ADB, int G>
 hipError_t launch_g(const GemmArgs &a, const Plan &pl, bool sf32, bool gu, hipStream_t st) {
-  return sf32 ? launch_r<MT, CPW, KPW, NWK, PD, ADB, G, true>(a, pl, gu, st)
-              : launch_r<MT, CPW, KPW, NWK, PD, ADB, G, false>(a, pl, gu, st);
+  if (gu)
+    return sf32 ? launch_t<MT, CPW, KPW, NWK, PD, ADB, G, true, true>(a, pl, st)
+                : launch_t<MT, CPW, KPW, NWK, PD, ADB, G, false, true>(a, pl, st);
+  return sf32 ? launch_t<MT, CPW, KPW, NWK, PD, ADB, G, true, false>(a, pl, st)
+              : launch_t<MT, CPW, KPW, NWK, PD, ADB, G, false, false>(a, pl, st);
 }
 
 template <int MT, int CPW, int KPW, int NWK, int PD, bool ADB>

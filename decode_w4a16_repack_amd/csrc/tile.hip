@@ -29,11 +29,10 @@
 //    the step loop unrolled by four);
 //  * the number of copies and loads per step is fixed (tail steps re-read
 //    the last tile), which keeps the one wait per step exact;
-//  * one barrier per step (two with the RMSNorm prologue, which normalizes
-//    the stage's activation tiles in place); after the last step, the
-//    slices' partial sums meet in LDS and wavefront (wc, ks) finishes row
-//    tiles ks, ks + 2 of its column quarter in slice order: RMSNorm factor,
-//    epilogue, one fp16 write.
+//  * one barrier per step; after the last step, the slices' partial sums
+//    meet in LDS and wavefront (wc, ks) finishes row tiles ks, ks + 2 of its
+//    column quarter in slice order: the RMSNorm row scale (rows staged by
+//    stage.hip), epilogue, one fp16 write.
 #include <type_traits>
 
 #include "device.h"
@@ -66,12 +65,10 @@ constexpr int tile_meta_block_bytes(int ct, int group, int sb, int nw) {
                (tile_mbs(ct, group, sb) * tile_step_zp_bytes(ct, group) + 15) / 16 * 16);
 }
 constexpr int tile_stage_bytes() { return kTileNKS * kTileABytes; }
-constexpr int tile_rms_bytes() { return kTileNKS * 64 * 4; }
 constexpr int tile_nbuf(int st, int mbs) { return (st - 1 + mbs - 1) / mbs + 1; }
 constexpr int tile_lds(int st, int ct, int group, int sb, int nw) {
   return st * tile_stage_bytes() +
-         kTileNWave * tile_nbuf(st, tile_mbs(ct, group, sb)) * tile_meta_block_bytes(ct, group, sb, nw) +
-         tile_rms_bytes();
+         kTileNWave * tile_nbuf(st, tile_mbs(ct, group, sb)) * tile_meta_block_bytes(ct, group, sb, nw);
 }
 constexpr int tile_stages(int ct, int group, int sb, int nw) {
   return tile_lds(4, ct, group, sb, nw) <= kLdsMax ? 4 : tile_lds(3, ct, group, sb, nw) <= kLdsMax ? 3 : 2;
@@ -96,7 +93,6 @@ tile_kernel(const GemmArgs p) {
   constexpr int MBLK = tile_meta_block_bytes(CT, G, SB, NW);
   constexpr int STAGE = tile_stage_bytes();
   constexpr int META_OFF = ST * STAGE;
-  constexpr int RMS_OFF = META_OFF + kTileNWave * NBUF * MBLK;
   constexpr int D = 3;  // steps the weight tiles are loaded ahead (ring of D + 1)
   static_assert(kTileNWave * NW * MT * CT * 1024 <= ST * STAGE, "reduction scratch");
   static_assert(D >= ST - 1, "weights at least as far ahead as the copies");
@@ -129,9 +125,7 @@ tile_kernel(const GemmArgs p) {
   const int mrows = min(64, p.M - m0);
   const int ctw = blockIdx.x * NWC * CT + wc * CT;  // first column tile of this wavefront
   const int nsteps = (KC + NKS - 1) / NKS;
-  const bool rms = p.gamma != nullptr;
   const bool has_zp = p.has_zp != 0;
-  float *lRms = reinterpret_cast<float *>(smem + RMS_OFF);  // [NKS][64 rows]
 
   auto ktile = [&](int j) __attribute__((always_inline)) { return j * NKS + ks; };
   auto abuf_of = [&](int st) __attribute__((always_inline)) {
@@ -219,59 +213,6 @@ tile_kernel(const GemmArgs p) {
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) acc[i][mt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // RMSNorm prologue, in place on the stage: wavefront w normalizes rows
-  // 16*(w/2) .. +15 of slice w%2's activation tile; lane l takes chunks
-  // l + 64i (i = 0..3), i.e. row 16*(w/2) + 4i + l/16, and keeps that row's
-  // running sum of squares in ssq[i].  With a residual (skip + RMSNorm) the
-  // chunk is first replaced by A + resid rounded once to fp16, which the
-  // workgroups of column block 0 also write out.  The gamma and residual
-  // chunks of a step are loaded one step ahead, into registers.
-  float ssq[4] = {0.f, 0.f, 0.f, 0.f};
-  const bool has_res = p.resid != nullptr;
-  const bool write_res = has_res && p.resid_out != nullptr && blockIdx.x == 0;
-  const int rsl = wave & 1, rh = wave >> 1;
-  f16x8 rgam[4], rres[4];
-  auto rms_chunk_k = [&](int i) __attribute__((always_inline)) {
-    const int e = lane + 64 * i, r = 16 * rh + (e >> 4), pos = e & 15;
-    return 8 * (pos ^ (r & 15));  // k offset of the chunk within its tile
-  };
-  auto rms_row = [&](int i) __attribute__((always_inline)) { return 16 * rh + 4 * i + (lane >> 4); };
-  auto rms_load = [&](int j) __attribute__((always_inline)) {
-    const size_t k0 = (size_t)min(j * NKS + rsl, KC - 1) * kTileK;  // slice rsl's k tile
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      rgam[i] = *reinterpret_cast<const f16x8 *>(p.gamma + k0 + rms_chunk_k(i));
-      if (has_res)
-        rres[i] = *reinterpret_cast<const f16x8 *>(
-            p.resid + (size_t)(m0 + min(rms_row(i), mrows - 1)) * p.K + k0 + rms_chunk_k(i));
-    }
-  };
-  auto rms_pass = [&](int j, int st) __attribute__((always_inline)) {
-    uint8_t *ab = smem + st * STAGE + rsl * kTileABytes;
-    // a step past K holds a re-read of the last k tile: it adds no squares
-    // and writes nothing
-    const bool valid = j * NKS + rsl < KC;
-    const float on = valid ? 1.0f : 0.0f;
-    const size_t k0 = (size_t)(j * NKS + rsl) * kTileK;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = lane + 64 * i;
-      const int r = 16 * rh + (e >> 4), pos = e & 15;
-      f16x8 *px = reinterpret_cast<f16x8 *>(ab + (r * 16 + pos) * 16);
-      f16x8 x = *px;
-      if (has_res) {
-        x = x + rres[i];
-        if (write_res && valid && r < mrows)
-          *reinterpret_cast<f16x8 *>(p.resid_out + (size_t)(m0 + r) * p.K + k0 + rms_chunk_k(i)) = x;
-      }
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const float xf = (float)x[q];
-        ssq[i] = __builtin_fmaf(xf * on, xf, ssq[i]);
-      }
-      *px = x * rgam[i];
-    }
-  };
 
   const int zshift = 4 * (c & 1);
   auto compute = [&](int j, int st, const u32x4 (&wreg)[NW][CT]) __attribute__((always_inline)) {
@@ -359,7 +300,6 @@ tile_kernel(const GemmArgs p) {
   // copies of step j + ST - 1 into that stage and the weights of step j + D,
   // and computes.
   u32x4 wring[D + 1][NW][CT];
-  if (rms) rms_load(0);
 #pragma unroll
   for (int u = 0; u < ST - 1; ++u) issue(u, u, u % MBS == 0);
 #pragma unroll
@@ -381,11 +321,6 @@ tile_kernel(const GemmArgs p) {
     lds_only_barrier();   // everyone's have, and step j - 1's reads are done
     issue(j + ST - 1, st == 0 ? ST - 1 : st - 1, (u + ST - 1) % MBS == 0);
     load_w(j + D, wring[(u + D) % (D + 1)]);
-    if (rms) {
-      rms_pass(j, st);
-      rms_load(j + 1);
-      lds_only_barrier();
-    }
     compute(j, st, wring[u]);
     st = st == ST - 1 ? 0 : st + 1;
   };
@@ -408,29 +343,12 @@ tile_kernel(const GemmArgs p) {
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct)
         red[((wave * NW + i) * MT + mt) * CT * 64 + ct * 64 + lane] = acc[i][mt][ct];
-  if (rms) {
-    // ssq[i] of lane l is row 16*(w/2) + 4i + l/16 of slice w%2: sum the 16
-    // lanes of each row
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float v = ssq[i];
-      v += __shfl_xor(v, 1);
-      v += __shfl_xor(v, 2);
-      v += __shfl_xor(v, 4);
-      v += __shfl_xor(v, 8);
-      if ((lane & 15) == 0) lRms[(wave & 1) * 64 + 16 * (wave >> 1) + 4 * i + (lane >> 4)] = v;
-    }
-  }
   __syncthreads();
 
   // wavefront (wc, ks) finishes row tiles ks, ks + NKS, ... of column quarter wc
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     if (mt % NKS != ks) continue;
-    f32x4 rs = {0.f, 0.f, 0.f, 0.f};
-    if (rms)
-      for (int s2 = 0; s2 < NKS; ++s2)
-        rs += reinterpret_cast<const f32x4 *>(lRms + s2 * 64 + 16 * mt)[kq];
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
       if (ctw + ct >= NTL) continue;
@@ -448,7 +366,7 @@ tile_kernel(const GemmArgs p) {
         const int row = 16 * mt + 4 * kq + e;
         if (row < mrows) {
           float rsc = 1.0f;
-          if (rms) rsc = 1.0f / sqrtf(rs[e] / (float)p.K + p.eps);
+          if (p.row_ss != nullptr) rsc = 1.0f / sqrtf(p.row_ss[m0 + row] / (float)p.K + p.eps);
           float y;
           if constexpr (GU) {
             y = silu(fin[0][e] * rsc) * (fin[1][e] * rsc);

@@ -107,11 +107,18 @@ int w4a16_repack(const uint8_t *qweight, const void *scales,
 /*
  * Workspace bytes w4a16_gemm (gate_up = 0) or w4a16_gemm_gate_up
  * (gate_up = 1) needs for this shape: fp32 split-K partial sums and
- * arrival counters.  0 when the shape runs without split-K.  The workspace
- * must be zero-filled once after allocation; the counters occupy its first
- * 4096 bytes for every shape and every call leaves them at zero again, so
- * one workspace (sized for the largest shape) serves calls of any shape.
- * Calls that share a workspace must not run concurrently.
+ * arrival counters, and for M > 16 the RMSNorm staging rows (fp16 [M][K]
+ * x * gamma activations and fp32 [M] sums of squares, written by a staging
+ * pass before the product, as the "fused RMS-norm" update on the onnx-genai
+ * pull request stages the normalized activation).  Only calls with the
+ * RMSNorm prologue need the staging part: a call without it on a shape
+ * without split-K (w4a16_plan reports split 1) may pass a NULL workspace.
+ * 0 when M <= 16 and the shape runs without split-K.  The workspace must be
+ * zero-filled once after allocation; the counters occupy its first 4096
+ * bytes for every shape (the staging rows never do) and every call leaves
+ * them at zero again, so one workspace (sized for the largest shape) serves
+ * calls of any shape.  Calls that share a workspace must not run
+ * concurrently.
  */
 size_t w4a16_workspace_bytes(int M, int K, int N, int group, int gate_up);
 
@@ -166,7 +173,9 @@ typedef struct {
   int grid[3];            /* launch grid */
   int block;              /* threads per workgroup */
   int lds_bytes;          /* dynamic LDS per workgroup */
-  size_t workspace_bytes; /* workspace the call needs (see w4a16_workspace_bytes) */
+  size_t workspace_bytes; /* workspace a call with the RMSNorm prologue needs
+                             (see w4a16_workspace_bytes); without it, the
+                             split-K part alone */
 } w4a16_plan_info;
 
 /* Host-only: fill *info with the plan a call of this shape launches.
@@ -218,6 +227,36 @@ int w4a16_gemm_gate_up_skip_rmsnorm(const void *A, const void *residual,
                                     void *out, void *workspace,
                                     size_t workspace_bytes,
                                     w4a16_stream stream);
+
+/*
+ * MLP block: the paired gate/up projection followed by the down projection
+ * of its output ("gate_up SwiGLU MLP fusion" update on the onnx-genai pull
+ * request: the MLP carries most of the decode cost; its down projection is
+ * the deep-k decode shape 13696 x 4096 of the "Small-M split-K retune"
+ * update).
+ *   inter = fp16( silu(X.Wg) * (X.Wu) )      fp16 [M][I]
+ *   out   = fp16( inter . Wd )               fp16 [M][H]
+ * with X = A, RMSNorm(A) (rms_gamma given) or RMSNorm(A + residual)
+ * (residual given, as in w4a16_gemm_gate_up_skip_rmsnorm; residual_out
+ * receives the sum when not NULL).  A: fp16 [M][H].  packed_gate and
+ * packed_up: repacked with K = H, N = I; packed_down: repacked with K = I,
+ * N = H; all three with the same group, scale_dtype and has_zp.  So I must
+ * be a multiple of 128 and H a multiple of 128.  inter: caller-owned
+ * device buffer of M*I fp16 that receives the intermediate (it is also the
+ * down projection's input; it must not overlap A, residual, residual_out,
+ * out or the workspace).  The two projections are enqueued in that order
+ * on `stream` and share the workspace, which must hold
+ * w4a16_mlp_workspace_bytes(M, H, I, group) bytes (zero-filled once after
+ * allocation, as for w4a16_gemm).  Both calls are validated before either
+ * is enqueued: on error nothing runs.
+ */
+size_t w4a16_mlp_workspace_bytes(int M, int H, int I, int group);
+int w4a16_mlp(const void *A, const void *residual, void *residual_out, int M,
+              int H, int I, int group, int scale_dtype, int has_zp,
+              const void *packed_gate, const void *packed_up,
+              const void *packed_down, const void *rms_gamma, float rms_eps,
+              void *inter, void *out, void *workspace, size_t workspace_bytes,
+              w4a16_stream stream);
 
 /* Static, human-readable text for a w4a16_status value. */
 const char *w4a16_status_string(int status);

@@ -125,10 +125,25 @@ def test_aux_validation(L):
 
 
 def test_workspace_only_for_narrow_grids(L):
-    # wide N fills the chip without k splits across workgroups: no workspace
-    for M in (1, 2, 16, 32, 64, 128):
+    # wide N fills the chip without k splits across workgroups.  M <= 16 (the
+    # streaming kernel, RMSNorm prologue in registers): no workspace.  Above
+    # 16 the workspace holds only the RMSNorm staging (fp16 [M][K] rows, fp32
+    # [M] sums of squares, each 256-byte aligned), which only calls with the
+    # prologue need.  It starts after the 4096 bytes of split-K arrival
+    # counters that every plan shares (and leaves at zero): staged rows
+    # written there would corrupt the next split-K call.
+    a256 = lambda v: (v + 255) // 256 * 256
+    for M in (1, 2, 16):
         assert L.w4a16_workspace_bytes(M, 5120, 13824, 128, 0) == 0
         assert L.w4a16_workspace_bytes(M, 5120, 13824, 128, 1) == 0
+    for M in (17, 32, 64, 128):
+        stage = 4096 + a256(M * 5120 * 2) + a256(M * 4)
+        assert L.w4a16_workspace_bytes(M, 5120, 13824, 128, 0) == stage
+        assert L.w4a16_workspace_bytes(M, 5120, 13824, 128, 1) == stage
+        # a call with the prologue checks for the staging before any launch
+        assert gemm(L, M=M, K=5120, N=13824, group=128, gamma=FAKE) == _lib.ERR_WORKSPACE
+        assert gemm(L, M=M, K=5120, N=13824, group=128, gamma=FAKE, ws=FAKE,
+                    ws_n=stage - 1) == _lib.ERR_WORKSPACE
     assert L.w4a16_workspace_bytes(0, 5120, 13824, 128, 0) == 0
     w1 = L.w4a16_workspace_bytes(1, 5120, 256, 128, 0)
     w1g = L.w4a16_workspace_bytes(1, 5120, 256, 128, 1)
@@ -164,7 +179,10 @@ def test_plan_query_matches_workspace_and_kernel_choice(L):
         assert info.grid[1] == info.split
         ws = max(plan(L, M, K, N, sdt=s, gu=gu)[1].workspace_bytes for s in (0, 1))
         assert ws == L.w4a16_workspace_bytes(M, K, N, 128, gu)
-        assert (info.workspace_bytes > 0) == (info.split > 1)
+        # split-K exchange, plus the RMSNorm staging rows above M = 16
+        stage = 0 if M <= 16 else 4096 + (M * K * 2 + 255) // 256 * 256 + (M * 4 + 255) // 256 * 256
+        assert (info.workspace_bytes > stage) == (info.split > 1)
+        assert info.workspace_bytes >= stage
 
 
 def test_plan_deep_k_splits_and_forced_splits(L):
@@ -237,3 +255,35 @@ def test_skip_rmsnorm_validation(L):
     assert L.w4a16_gemm_gate_up_skip_rmsnorm(FAKE, FAKE, None, 8, 1000, 256, 128, 0, 1, FAKE,
                                              FAKE, FAKE, 1e-6, FAKE, FAKE, 1 << 30,
                                              None) == _lib.ERR_SHAPE
+
+
+def test_mlp_validation_before_any_launch(L):
+    """w4a16_mlp checks both projections on the host before it enqueues
+    either: a bad down projection (or workspace) fails with nothing run."""
+    FAKE = 1 << 20
+    M, H, I, g = 8, 1024, 2048, 128
+    need = L.w4a16_mlp_workspace_bytes(M, H, I, g)
+    assert need == max(L.w4a16_workspace_bytes(M, H, I, g, 1),
+                       L.w4a16_workspace_bytes(M, I, H, g, 0))
+    assert L.w4a16_mlp_workspace_bytes(M, H, I + 1, g) == 0
+
+    def mlp(A=FAKE, res=None, res_out=None, M=M, H=H, I=I, g=g, gate=FAKE, up=FAKE,
+            down=FAKE, gamma=None, inter=FAKE, out=FAKE, ws=FAKE, ws_n=1 << 30):
+        return L.w4a16_mlp(A, res, res_out, M, H, I, g, 0, 1, gate, up, down, gamma, 1e-6,
+                           inter, out, ws, ws_n, None)
+    assert mlp(inter=None) == _lib.ERR_NULL
+    assert mlp(down=None) == _lib.ERR_NULL
+    assert mlp(I=2048 + 64) == _lib.ERR_SHAPE        # down projection's K = I
+    assert mlp(H=1024 + 16) == _lib.ERR_SHAPE        # gate_up's K = H
+    assert mlp(inter=FAKE + 8) == _lib.ERR_ALIGN
+    assert mlp(down=FAKE + 4) == _lib.ERR_ALIGN
+    assert mlp(res=FAKE) == _lib.ERR_NULL            # residual needs gamma
+    assert mlp(res_out=FAKE) == _lib.ERR_NULL        # residual_out needs residual
+    if need:
+        assert mlp(ws=FAKE, ws_n=need - 1) == _lib.ERR_WORKSPACE
+    # M=1 deep down projection: the down plan needs more workspace than gate_up
+    d = L.w4a16_workspace_bytes(1, 13696, 4096, 128, 0)
+    u = L.w4a16_workspace_bytes(1, 4096, 13696, 128, 1)
+    assert L.w4a16_mlp_workspace_bytes(1, 4096, 13696, 128) == max(d, u)
+    if d > u:
+        assert mlp(M=1, H=4096, I=13696, ws_n=d - 1) == _lib.ERR_WORKSPACE

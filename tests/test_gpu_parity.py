@@ -236,6 +236,25 @@ def test_rmsnorm_odd_k_tile_count(M, g, gu):
         check_close(run_gemm(p), ref_gemm(p), f"odd-k M={M} g={g}")
 
 
+def test_staging_and_split_calls_share_one_workspace():
+    """Calls with the RMSNorm prologue above M = 16 stage their rows in the
+    workspace; split-K calls count arrivals at its start.  Alternating them on
+    one workspace must leave every result right (the staging never overlaps
+    the counters, which every call leaves at zero)."""
+    ws = w4.Workspace()
+    cases = [synth.make_problem(70, 1152, 256, 128, seed=1, gamma=True),   # tile, staged
+             synth.make_problem(5, 1152, 256, 64, seed=2, gamma=True),     # stream, split-K
+             synth.make_problem(20, 1152, 256, 64, seed=3, gamma=True),    # panel, split-K + staged
+             synth.make_problem(9, 1152, 256, 128, seed=4)]                # stream, split-K
+    dev = [(to_dev(p.A), repack_dev(p.w), to_dev(p.gamma)) for p in cases]
+    for rep in range(2):
+        for p, (A, w, gm) in zip(cases, dev):
+            y = w4.gemm(A, w, gamma=gm, out=nan_out(p.M, p.N), workspace=ws)
+            torch.cuda.synchronize()
+            check_close(y.cpu().numpy(), ref_gemm(p, rms=p.gamma is not None),
+                        f"shared workspace M={p.M} pass {rep}")
+
+
 def test_unfused_chain_matches_fused():
     """FUSED=0 chain (GEMM -> bias pass -> ReLU pass; RMSNorm pass -> GEMM)
     computes the same as the fused kernels, within the tolerance."""
@@ -417,3 +436,73 @@ def test_probes():
     w4.probe_read(src, sink)
     torch.cuda.synchronize()
     assert torch.equal(src, dst)
+
+
+# ------------------------------------------------------------ MLP chain
+
+
+def _mlp_case(M, H, I, g, seed, gamma=False, resid=False, asym=True):
+    rng = np.random.default_rng(seed)
+    A = rng.standard_normal((M, H)).astype(F16)
+    ws = [synth.draw_weight(rng, H, I, g, asym=asym), synth.draw_weight(rng, H, I, g, asym=asym),
+          synth.draw_weight(rng, I, H, g, asym=asym)]
+    gm = rng.normal(1.0, 0.1, size=H).astype(F16) if gamma or resid else None
+    R = rng.standard_normal((M, H)).astype(F16) if resid else None
+    return A, ws, gm, R
+
+
+def _mlp_ref(A, ws, gm, R, g, I, H, cols=None):
+    X = A if R is None else oracle.skip_sum(A, R)
+    t = [(w.qweight, w.scales, w.zeros) for w in ws]
+    return X, oracle.mlp(X, t[0], t[1], t[2], g, I, H, gamma=gm, cols=cols)
+
+
+@pytest.mark.parametrize("M,H,I,g,gamma,resid", [
+    (1, 512, 1024, 128, False, False), (8, 512, 1536, 64, True, False),
+    (13, 384, 768, 32, False, False), (24, 512, 1024, 128, True, True),
+    (64, 256, 512, 16, False, False), (129, 256, 384, 128, True, False),
+    (3, 1024, 256, 64, False, True)])
+def test_mlp_chain_all_outputs(M, H, I, g, gamma, resid):
+    """w4a16_mlp: the intermediate against the oracle's gate_up, the output
+    against the oracle's chain (both every element), the residual sum
+    bit-exact, and the output bit-identical to the two separate calls."""
+    A, ws, gm, R = _mlp_case(M, H, I, g, seed=M * 7 + I, gamma=gamma, resid=resid)
+    X, ref = _mlp_ref(A, ws, gm, R, g, I, H)
+    pg, pu, pd = (repack_dev(w) for w in ws)
+    Ad, gd, Rd = to_dev(A), to_dev(gm), to_dev(R)
+    inter = nan_out(M, I)
+    s_out = torch.full((M, H), float("nan"), dtype=torch.float16, device="cuda") if resid else None
+    y = w4.mlp(Ad, pg, pu, pd, gamma=gd, residual=Rd, residual_out=s_out, inter=inter,
+               out=nan_out(M, H))
+    torch.cuda.synchronize()
+    t = [(w.qweight, w.scales, w.zeros) for w in ws]
+    check_close(inter.cpu().numpy(), oracle.gate_up(X, t[0], t[1], g, I, gamma=gm),
+                f"mlp intermediate M={M} H={H} I={I}")
+    check_close(y.cpu().numpy(), ref, f"mlp M={M} H={H} I={I} g={g}")
+    if resid:
+        assert np.array_equal(s_out.cpu().numpy().view(np.uint16), X.view(np.uint16))
+    h = w4.gemm_gate_up(Ad, pg, pu, gamma=gd, residual=Rd)
+    y2 = w4.gemm(h, pd)
+    torch.cuda.synchronize()
+    assert torch.equal(h, inter) and torch.equal(y2, y)
+
+
+@pytest.mark.parametrize("M,H,I", [(8, 4096, 13696), (1, 5120, 13824), (32, 4096, 13696)])
+def test_mlp_decode_shapes_sampled(M, H, I):
+    """The decode MLP shapes (gate_up H x 2*I, down I x H; the down
+    projection is the deep-k split-K shape) with the RMSNorm prologue: the
+    intermediate and the output on sampled columns."""
+    g = 128
+    A, ws, gm, R = _mlp_case(M, H, I, g, seed=H + I + M, gamma=True)
+    cols = sample_cols(H, 96, seed=M)
+    X, ref = _mlp_ref(A, ws, gm, R, g, I, H, cols=cols)
+    inter = nan_out(M, I)
+    y = w4.mlp(to_dev(A), *(repack_dev(w) for w in ws), gamma=to_dev(gm), inter=inter,
+               out=nan_out(M, H))
+    torch.cuda.synchronize()
+    icols = sample_cols(I, 96, seed=M + 1)
+    t = [(w.qweight, w.scales, w.zeros) for w in ws]
+    check_close(inter.cpu().numpy()[:, icols],
+                oracle.gate_up(X, t[0], t[1], g, I, gamma=gm, cols=icols), f"mlp inter M={M}")
+    check_close(y.cpu().numpy()[:, cols], ref, f"mlp decode M={M} H={H} I={I}")
+    assert torch.isfinite(y).all()
