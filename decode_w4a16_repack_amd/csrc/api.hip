@@ -42,9 +42,9 @@ int check_gemm(const void *A, int M, int K, int N, int group, int scale_dtype,
   return W4A16_OK;
 }
 
-// A call with the RMSNorm prologue needs the plan's staging buffers too.
-int check_workspace(const Plan &pl, bool rms, const void *ws, size_t ws_bytes) {
-  const size_t need = rms ? pl.ws_total_rms : pl.ws_total;
+// A call that stages its RMSNorm prologue needs the plan's staging buffers too.
+int check_workspace(const Plan &pl, bool staged, const void *ws, size_t ws_bytes) {
+  const size_t need = staged ? pl.ws_total_rms : pl.ws_total;
   if (need == 0) return W4A16_OK;
   if (ws == nullptr) return W4A16_ERR_WORKSPACE;
   if (ws_bytes < need) return W4A16_ERR_WORKSPACE;
@@ -84,7 +84,7 @@ void fill_workspace(GemmArgs &a, const Plan &pl, void *ws) {
   a.ws_part = pl.ws_total ? reinterpret_cast<float *>(b + pl.ws_part_off) : nullptr;
   a.ws_rms = pl.ws_total ? reinterpret_cast<float *>(b + pl.ws_rms_off) : nullptr;
   a.ws_cnt = pl.ws_total ? reinterpret_cast<uint32_t *>(b + pl.ws_cnt_off) : nullptr;
-  const bool staged = b != nullptr && pl.kind != kKindStream;
+  const bool staged = b != nullptr && pl.ws_total_rms > pl.ws_total;
   a.ws_x = staged ? reinterpret_cast<f16 *>(b + pl.ws_x_off) : nullptr;
   a.ws_ss = staged ? reinterpret_cast<float *>(b + pl.ws_ss_off) : nullptr;
 }
@@ -172,7 +172,8 @@ int prep_gemm(const void *A, const void *resid, void *resid_out, int M, int K, i
     return W4A16_ERR_ALIGN;
   st = plan_for(M, K, N, group, scale_dtype, false, split, c.pl);
   if (st != W4A16_OK) return st;
-  st = check_workspace(c.pl, rms_gamma != nullptr, workspace, workspace_bytes);
+  st = check_workspace(c.pl, staged_prologue(c.pl.kind, M, rms_gamma != nullptr, resid != nullptr),
+                       workspace, workspace_bytes);
   if (st != W4A16_OK) return st;
 
   const int sb = scale_bytes_of(scale_dtype);
@@ -211,7 +212,8 @@ int prep_gate_up(const void *A, const void *resid, void *resid_out, int M, int K
   if (rms_gamma != nullptr && !aligned16(rms_gamma)) return W4A16_ERR_ALIGN;
   st = plan_for(M, K, N, group, scale_dtype, true, split, c.pl);
   if (st != W4A16_OK) return st;
-  st = check_workspace(c.pl, rms_gamma != nullptr, workspace, workspace_bytes);
+  st = check_workspace(c.pl, staged_prologue(c.pl.kind, M, rms_gamma != nullptr, resid != nullptr),
+                       workspace, workspace_bytes);
   if (st != W4A16_OK) return st;
 
   const int sb = scale_bytes_of(scale_dtype);

@@ -111,6 +111,15 @@ struct Plan {
   size_t ws_x_off, ws_ss_off, ws_total_rms;
 };
 
+// Whether a call stages its RMSNorm prologue (stage.hip) instead of running
+// it inside the product kernel: always for the panel and tile kernels; for
+// the streaming kernel only with the residual and more than 4 rows, where
+// re-reading both activation slices in every column block costs more than
+// one staging pass.
+inline bool staged_prologue(int kind, int M, bool gamma, bool resid) {
+  return gamma && (kind != kKindStream || (resid && M > 4));
+}
+
 // force_kind: -1 automatic, else a PlanKind; force_cfg < 0 /
 // force_split <= 0 select the built-in choice.
 Plan make_plan(int M, int K, int N, int group, int scale_bytes, bool gate_up,

@@ -100,7 +100,9 @@ bool plan_stream(Plan &p, int M, int K, int N, int group, int scale_bytes, bool 
   const int gpw = c.kpw * (kTileK / group);
   const size_t ms = (size_t)c.cpw * gpw * 16 * scale_bytes;
   const size_t mz = align16((size_t)c.cpw * gpw * 8);
-  const size_t meta = NW * (ms + mz);
+  // scales and zero-points per weight stream, then the slice's RMSNorm gamma
+  // (reserved whether or not a call has one: the plan depends on the shape)
+  const size_t meta = NW * (ms + mz) + (size_t)c.kpw * kTileK * 2;
   const size_t red = (size_t)NW * c.cpw * 1024;
   p.rows_pow2 = pow2_at_least(M);
   const size_t a_lds = (size_t)c.kpw * 256 * p.rows_pow2;
@@ -213,12 +215,12 @@ void plan_tile(Plan &p, int M, int K, int N, int group, int scale_bytes, bool ga
   p.ws_total = 0;
 }
 
-// Panel and tile plans: the RMSNorm staging buffers after the plan's own
+// Plans whose prologue may be staged: the RMSNorm staging buffers after the plan's own
 // workspace (fp16 [M][K] staged rows, fp32 [M] sums of squares), and never
 // inside the arrival counters at its start, which every plan shares and
 // leaves at zero (a plan without split-K has no workspace of its own).
 void add_staging(Plan &p, int M, int K) {
-  if (p.kind == kKindStream) {
+  if (!staged_prologue(p.kind, M, true, true)) {
     p.ws_total_rms = p.ws_total;
     return;
   }
@@ -253,10 +255,9 @@ Plan make_plan(int M, int K, int N, int group, int scale_bytes, bool gate_up, in
 
 hipError_t launch_gemm(const GemmArgs &a, const Plan &pl, int group, bool scale_f32,
                        bool gate_up, hipStream_t stream) {
-  if (pl.kind == kKindStream) return launch_stream(a, pl, group, scale_f32, gate_up, stream);
-  if (a.gamma != nullptr) {
-    // RMSNorm prologue of the panel / tile kernels: stage the rows, then the
-    // plain product on them with the row scale in the epilogue
+  if (staged_prologue(pl.kind, a.M, a.gamma != nullptr, a.resid != nullptr)) {
+    // stage the normalized rows, then the plain product on them with the
+    // row scale in the epilogue
     const hipError_t e = launch_rms_stage(a.A, a.resid, a.resid_out, a.gamma, a.M, a.K,
                                           a.ws_x, a.ws_ss, stream);
     if (e != hipSuccess) return e;
@@ -268,6 +269,7 @@ hipError_t launch_gemm(const GemmArgs &a, const Plan &pl, int group, bool scale_
     b.row_ss = a.ws_ss;
     return launch_gemm(b, pl, group, scale_f32, gate_up, stream);
   }
+  if (pl.kind == kKindStream) return launch_stream(a, pl, group, scale_f32, gate_up, stream);
   if (pl.kind == kKindPanel) return launch_panel(a, pl, group, scale_f32, gate_up, stream);
   return launch_tile(a, pl, group, scale_f32, gate_up, stream);
 }

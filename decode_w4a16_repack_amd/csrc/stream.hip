@@ -30,7 +30,9 @@
 //    final reduction, so the only barrier is the one before it;
 //  * the slice partial sums go through the same private regions; wavefront
 //    c < CPW finishes column tile c: slice sum in slice order, RMSNorm
-//    factor, epilogue, one fp16 write.
+//    factor, epilogue, one fp16 write.  With a residual and more than 4 rows
+//    the skip + RMSNorm prologue is staged instead (stage.hip): every column
+//    block would otherwise read both activation slices.
 #include "device.h"
 
 namespace w4a16 {
@@ -89,7 +91,8 @@ stream_kernel(const GemmArgs p) {
   uint8_t *region = smem + wk * p.lds_s;
   uint8_t *ms = region;                   // [NW] x MS_BYTES
   uint8_t *mz = region + NW * MS_BYTES;   // [NW] x MZ_PAD
-  uint8_t *aslots = mz + NW * MZ_PAD;     // ALDS: KPW * 16 * R slots of 16 bytes
+  uint8_t *mg = mz + NW * MZ_PAD;         // the slice's gamma, [KPW][128] fp16
+  uint8_t *aslots = mg + KPW * kTileK * 2;  // ALDS: KPW * 16 * R slots of 16 bytes
   float *lRms = reinterpret_cast<float *>(smem + p.lds_r);  // [NWK][16]
 
   // 1. this slice's scales and zero-points of the CPW column tiles: runs of
@@ -127,6 +130,20 @@ stream_kernel(const GemmArgs p) {
     } else {
       for (int e = lane; e * 4 < MZ_BYTES; e += 64)  // symmetric: every zero-point is 8
         reinterpret_cast<uint32_t *>(mzi)[e] = 0x88888888u;
+    }
+  }
+
+  if (rms) {
+    // the slice's gamma (positions past the slice copy a valid tile): read
+    // back from LDS by the prologue, so it holds no registers while the
+    // activations, the residual and the first weight tiles are in flight
+#pragma unroll
+    for (int q = 0; q < (KPW * 16 + 63) / 64; ++q) {
+      const int u = q * 64 + lane;
+      if (u < KPW * 16) {
+        const int kc = min(my_kb + min(u >> 4, max(my_n - 1, 0)), KC - 1);
+        copy16_to_lds(p.gamma + kc * kTileK + (u & 15) * 8, mg + q * 1024);
+      }
     }
   }
 
@@ -183,68 +200,20 @@ stream_kernel(const GemmArgs p) {
     }
   };
 
-  // 3. RMSNorm prologue on the fragments (before the weight stream starts,
-  //    so the gamma fragments are dead by then): per-lane sum of squares
-  //    (row l%16, this lane's k slots), x * gamma rounded once to fp16; the
-  //    factor 1/sqrt(mean + eps) is applied in the epilogue.
-  float ss = 0.f;
-  if (rms) {
-    if (p.resid != nullptr) {
-      // residual add first (skip + RMSNorm): s = A + resid rounded once to
-      // fp16; the workgroups of column block 0 write s out, each (row, k)
-      // once
-      f16x8 rr[KPW][4];
-      const f16 *rrow = p.resid + (size_t)(m0 + arow) * p.K + 8 * kq;
-#pragma unroll
-      for (int t = 0; t < KPW; ++t) {
-        const int kc = min(my_kb + min(t, max(my_n - 1, 0)), KC - 1);
-#pragma unroll
-        for (int d = 0; d < 4; ++d)
-          rr[t][d] = *reinterpret_cast<const f16x8 *>(rrow + kc * kTileK + 32 * d);
-      }
-      wait_vmcnt<0>();
-      read_slots();
-#pragma unroll
-      for (int t = 0; t < KPW; ++t)
-#pragma unroll
-        for (int d = 0; d < 4; ++d) a[t][d][0] = a[t][d][0] + rr[t][d];
-      zero_tail();
-      if (p.resid_out != nullptr && blockIdx.x == 0 && c < mrows) {
-        f16 *orow = p.resid_out + (size_t)(m0 + c) * p.K + 8 * kq;
-#pragma unroll
-        for (int t = 0; t < KPW; ++t)
-          if (t < my_n)
-#pragma unroll
-            for (int d = 0; d < 4; ++d)
-              *reinterpret_cast<f16x8 *>(orow + (my_kb + t) * kTileK + 32 * d) = a[t][d][0];
-      }
-    }
-    f16x8 gam[KPW][4];
+  // 3. skip + RMSNorm: the residual fragments of the slice, issued with the
+  //    activations so that one wait covers both (the first weight tiles,
+  //    issued next, stay in flight)
+  const bool has_res = rms && p.resid != nullptr;
+  f16x8 rr[KPW][4];
+  if (has_res) {
+    const f16 *rrow = p.resid + (size_t)(m0 + arow) * p.K + 8 * kq;
 #pragma unroll
     for (int t = 0; t < KPW; ++t) {
       const int kc = min(my_kb + min(t, max(my_n - 1, 0)), KC - 1);
 #pragma unroll
       for (int d = 0; d < 4; ++d)
-        gam[t][d] = *reinterpret_cast<const f16x8 *>(p.gamma + kc * kTileK + 32 * d + 8 * kq);
+        rr[t][d] = *reinterpret_cast<const f16x8 *>(rrow + kc * kTileK + 32 * d);
     }
-    wait_vmcnt<0>();
-    if (p.resid == nullptr) {
-      read_slots();
-      zero_tail();
-    }
-#pragma unroll
-    for (int t = 0; t < KPW; ++t)
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        f16x8 x = a[t][d][0];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float xf = (float)x[e];
-          ss += xf * xf;
-          x[e] = (f16)(xf * (float)gam[t][d][e]);
-        }
-        a[t][d][0] = x;
-      }
   }
 
   // 4. the first PD weight tiles; tile f = t * CPW + w (k tile t, column
@@ -265,12 +234,47 @@ stream_kernel(const GemmArgs p) {
   // 5. this wavefront's copies into its region have landed (completion is
   //    in issue order); no other wavefront reads the region before the end
   wait_vmcnt<(AFTER_COPIES < 63 ? AFTER_COPIES : 63)>();
-  if (!rms) {
-    read_slots();
-    zero_tail();
+  read_slots();
+
+  // 6. RMSNorm prologue on the fragments: with a residual, s = A + resid
+  //    rounded once to fp16 (the workgroups of column block 0 write s out,
+  //    each (row, k) once); then the per-lane sum of squares (row l%16, this
+  //    lane's k slots; fp16 products are exact in fp32) and x * gamma rounded
+  //    once to fp16 (the packed multiply rounds the exact product once).
+  //    The factor 1/sqrt(mean + eps) is applied in the epilogue.
+  float ss = 0.f;
+  if (has_res) {
+#pragma unroll
+    for (int t = 0; t < KPW; ++t)
+#pragma unroll
+      for (int d = 0; d < 4; ++d) a[t][d][0] = a[t][d][0] + rr[t][d];
+  }
+  zero_tail();
+  if (has_res && p.resid_out != nullptr && blockIdx.x == 0 && c < mrows) {
+    f16 *orow = p.resid_out + (size_t)(m0 + c) * p.K + 8 * kq;
+#pragma unroll
+    for (int t = 0; t < KPW; ++t)
+      if (t < my_n)
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+          *reinterpret_cast<f16x8 *>(orow + (my_kb + t) * kTileK + 32 * d) = a[t][d][0];
+  }
+  if (rms) {
+#pragma unroll
+    for (int t = 0; t < KPW; ++t)
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const f16x8 x = a[t][d][0];
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          const f16x2 x2 = {x[2 * h], x[2 * h + 1]};
+          ss = __builtin_amdgcn_fdot2(x2, x2, ss, false);
+        }
+        a[t][d][0] = x * *reinterpret_cast<const f16x8 *>(mg + (t * kTileK + 32 * d + 8 * kq) * 2);
+      }
   }
 
-  // 6. contraction, k tile outer, column tile inner.  The codes enter the
+  // 7. contraction, k tile outer, column tile inner.  The codes enter the
   //    matrix core bare (q * 2^-24); the activation slots facing 16q codes
   //    are pre-scaled by 1/16, and each k tile's group row sums serve its
   //    CPW column tiles for the zero-point term.
@@ -310,7 +314,7 @@ stream_kernel(const GemmArgs p) {
     }
   }
 
-  // 7. slice partial sums into the wavefront's own region ([i][w][lane],
+  // 8. slice partial sums into the wavefront's own region ([i][w][lane],
   //    16 bytes per lane), row sums of squares of the slice; one barrier;
   //    wavefront w < CPW then sums column tile w over the slices in order
   f32x4 *red = reinterpret_cast<f32x4 *>(region);
@@ -341,7 +345,7 @@ stream_kernel(const GemmArgs p) {
     for (int w2 = 0; w2 < NWK; ++w2) rs += reinterpret_cast<const f32x4 *>(lRms + w2 * 16)[kq];
   const int ncol = (ct0 + wfin) * kTileN + c;
 
-  // 8. k splits across workgroups (narrow grids and very deep k only): the
+  // 9. k splits across workgroups (narrow grids and very deep k only): the
   //    finishing wavefronts store partials; the finishing wavefront of the
   //    last workgroup to arrive (counted per column tile) sums them in split
   //    order.  Partials, sums of squares and counters are agent-scope atomic
@@ -391,13 +395,15 @@ stream_kernel(const GemmArgs p) {
     if (lane == 0) reset_arrival(&p.ws_cnt[cnt]);
   }
 
-  // 9. epilogue, one fp16 write per output
+  // 10. epilogue, one fp16 write per output
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int row = 4 * kq + e;
     if (row < mrows) {
       float rsc = 1.0f;
       if (rms) rsc = 1.0f / sqrtf(rs[e] / (float)p.K + p.eps);
+      else if (p.row_ss != nullptr)  // rows staged by stage.hip
+        rsc = 1.0f / sqrtf(p.row_ss[m0 + row] / (float)p.K + p.eps);
       float y;
       if constexpr (GU) {
         y = silu(fin[0][e] * rsc) * (fin[1][e] * rsc);

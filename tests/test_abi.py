@@ -125,25 +125,30 @@ def test_aux_validation(L):
 
 
 def test_workspace_only_for_narrow_grids(L):
-    # wide N fills the chip without k splits across workgroups.  M <= 16 (the
+    # wide N fills the chip without k splits across workgroups.  M <= 4 (the
     # streaming kernel, RMSNorm prologue in registers): no workspace.  Above
-    # 16 the workspace holds only the RMSNorm staging (fp16 [M][K] rows, fp32
-    # [M] sums of squares, each 256-byte aligned), which only calls with the
-    # prologue need.  It starts after the 4096 bytes of split-K arrival
+    # that the workspace holds only the RMSNorm staging (fp16 [M][K] rows,
+    # fp32 [M] sums of squares, each 256-byte aligned), which only calls that
+    # stage their prologue need.  It starts after the 4096 bytes of split-K arrival
     # counters that every plan shares (and leaves at zero): staged rows
     # written there would corrupt the next split-K call.
     a256 = lambda v: (v + 255) // 256 * 256
-    for M in (1, 2, 16):
+    for M in (1, 2, 4):
         assert L.w4a16_workspace_bytes(M, 5120, 13824, 128, 0) == 0
         assert L.w4a16_workspace_bytes(M, 5120, 13824, 128, 1) == 0
-    for M in (17, 32, 64, 128):
+    # M = 5..16: the streaming kernel stages only the skip + RMSNorm prologue
+    for M in (5, 16, 17, 32, 64, 128):
         stage = 4096 + a256(M * 5120 * 2) + a256(M * 4)
         assert L.w4a16_workspace_bytes(M, 5120, 13824, 128, 0) == stage
         assert L.w4a16_workspace_bytes(M, 5120, 13824, 128, 1) == stage
-        # a call with the prologue checks for the staging before any launch
-        assert gemm(L, M=M, K=5120, N=13824, group=128, gamma=FAKE) == _lib.ERR_WORKSPACE
-        assert gemm(L, M=M, K=5120, N=13824, group=128, gamma=FAKE, ws=FAKE,
-                    ws_n=stage - 1) == _lib.ERR_WORKSPACE
+        # a call that stages checks for the staging before any launch
+        if M > 16:
+            assert gemm(L, M=M, K=5120, N=13824, group=128, gamma=FAKE) == _lib.ERR_WORKSPACE
+            assert gemm(L, M=M, K=5120, N=13824, group=128, gamma=FAKE, ws=FAKE,
+                        ws_n=stage - 1) == _lib.ERR_WORKSPACE
+        skip = L.w4a16_gemm_skip_rmsnorm(FAKE, FAKE, None, M, 5120, 13824, 128, 0, 1, FAKE, 0,
+                                         None, FAKE, 1e-6, FAKE, FAKE, stage - 1, None)
+        assert skip == _lib.ERR_WORKSPACE
     assert L.w4a16_workspace_bytes(0, 5120, 13824, 128, 0) == 0
     w1 = L.w4a16_workspace_bytes(1, 5120, 256, 128, 0)
     w1g = L.w4a16_workspace_bytes(1, 5120, 256, 128, 1)
@@ -180,7 +185,7 @@ def test_plan_query_matches_workspace_and_kernel_choice(L):
         ws = max(plan(L, M, K, N, sdt=s, gu=gu)[1].workspace_bytes for s in (0, 1))
         assert ws == L.w4a16_workspace_bytes(M, K, N, 128, gu)
         # split-K exchange, plus the RMSNorm staging rows above M = 16
-        stage = 0 if M <= 16 else 4096 + (M * K * 2 + 255) // 256 * 256 + (M * 4 + 255) // 256 * 256
+        stage = 0 if M <= 4 else 4096 + (M * K * 2 + 255) // 256 * 256 + (M * 4 + 255) // 256 * 256
         assert (info.workspace_bytes > stage) == (info.split > 1)
         assert info.workspace_bytes >= stage
 
@@ -205,7 +210,8 @@ def test_plan_deep_k_splits_and_forced_splits(L):
         st, f = plan(L, 8, 13696, 4096, split=sk)
         assert st == _lib.OK and f.split <= sk and f.workspace_bytes > 0
     st, f = plan(L, 8, 4096, 4096, split=1)
-    assert st == _lib.OK and f.split == 1 and f.workspace_bytes == 0
+    # no split-K exchange: only the skip + RMSNorm staging (after the counters)
+    assert st == _lib.OK and f.split == 1 and f.workspace_bytes == 4096 + 8 * 4096 * 2 + 256
     assert L.w4a16_plan(8, 4096, 4096, 128, 0, 0, 0, None) == _lib.ERR_NULL
     assert plan(L, 8, 4000, 4096)[0] == _lib.ERR_SHAPE
 
@@ -215,9 +221,13 @@ def test_forced_split_workspace_checked_before_launch(L):
     on the host (FAKE pointers are never dereferenced)."""
     FAKE = 1 << 20
     st, f = plan(L, 8, 13696, 4096, split=8)
-    assert f.workspace_bytes > 0
+    # the reported size ends with the skip + RMSNorm staging rows; a call
+    # without that prologue needs the split-K part before them
+    staging = (8 * 13696 * 2 + 255) // 256 * 256 + 256
+    split_part = f.workspace_bytes - staging
+    assert split_part > 4096
     assert L.w4a16_gemm_split(FAKE, 8, 13696, 4096, 128, 0, 1, FAKE, 0, None, None, 1e-6,
-                              FAKE, FAKE, f.workspace_bytes - 1, 8, None) == _lib.ERR_WORKSPACE
+                              FAKE, FAKE, split_part - 1, 8, None) == _lib.ERR_WORKSPACE
     assert L.w4a16_gemm_split(FAKE, 8, 13696, 4096, 128, 0, 1, FAKE, 0, None, None, 1e-6,
                               FAKE, FAKE, 1 << 30, 2, None) == _lib.ERR_SPLIT
     assert L.w4a16_gemm_gate_up_split(FAKE, 20, 4096, 4096, 128, 0, 1, FAKE, FAKE, None, 1e-6,
@@ -279,8 +289,10 @@ def test_mlp_validation_before_any_launch(L):
     assert mlp(down=FAKE + 4) == _lib.ERR_ALIGN
     assert mlp(res=FAKE) == _lib.ERR_NULL            # residual needs gamma
     assert mlp(res_out=FAKE) == _lib.ERR_NULL        # residual_out needs residual
-    if need:
-        assert mlp(ws=FAKE, ws_n=need - 1) == _lib.ERR_WORKSPACE
+    # with the skip prologue (staged above 4 rows) every byte of the reported
+    # size is needed by one of the two projections
+    assert need > 0
+    assert mlp(res=FAKE, gamma=FAKE, ws=FAKE, ws_n=need - 1) == _lib.ERR_WORKSPACE
     # M=1 deep down projection: the down plan needs more workspace than gate_up
     d = L.w4a16_workspace_bytes(1, 13696, 4096, 128, 0)
     u = L.w4a16_workspace_bytes(1, 4096, 13696, 128, 1)
