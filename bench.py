@@ -16,7 +16,7 @@ projection) at the decode MLP shapes; a streaming-read probe of the achievable H
 the CPU oracle timed on the host's cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
-                       [--profile-kernel M [--eager]]
+                       [--profile-kernel M [--eager]] [--profile-mlp M]
                        [--traffic-summary FETCH_DIR WRITE_DIR]
 
 --profile-kernel M launches only the GEMM at M (graph-replayed, or eagerly
@@ -50,7 +50,8 @@ INFINITY_CACHE = 256 << 20
 PAGE_M1_US = 69.5  # the pages' M=1 time for this shape (H200, context only)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemv_m1.json")
 KERNEL_SOURCES = ["decode_w4a16_repack_amd/csrc/" + f for f in
-                  ("stream.hip", "panel.hip", "tile.hip", "device.h", "gemm.hip", "common.h")]
+                  ("stream.hip", "stream_kernel.h", "panel.hip", "tile.hip", "device.h", "gemm.hip",
+                   "common.h")]
 COPY_PROBE_BYTES = 256 << 20  # plain copy of known size, counter calibration
 
 
@@ -341,6 +342,38 @@ def split_sweep(ws, M=8, group=128):
 MLP_SHAPES = [("mlp_4096x13696", 4096, 13696), ("mlp_5120x13824", 5120, 13824)]
 
 
+def mlp_weight_bytes(H, I, group):
+    return 2 * algorithmic_bytes(0, H, I, group) + algorithmic_bytes(0, I, H, group)
+
+
+def mlp_sets(gen, H, I, group):
+    """Rotating resident sets of the three packed MLP weights (gate, up:
+    K = H, N = I; down: K = I, N = H) and gamma, enough that a replay cycle
+    streams twice the Infinity Cache from HBM."""
+    import torch
+    import decode_w4a16_repack_amd as w4
+
+    def packed(K_, N_):
+        G = K_ // group
+        q = torch.randint(0, 256, (N_, K_ // 2), dtype=torch.uint8, device="cuda", generator=gen)
+        sc = (torch.rand((N_, G), device="cuda", generator=gen) * 0.019 + 0.001).half()
+        z = torch.randint(0, 256, (N_, (G + 1) // 2), dtype=torch.uint8, device="cuda", generator=gen)
+        return w4.repack(q, sc, z, K_, N_, group)
+    R = max(2, math.ceil(2 * INFINITY_CACHE / mlp_weight_bytes(H, I, group)))
+    return [{"w": [packed(H, I), packed(H, I), packed(I, H)], "H": H, "I": I,
+             "gamma": (1.0 + 0.1 * torch.randn((H,), device="cuda", generator=gen)).half()}
+            for _ in range(R)]
+
+
+def mlp_inputs(gen, sets, M):
+    """Activations, intermediate and output buffers of M rows in every set."""
+    import torch
+    for st in sets:
+        st["A"] = torch.randn((M, st["H"]), device="cuda", generator=gen).half()
+        st["inter"] = torch.empty((M, st["I"]), dtype=torch.float16, device="cuda")
+        st["out"] = torch.empty((M, st["H"]), dtype=torch.float16, device="cuda")
+
+
 def mlp_chain(ws, Ms=(1, 8, 32), group=128):
     """w4a16_mlp (gate_up with the RMSNorm prologue, fp16 intermediate, down
     projection) at the decode MLP shapes, beside its two projections timed
@@ -351,24 +384,12 @@ def mlp_chain(ws, Ms=(1, 8, 32), group=128):
     rows = []
     gen = torch.Generator(device="cuda")
     gen.manual_seed(500)
-
-    def packed(K_, N_):
-        G = K_ // group
-        q = torch.randint(0, 256, (N_, K_ // 2), dtype=torch.uint8, device="cuda", generator=gen)
-        sc = (torch.rand((N_, G), device="cuda", generator=gen) * 0.019 + 0.001).half()
-        z = torch.randint(0, 256, (N_, (G + 1) // 2), dtype=torch.uint8, device="cuda", generator=gen)
-        return w4.repack(q, sc, z, K_, N_, group)
     for name, H, I in MLP_SHAPES:
-        wbytes = 2 * algorithmic_bytes(0, H, I, group) + algorithmic_bytes(0, I, H, group)
-        R = max(2, math.ceil(2 * INFINITY_CACHE / wbytes))
-        sets = [{"w": [packed(H, I), packed(H, I), packed(I, H)],
-                 "gamma": (1.0 + 0.1 * torch.randn((H,), device="cuda", generator=gen)).half()}
-                for _ in range(R)]
+        wbytes = mlp_weight_bytes(H, I, group)
+        sets = mlp_sets(gen, H, I, group)
+        R = len(sets)
         for M in Ms:
-            for st in sets:
-                st["A"] = torch.randn((M, H), device="cuda", generator=gen).half()
-                st["inter"] = torch.empty((M, I), dtype=torch.float16, device="cuda")
-                st["out"] = torch.empty((M, H), dtype=torch.float16, device="cuda")
+            mlp_inputs(gen, sets, M)
             byt = wbytes + 2 * M * H + 2 * 2 * M * I + 2 * M * H
             t_mlp = time_graph(lambda st: w4.mlp(st["A"], *st["w"], gamma=st["gamma"],
                                                  inter=st["inter"], out=st["out"], workspace=ws),
@@ -521,6 +542,9 @@ def main():
                     help="only launch the GEMM at this M (for rocprofv3)")
     ap.add_argument("--eager", action="store_true",
                     help="with --profile-kernel: eager launches, no graph")
+    ap.add_argument("--profile-mlp", type=int, default=0,
+                    help="only run the MLP block (H=4096, I=13696, RMSNorm) at this M "
+                         "(for rocprofv3)")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     args = ap.parse_args()
     if args.traffic_summary:
@@ -537,6 +561,17 @@ def main():
     torch.cuda.set_device(0)
     ws = w4.Workspace()
 
+    if args.profile_mlp:
+        M = args.profile_mlp
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(500)
+        sets = mlp_sets(gen, 4096, 13696, GROUP)
+        mlp_inputs(gen, sets, M)
+        us = time_graph(lambda st: w4.mlp(st["A"], *st["w"], gamma=st["gamma"],
+                                          inter=st["inter"], out=st["out"], workspace=ws),
+                        sets, steps=args.steps, warmup=args.warmup)
+        log(f"profile mlp M={M}: {us:.2f} us per block, graph-replayed")
+        return
     if args.profile_kernel:
         M = args.profile_kernel
         sets = InputSets(M, rotations_needed(M))

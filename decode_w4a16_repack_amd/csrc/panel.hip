@@ -36,8 +36,9 @@ namespace w4a16 {
 
 namespace {
 
+// (occupancy NWK / 4 wavefronts per SIMD, as for the streaming kernel)
 template <int MT, int CPW, int KPW, int NWK, int PD, bool ADB, int G, bool SF32, bool GU>
-__global__ void __launch_bounds__(64 * NWK)
+__global__ void __launch_bounds__(64 * NWK) __attribute__((amdgpu_waves_per_eu(NWK / 4, NWK / 4)))
 panel_kernel(const GemmArgs p) {
   constexpr int NW = GU ? 2 : 1;
   constexpr int PDE = GU ? (PD + 1) / 2 : PD;  // tiles in flight per weight stream

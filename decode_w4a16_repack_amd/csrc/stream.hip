@@ -1,476 +1,10 @@
-// Small-M fused W4A16 GEMM/GEMV for gfx950 (M <= 16 per 16-row tile): the
-// HBM-bound decode regime, where the whole cost is streaming the packed
-// weights once.
-//
-// Method (onnx-genai pull request "Marlin-style fused fp16xint4 tensor-core
-// GEMM", "What's landed"): repacked weights, in-register unpack to the exact
-// integers (q - zp), matrix-core contraction, per-group scale after the
-// accumulate; split-K with a fixed-order reduction ("P2 - widen the win:
-// split-K" and "Small-M split-K retune": at small M the weight loads in
-// flight set the speed, so k is split to put more of them in flight).
-//
-// gfx950 design:
-//  * a workgroup is NWK wavefronts, one per k slice; each wavefront owns
-//    KPW consecutive 128-k tiles of the workgroup's k range for the same
-//    CPW 16-column weight tiles, so the workgroup covers CPW column tiles
-//    over its whole k range and reduces the NWK slices in LDS in slice order
-//    (no partial sums leave the workgroup unless the k range itself is split
-//    across workgroups, which only narrow or very deep shapes need);
-//  * each lane keeps its activation fragments for the wavefront's k slice in
-//    registers for the whole kernel (row l%16, k slots 8*(l/16)..+7 of every
-//    32-k step), so the CPW column tiles reuse them and no activation
-//    traffic or barrier sits in the loop;
-//  * the wavefront streams its CPW x KPW weight tiles (one 16-byte load per
-//    lane per 1 KiB tile), PD tiles ahead of the contraction, k tile outer
-//    and column tile inner so consecutive MFMA chains are independent;
-//  * each wavefront copies the scales and zero-points of its slice (runs of
-//    the packed layout) into a private LDS region with direct global-to-LDS
-//    loads, and for M <= 8 also its activation rows (unique data, then read
-//    back as fragments); nothing is shared between wavefronts until the
-//    final reduction, so the only barrier is the one before it;
-//  * the slice partial sums go through the same private regions; wavefront
-//    c < CPW finishes column tile c: slice sum in slice order, RMSNorm
-//    factor, epilogue, one fp16 write.  With a residual and more than 4 rows
-//    the skip + RMSNorm prologue is staged instead (stage.hip): every column
-//    block would otherwise read both activation slices.
-#include "device.h"
+// Small-M fused W4A16 GEMM/GEMV for gfx950 (M <= 16): the plain kernels
+// (no RMSNorm prologue, or the prologue staged by stage.hip) and the
+// configuration table the planner reads.  The kernel and its design notes
+// are in stream_kernel.h.
+#include "stream_kernel.h"
 
 namespace w4a16 {
-
-namespace {
-
-template <int CPW, int KPW, int NWK, int PD, bool ALDS, int G, bool SF32, bool GU>
-__global__ void __launch_bounds__(64 * NWK)
-stream_kernel(const GemmArgs p) {
-  static_assert(CPW <= NWK, "one finishing wavefront per column tile");
-  static_assert(PD >= 1 && PD <= CPW * KPW, "prefetch depth");
-  constexpr int NW = GU ? 2 : 1;
-  // tiles in flight: gate_up loads two per tile, so half as many tiles
-  constexpr int PDE = GU ? (PD + 1) / 2 : PD;
-  constexpr int GPC = 128 / G;
-  constexpr int SB = SF32 ? 4 : 2;
-  constexpr int NTILE = CPW * KPW;
-  constexpr int GPW = KPW * GPC;                 // groups of one wavefront's k slice
-  constexpr int MS_BYTES = CPW * GPW * 16 * SB;  // its scales, [CPW][GPW][16]
-  constexpr int MZ_BYTES = CPW * GPW * 8;        // its zero-points, [CPW][GPW][8 bytes]
-  constexpr int MZ_PAD = (MZ_BYTES + 15) / 16 * 16;
-  constexpr int SU = GPW * SB;                   // 16-byte scale units per column tile
-  constexpr int ZU = GPW * 2;                    // 4-byte zero-point units per column tile
-  // loads issued after the direct-to-LDS copies that may still be in
-  // flight when the copies are waited for: the register activation
-  // fragments (unless they come through LDS) and the first PD tiles
-  constexpr int AFTER_COPIES = (ALDS ? 0 : 4 * KPW) + PDE * NW;
-
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wk = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int NTL = p.N / kTileN;
-  const int KC = p.K / kTileK;
-  const int Gall = p.K / G;
-  const int ct0 = blockIdx.x * CPW;
-  const int s = blockIdx.y;
-  const int S = p.split;
-  const int m0 = blockIdx.z * 16;
-  const int mrows = min(16, p.M - m0);
-  const int kb = s * p.cps;
-  const int nkc = min(KC, kb + p.cps) - kb;
-  const int my_kb = kb + wk * KPW;
-  const int my_n = max(0, min(KPW, nkc - wk * KPW));  // valid k tiles of this slice
-  const bool rms = p.gamma != nullptr;
-  const bool has_zp = p.has_zp != 0;
-  const int kq = lane >> 4;
-  const int c = lane & 15;
-  const int R = p.rows_pow2;  // activation rows staged in LDS (ALDS)
-
-  // LDS: one private region per wavefront (its scales, zero-points and,
-  // with ALDS, activation slots; reused for its partial sums at the end),
-  // then the per-slice row sums of squares.  No region is shared before
-  // the final reduction, so nothing waits for another wavefront until then.
-  uint8_t *region = smem + wk * p.lds_s;
-  uint8_t *ms = region;                   // [NW] x MS_BYTES
-  uint8_t *mz = region + NW * MS_BYTES;   // [NW] x MZ_PAD
-  uint8_t *mg = mz + NW * MZ_PAD;         // the slice's gamma, [KPW][128] fp16
-  uint8_t *aslots = mg + KPW * kTileK * 2;  // ALDS: KPW * 16 * R slots of 16 bytes
-  float *lRms = reinterpret_cast<float *>(smem + p.lds_r);  // [NWK][16]
-
-  // 1. this slice's scales and zero-points of the CPW column tiles: runs of
-  //    the packed layout, copied straight into the region (reads clamped to
-  //    the column tile's own groups; lanes past the copy write nothing)
-  const int g0 = my_kb * GPC;
-  const size_t srun = (size_t)Gall * 16 * SB;  // scale bytes of one column tile
-#pragma unroll
-  for (int i = 0; i < NW; ++i) {
-    uint8_t *msi = ms + i * MS_BYTES;
-    uint8_t *mzi = mz + i * MZ_PAD;
-    const uint8_t *sbase = reinterpret_cast<const uint8_t *>(p.scales[i]);
-#pragma unroll
-    for (int q = 0; q < (CPW * SU + 63) / 64; ++q) {
-      const int u = q * 64 + lane;
-      if (u < CPW * SU) {
-        const int w = u / SU, o = u - w * SU;
-        const size_t tw = (size_t)min(ct0 + w, NTL - 1);
-        const size_t off = min((size_t)g0 * 16 * SB + (size_t)o * 16, srun - 16);
-        copy16_to_lds(sbase + tw * srun + off, msi + q * 1024);
-      }
-    }
-    if (has_zp) {
-      const size_t zrun = (size_t)Gall * 8;
-#pragma unroll
-      for (int q = 0; q < (CPW * ZU + 63) / 64; ++q) {
-        const int u = q * 64 + lane;
-        if (u < CPW * ZU) {
-          const int w = u / ZU, o = u - w * ZU;
-          const size_t tw = (size_t)min(ct0 + w, NTL - 1);
-          const size_t off = min((size_t)g0 * 8 + (size_t)o * 4, zrun - 4);
-          copy4_to_lds(p.zeros[i] + tw * zrun + off, mzi + q * 256);
-        }
-      }
-    } else {
-      for (int e = lane; e * 4 < MZ_BYTES; e += 64)  // symmetric: every zero-point is 8
-        reinterpret_cast<uint32_t *>(mzi)[e] = 0x88888888u;
-    }
-  }
-
-  if (rms) {
-    // the slice's gamma (positions past the slice copy a valid tile): read
-    // back from LDS by the prologue, so it holds no registers while the
-    // activations, the residual and the first weight tiles are in flight
-#pragma unroll
-    for (int q = 0; q < (KPW * 16 + 63) / 64; ++q) {
-      const int u = q * 64 + lane;
-      if (u < KPW * 16) {
-        const int kc = min(my_kb + min(u >> 4, max(my_n - 1, 0)), KC - 1);
-        copy16_to_lds(p.gamma + kc * kTileK + (u & 15) * 8, mg + q * 1024);
-      }
-    }
-  }
-
-  // 2. activation fragments of this slice (row l%16, k slots 8*(l/16)..+7 of
-  //    each 32-k step).  Rows past M read row M-1 (an A row feeds only its
-  //    own output row, never written); k tiles past the slice read a valid
-  //    tile and are zeroed below, so they add nothing.
-  //    ALDS: the slice's rows are first copied into the region in fragment
-  //    order (slot ((t*4 + d)*4 + kq)*R + row), unique data only.
-  const int arow = min(c, mrows - 1);
-  f16x8 a[KPW][4][1];
-  if constexpr (ALDS) {
-    const int lr = __builtin_ctz(R);
-    const int n_slots = KPW * 16 * R;
-    for (int q = 0; q * 64 < n_slots; ++q) {
-      const int sl = q * 64 + lane;
-      if (sl < n_slots) {
-        const int row = sl & (R - 1);
-        const int rest = sl >> lr;
-        const int kqs = rest & 3, d = (rest >> 2) & 3, t = rest >> 4;
-        const int kc = min(my_kb + min(t, max(my_n - 1, 0)), KC - 1);
-        const f16 *src = p.A + (size_t)(m0 + min(row, mrows - 1)) * p.K + kc * kTileK + 32 * d + 8 * kqs;
-        copy16_to_lds(src, aslots + q * 1024);
-      }
-    }
-  } else {
-    const f16 *arow_p = p.A + (size_t)(m0 + arow) * p.K + 8 * kq;
-#pragma unroll
-    for (int t = 0; t < KPW; ++t) {
-      const int kc = min(my_kb + min(t, max(my_n - 1, 0)), KC - 1);
-#pragma unroll
-      for (int d = 0; d < 4; ++d)
-        a[t][d][0] = *reinterpret_cast<const f16x8 *>(arow_p + kc * kTileK + 32 * d);
-    }
-  }
-  // activation fragments from the slots (ALDS), once the copies landed
-  auto read_slots = [&]() __attribute__((always_inline)) {
-    if constexpr (ALDS) {
-      const uint8_t *ap = aslots + (kq * R + arow) * 16;
-#pragma unroll
-      for (int t = 0; t < KPW; ++t)
-#pragma unroll
-        for (int d = 0; d < 4; ++d)
-          a[t][d][0] = *reinterpret_cast<const f16x8 *>(ap + (t * 4 + d) * 64 * R);
-    }
-  };
-  auto zero_tail = [&]() __attribute__((always_inline)) {
-    if (my_n < KPW) {
-#pragma unroll
-      for (int t = 0; t < KPW; ++t)
-        if (t >= my_n)
-#pragma unroll
-          for (int d = 0; d < 4; ++d) a[t][d][0] = f16x8{};
-    }
-  };
-
-  // 3. skip + RMSNorm: the residual fragments of the slice, issued with the
-  //    activations so that one wait covers both (the first weight tiles,
-  //    issued next, stay in flight)
-  const bool has_res = rms && p.resid != nullptr;
-  f16x8 rr[KPW][4];
-  if (has_res) {
-    const f16 *rrow = p.resid + (size_t)(m0 + arow) * p.K + 8 * kq;
-#pragma unroll
-    for (int t = 0; t < KPW; ++t) {
-      const int kc = min(my_kb + min(t, max(my_n - 1, 0)), KC - 1);
-#pragma unroll
-      for (int d = 0; d < 4; ++d)
-        rr[t][d] = *reinterpret_cast<const f16x8 *>(rrow + kc * kTileK + 32 * d);
-    }
-  }
-
-  // 4. the first PD weight tiles; tile f = t * CPW + w (k tile t, column
-  //    tile w) is issued PD tiles before it is contracted.  Tiles past the
-  //    slice or past N re-read a valid tile.
-  u32x4 wv[NW][NTILE];
-  auto issue_tile = [&](int f) __attribute__((always_inline)) {
-    const int t = f / CPW, w = f % CPW;
-    const int kc = min(my_kb + min(t, max(my_n - 1, 0)), KC - 1);
-    const size_t tile = (size_t)min(ct0 + w, NTL - 1) * KC + kc;
-#pragma unroll
-    for (int i = 0; i < NW; ++i)
-      wv[i][f] = load_weights(p.w[i] + tile * kTileBytes, lane);
-  };
-#pragma unroll
-  for (int f = 0; f < PDE; ++f) issue_tile(f);
-
-  // 5. this wavefront's copies into its region have landed (completion is
-  //    in issue order); no other wavefront reads the region before the end
-  wait_vmcnt<(AFTER_COPIES < 63 ? AFTER_COPIES : 63)>();
-  read_slots();
-
-  // 6. RMSNorm prologue on the fragments: with a residual, s = A + resid
-  //    rounded once to fp16 (the workgroups of column block 0 write s out,
-  //    each (row, k) once); then the per-lane sum of squares (row l%16, this
-  //    lane's k slots; fp16 products are exact in fp32) and x * gamma rounded
-  //    once to fp16 (the packed multiply rounds the exact product once).
-  //    The factor 1/sqrt(mean + eps) is applied in the epilogue.
-  float ss = 0.f;
-  if (has_res) {
-#pragma unroll
-    for (int t = 0; t < KPW; ++t)
-#pragma unroll
-      for (int d = 0; d < 4; ++d) a[t][d][0] = a[t][d][0] + rr[t][d];
-  }
-  zero_tail();
-  if (has_res && p.resid_out != nullptr && blockIdx.x == 0 && c < mrows) {
-    f16 *orow = p.resid_out + (size_t)(m0 + c) * p.K + 8 * kq;
-#pragma unroll
-    for (int t = 0; t < KPW; ++t)
-      if (t < my_n)
-#pragma unroll
-        for (int d = 0; d < 4; ++d)
-          *reinterpret_cast<f16x8 *>(orow + (my_kb + t) * kTileK + 32 * d) = a[t][d][0];
-  }
-  if (rms) {
-#pragma unroll
-    for (int t = 0; t < KPW; ++t)
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const f16x8 x = a[t][d][0];
-#pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          const f16x2 x2 = {x[2 * h], x[2 * h + 1]};
-          ss = __builtin_amdgcn_fdot2(x2, x2, ss, false);
-        }
-        a[t][d][0] = x * *reinterpret_cast<const f16x8 *>(mg + (t * kTileK + 32 * d + 8 * kq) * 2);
-      }
-  }
-
-  // 7. contraction, k tile outer, column tile inner.  The codes enter the
-  //    matrix core bare (q * 2^-24); the activation slots facing 16q codes
-  //    are pre-scaled by 1/16, and each k tile's group row sums serve its
-  //    CPW column tiles for the zero-point term.
-#pragma unroll
-  for (int t = 0; t < KPW; ++t)
-#pragma unroll
-    for (int d = 0; d < 4; ++d) a[t][d][0] = prescale_frag(a[t][d][0]);
-  f32x4 acc[NW][CPW][1];
-#pragma unroll
-  for (int i = 0; i < NW; ++i)
-#pragma unroll
-    for (int w = 0; w < CPW; ++w) acc[i][w][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int zshift = 4 * (c & 1);
-  f32x4 ug[GPC];
-#pragma unroll
-  for (int f = 0; f < NTILE; ++f) {
-    if (f + PDE < NTILE) issue_tile(f + PDE);
-    const int t = f / CPW, w = f % CPW;
-    f16x8 at[4];
-#pragma unroll
-    for (int d = 0; d < 4; ++d) at[d] = a[t][d][0];
-    if (w == 0) group_row_sums<G>(ug, at, kq);
-    const int gi0 = (w * KPW + t) * GPC;  // first group of the tile in the region
-#pragma unroll
-    for (int i = 0; i < NW; ++i) {
-      const uint8_t *st = ms + i * MS_BYTES + (gi0 * 16 + c) * SB;
-      const uint8_t *zt = mz + i * MZ_PAD + gi0 * 8 + (c >> 1);
-      contract_tile_sub<G>(
-          acc[i][w][0], wv[i][f], at, ug, kq,
-          [&](int gl) __attribute__((always_inline)) { return (zt[gl * 8] >> zshift) & 15; },
-          [&](int gl) __attribute__((always_inline)) {
-            if constexpr (SF32)
-              return *reinterpret_cast<const float *>(st + gl * 16 * SB);
-            else
-              return (float)*reinterpret_cast<const f16 *>(st + gl * 16 * SB);
-          });
-    }
-  }
-
-  // 8. slice partial sums into the wavefront's own region ([i][w][lane],
-  //    16 bytes per lane), row sums of squares of the slice; one barrier;
-  //    wavefront w < CPW then sums column tile w over the slices in order
-  f32x4 *red = reinterpret_cast<f32x4 *>(region);
-#pragma unroll
-  for (int i = 0; i < NW; ++i)
-#pragma unroll
-    for (int w = 0; w < CPW; ++w) red[(i * CPW + w) * 64 + lane] = acc[i][w][0];
-  if (rms) {
-    // row l%16's k slots of this slice are spread over lanes l%16 + 16j
-    ss += __shfl_xor(ss, 16);
-    ss += __shfl_xor(ss, 32);
-    if (lane < 16) lRms[wk * 16 + lane] = ss;
-  }
-  lds_barrier();
-  const int wfin = wk;  // the column tile this wavefront finishes (if < CPW)
-  if (wfin >= CPW || ct0 + wfin >= NTL) return;
-  f32x4 fin[NW];
-#pragma unroll
-  for (int i = 0; i < NW; ++i) {
-    f32x4 v = {0.f, 0.f, 0.f, 0.f};
-    for (int w2 = 0; w2 < NWK; ++w2)
-      v += reinterpret_cast<const f32x4 *>(smem + w2 * p.lds_s)[(i * CPW + wfin) * 64 + lane];
-    fin[i] = v;
-  }
-  // sums of squares of this lane's output rows 4*(l/16) + e
-  f32x4 rs = {0.f, 0.f, 0.f, 0.f};
-  if (rms)
-    for (int w2 = 0; w2 < NWK; ++w2) rs += reinterpret_cast<const f32x4 *>(lRms + w2 * 16)[kq];
-  const int ncol = (ct0 + wfin) * kTileN + c;
-
-  // 9. k splits across workgroups (narrow grids and very deep k only): the
-  //    finishing wavefronts store partials; the finishing wavefront of the
-  //    last workgroup to arrive (counted per column tile) sums them in split
-  //    order.  Partials, sums of squares and counters are agent-scope atomic
-  //    accesses, coherent across the XCDs' separate L2 caches by themselves;
-  //    the only ordering needed is that a wavefront's partial stores have
-  //    completed before its arrival is counted (a wait on its own stores),
-  //    and the last arrival reads them only after its count returned.  A
-  //    device-wide fence instead would write back and invalidate the whole
-  //    L2 of the XCD once per finishing wavefront.
-  if (S > 1) {
-    const size_t cnt = (size_t)blockIdx.z * NTL + ct0 + wfin;  // per column tile
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int row = 4 * kq + e;
-      if (row < mrows) {
-#pragma unroll
-        for (int i = 0; i < NW; ++i)
-          store_agent(&p.ws_part[(((size_t)s * NW + i) * p.M + m0 + row) * p.N + ncol], fin[i][e]);
-        if (rms && c == 0) store_agent(&p.ws_rms[(cnt * S + s) * 16 + row], rs[e]);
-      }
-    }
-    wait_stores();
-    int last = 0;
-    if (lane == 0) last = count_arrival(&p.ws_cnt[cnt]) == (unsigned)(S - 1);
-    last = __shfl(last, 0);
-    if (!last) return;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int row = 4 * kq + e;
-      if (row < mrows) {
-#pragma unroll
-        for (int i = 0; i < NW; ++i) {
-          float v = 0.f;
-          for (int s2 = 0; s2 < S; ++s2)
-            v += (s2 == s) ? fin[i][e]
-                           : load_agent(&p.ws_part[(((size_t)s2 * NW + i) * p.M + m0 + row) * p.N + ncol]);
-          fin[i][e] = v;
-        }
-        if (rms) {
-          float v = 0.f;
-          for (int s2 = 0; s2 < S; ++s2)
-            v += (s2 == s) ? rs[e] : load_agent(&p.ws_rms[(cnt * S + s2) * 16 + row]);
-          rs[e] = v;
-        }
-      }
-    }
-    if (lane == 0) reset_arrival(&p.ws_cnt[cnt]);
-  }
-
-  // 10. epilogue, one fp16 write per output
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int row = 4 * kq + e;
-    if (row < mrows) {
-      float rsc = 1.0f;
-      if (rms) rsc = 1.0f / sqrtf(rs[e] / (float)p.K + p.eps);
-      else if (p.row_ss != nullptr)  // rows staged by stage.hip
-        rsc = 1.0f / sqrtf(p.row_ss[m0 + row] / (float)p.K + p.eps);
-      float y;
-      if constexpr (GU) {
-        y = silu(fin[0][e] * rsc) * (fin[1][e] * rsc);
-      } else {
-        y = fin[0][e] * rsc;
-        if (p.epilogue != 0) y += (float)p.bias[ncol];
-        if (p.epilogue == 2) y = y > 0.f ? y : 0.f;
-      }
-      p.out[(size_t)(m0 + row) * p.N + ncol] = (f16)y;
-    }
-  }
-}
-
-template <int CPW, int KPW, int NWK, int PD, bool ALDS, int G, bool SF32, bool GU>
-hipError_t launch_t(const GemmArgs &a, const Plan &pl, hipStream_t stream) {
-  auto kern = stream_kernel<CPW, KPW, NWK, PD, ALDS, G, SF32, GU>;
-  // Raise the kernel's dynamic-LDS limit when a plan needs more than the
-  // default 64 KiB; only the first launch that needs a larger size makes the
-  // attribute call, so repeated launches (also under stream capture) make none.
-  static size_t lds_limit = 64 * 1024;
-  if (pl.lds_bytes > lds_limit) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)pl.lds_bytes);
-    if (e != hipSuccess) {
-      (void)hipGetLastError();  // leave no sticky error for the caller's next launch
-      return e;
-    }
-    lds_limit = pl.lds_bytes;
-  }
-  hipLaunchKernelGGL(kern, dim3(pl.gx, pl.gy, pl.gz), dim3(64 * NWK), pl.lds_bytes, stream, a);
-  return hipGetLastError();
-}
-
-template <int CPW, int KPW, int NWK, int PD, bool ALDS, int G>
-hipError_t launch_g(const GemmArgs &a, const Plan &pl, bool sf32, bool gu, hipStream_t st) {
-  if (sf32) return gu ? launch_t<CPW, KPW, NWK, PD, ALDS, G, true, true>(a, pl, st)
-                      : launch_t<CPW, KPW, NWK, PD, ALDS, G, true, false>(a, pl, st);
-  return gu ? launch_t<CPW, KPW, NWK, PD, ALDS, G, false, true>(a, pl, st)
-            : launch_t<CPW, KPW, NWK, PD, ALDS, G, false, false>(a, pl, st);
-}
-
-template <int CPW, int KPW, int NWK, int PD, int G>
-hipError_t launch_a(const GemmArgs &a, const Plan &pl, bool sf32, bool gu, hipStream_t st) {
-  return pl.alds ? launch_g<CPW, KPW, NWK, PD, true, G>(a, pl, sf32, gu, st)
-                 : launch_g<CPW, KPW, NWK, PD, false, G>(a, pl, sf32, gu, st);
-}
-
-template <int CPW, int KPW, int NWK, int PD>
-hipError_t launch_c(const GemmArgs &a, const Plan &pl, int group, bool sf32, bool gu,
-                    hipStream_t st) {
-  switch (group) {
-    case 16: return launch_a<CPW, KPW, NWK, PD, 16>(a, pl, sf32, gu, st);
-    case 32: return launch_a<CPW, KPW, NWK, PD, 32>(a, pl, sf32, gu, st);
-    case 64: return launch_a<CPW, KPW, NWK, PD, 64>(a, pl, sf32, gu, st);
-    default: return launch_a<CPW, KPW, NWK, PD, 128>(a, pl, sf32, gu, st);
-  }
-}
-
-}  // namespace
-
-// (CPW, KPW, NWK, PD) of each configuration, in plan order: the planner
-// takes the first one whose grid reaches 200 workgroups.
-#define W4A16_STREAM_CFGS(X) \
-  X(4, 5, 8, 8)   /* 4 column tiles x 8 slices of 5 k tiles (K <= 5120) */ \
-  X(2, 5, 8, 6)   /* 2 column tiles, for narrower N */                     \
-  X(1, 5, 8, 4)   /* 1 column tile, for narrow N */
 
 const StreamCfg kStreamCfgs[kNumStreamCfgs] = {
 #define W4A16_CFG_ROW(cpw, kpw, nwk, pd) {cpw, kpw, nwk, pd},
@@ -480,12 +14,8 @@ const StreamCfg kStreamCfgs[kNumStreamCfgs] = {
 
 hipError_t launch_stream(const GemmArgs &a, const Plan &pl, int group, bool scale_f32,
                          bool gate_up, hipStream_t stream) {
-  int i = 0;
-#define W4A16_CFG_CASE(cpw, kpw, nwk, pd) \
-  if (pl.cfg == i++) return launch_c<cpw, kpw, nwk, pd>(a, pl, group, scale_f32, gate_up, stream);
-  W4A16_STREAM_CFGS(W4A16_CFG_CASE)
-#undef W4A16_CFG_CASE
-  return hipErrorInvalidValue;
+  if (a.gamma != nullptr) return launch_stream_rms(a, pl, group, scale_f32, gate_up, stream);
+  return launch_stream_cfg<false>(a, pl, group, scale_f32, gate_up, stream);
 }
 
 }  // namespace w4a16

@@ -74,8 +74,11 @@ constexpr int tile_stages(int ct, int group, int sb, int nw) {
   return tile_lds(4, ct, group, sb, nw) <= kLdsMax ? 4 : tile_lds(3, ct, group, sb, nw) <= kLdsMax ? 3 : 2;
 }
 
+// (occupancy: one workgroup of kTileNWave wavefronts per compute unit, which
+// its LDS stages allow anyway)
 template <int CT, int G, bool SF32, bool GU>
 __global__ void __launch_bounds__(64 * kTileNWave)
+    __attribute__((amdgpu_waves_per_eu(kTileNWave / 4, kTileNWave / 4)))
 tile_kernel(const GemmArgs p) {
   constexpr int MT = kTileMT;
   constexpr int NWC = kTileNWC;
