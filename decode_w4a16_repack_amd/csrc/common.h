@@ -127,9 +127,12 @@ Plan make_plan(int M, int K, int N, int group, int scale_bytes, bool gate_up,
 
 hipError_t launch_stream(const GemmArgs &a, const Plan &p, int group, bool scale_f32,
                          bool gate_up, hipStream_t stream);
-// stream_rms.hip: the streaming kernel with the in-register RMSNorm prologue
+// stream_rms.hip / stream_skip.hip: the streaming kernel with the in-register
+// RMSNorm / skip + RMSNorm prologue
 hipError_t launch_stream_rms(const GemmArgs &a, const Plan &p, int group, bool scale_f32,
                              bool gate_up, hipStream_t stream);
+hipError_t launch_stream_skip(const GemmArgs &a, const Plan &p, int group, bool scale_f32,
+                              bool gate_up, hipStream_t stream);
 
 hipError_t launch_panel(const GemmArgs &a, const Plan &p, int group, bool scale_f32,
                         bool gate_up, hipStream_t stream);

@@ -14,8 +14,10 @@ const StreamCfg kStreamCfgs[kNumStreamCfgs] = {
 
 hipError_t launch_stream(const GemmArgs &a, const Plan &pl, int group, bool scale_f32,
                          bool gate_up, hipStream_t stream) {
-  if (a.gamma != nullptr) return launch_stream_rms(a, pl, group, scale_f32, gate_up, stream);
-  return launch_stream_cfg<false>(a, pl, group, scale_f32, gate_up, stream);
+  if (a.gamma != nullptr)
+    return a.resid != nullptr ? launch_stream_skip(a, pl, group, scale_f32, gate_up, stream)
+                              : launch_stream_rms(a, pl, group, scale_f32, gate_up, stream);
+  return launch_stream_cfg<0>(a, pl, group, scale_f32, gate_up, stream);
 }
 
 }  // namespace w4a16

@@ -50,7 +50,8 @@ namespace {
 // this loop nor the plan allow; so the compiler is told that NWK / 4 is the
 // occupancy, and spends the registers a higher target would have reserved
 // on keeping more loads in flight (M=1: 8.9 -> 8.3 us).
-template <int CPW, int KPW, int NWK, int PD, bool ALDS, int G, bool SF32, bool GU, bool RMS>
+// RMS: 0 no prologue, 1 RMSNorm of A, 2 RMSNorm of A + residual.
+template <int CPW, int KPW, int NWK, int PD, bool ALDS, int G, bool SF32, bool GU, int RMS>
 __global__ void __launch_bounds__(64 * NWK) __attribute__((amdgpu_waves_per_eu(NWK / 4, NWK / 4)))
 stream_kernel(const GemmArgs p) {
   static_assert(CPW <= NWK, "one finishing wavefront per column tile");
@@ -67,10 +68,17 @@ stream_kernel(const GemmArgs p) {
   constexpr int MZ_PAD = (MZ_BYTES + 15) / 16 * 16;
   constexpr int SU = GPW * SB;                   // 16-byte scale units per column tile
   constexpr int ZU = GPW * 2;                    // 4-byte zero-point units per column tile
+  constexpr bool RES = RMS == 2;  // residual added before the norm
+  // k tiles whose activation fragments are loaded with the first PDE weight
+  // tiles (each k tile's just before its first weight tile)
+  constexpr int A_EARLY = (PDE - 1) / CPW + 1 < KPW ? (PDE - 1) / CPW + 1 : KPW;
+  // (the skip prologue loads the whole slice before the weights: more loads
+  // after the copies than counted here, which only makes the wait stricter)
   // loads issued after the direct-to-LDS copies that may still be in
-  // flight when the copies are waited for: the register activation
-  // fragments (unless they come through LDS) and the first PD tiles
-  constexpr int AFTER_COPIES = (ALDS ? 0 : 4 * KPW) + PDE * NW;
+  // flight when the copies are waited for (at least): the register
+  // activation fragments of the first k tiles (unless they come through
+  // LDS) and the first PDE tiles
+  constexpr int AFTER_COPIES = (ALDS ? 0 : 4 * A_EARLY) + PDE * NW;
 
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
@@ -91,7 +99,7 @@ stream_kernel(const GemmArgs p) {
   const int my_n = max(0, min(KPW, nkc - wk * KPW));  // valid k tiles of this slice
   // the RMSNorm prologue is its own instantiation, so the plain kernel holds
   // none of its registers
-  constexpr bool rms = RMS;
+  constexpr bool rms = RMS != 0;
   const bool has_zp = p.has_zp != 0;
   const int kq = lane >> 4;
   const int c = lane & 15;
@@ -146,7 +154,7 @@ stream_kernel(const GemmArgs p) {
     }
   }
 
-  if constexpr (RMS) {
+  if constexpr (rms) {
     // the slice's gamma (positions past the slice copy a valid tile): read
     // back from LDS by the prologue, so it holds no registers while the
     // activations, the residual and the first weight tiles are in flight
@@ -182,59 +190,47 @@ stream_kernel(const GemmArgs p) {
         copy16_to_lds(src, aslots + q * 1024);
       }
     }
-  } else {
-    const f16 *arow_p = p.A + (size_t)(m0 + arow) * p.K + 8 * kq;
+  }
+  // activation fragment (t, d) from the slots (ALDS), once the copies landed
+  const uint8_t *aslot_p = aslots + (kq * R + arow) * 16;
+  auto read_slot = [&](int t, int d) __attribute__((always_inline)) {
+    return *reinterpret_cast<const f16x8 *>(aslot_p + (t * 4 + d) * 64 * R);
+  };
+  // Otherwise the fragments of k tile t are loaded just before the first
+  // weight tile of t: loads complete in issue order, so a slice loaded up
+  // front made the first tile wait for all of it.  The skip prologue (at most
+  // 4 rows) loads the slice and its residual up front and adds them before
+  // the loop: a conditional store of the sum inside the loop would split it
+  // into branches and spill.
+  const f16 *arow_p = p.A + (size_t)(m0 + arow) * p.K + 8 * kq;
+  auto load_a = [&](int t) __attribute__((always_inline)) {
+    const int kc = min(my_kb + min(t, max(my_n - 1, 0)), KC - 1);
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+      a[t][d][0] = *reinterpret_cast<const f16x8 *>(arow_p + kc * kTileK + 32 * d);
+  };
+  constexpr bool A_PROGRESSIVE = !ALDS && !RES;
+  f16x8 rr[RES ? KPW : 1][4];
+  if constexpr (RES) {
+    const f16 *rrow_p = p.resid + (size_t)(m0 + arow) * p.K + 8 * kq;
 #pragma unroll
     for (int t = 0; t < KPW; ++t) {
+      if constexpr (!ALDS) load_a(t);
       const int kc = min(my_kb + min(t, max(my_n - 1, 0)), KC - 1);
 #pragma unroll
       for (int d = 0; d < 4; ++d)
-        a[t][d][0] = *reinterpret_cast<const f16x8 *>(arow_p + kc * kTileK + 32 * d);
-    }
-  }
-  // activation fragments from the slots (ALDS), once the copies landed
-  auto read_slots = [&]() __attribute__((always_inline)) {
-    if constexpr (ALDS) {
-      const uint8_t *ap = aslots + (kq * R + arow) * 16;
-#pragma unroll
-      for (int t = 0; t < KPW; ++t)
-#pragma unroll
-        for (int d = 0; d < 4; ++d)
-          a[t][d][0] = *reinterpret_cast<const f16x8 *>(ap + (t * 4 + d) * 64 * R);
-    }
-  };
-  auto zero_tail = [&]() __attribute__((always_inline)) {
-    if (my_n < KPW) {
-#pragma unroll
-      for (int t = 0; t < KPW; ++t)
-        if (t >= my_n)
-#pragma unroll
-          for (int d = 0; d < 4; ++d) a[t][d][0] = f16x8{};
-    }
-  };
-
-  // 3. skip + RMSNorm: the residual fragments of the slice, issued with the
-  //    activations so that one wait covers both (the first weight tiles,
-  //    issued next, stay in flight)
-  const bool has_res = RMS && p.resid != nullptr;
-  f16x8 rr[RMS ? KPW : 1][4];
-  if (has_res) {
-    const f16 *rrow = p.resid + (size_t)(m0 + arow) * p.K + 8 * kq;
-#pragma unroll
-    for (int t = 0; t < (RMS ? KPW : 0); ++t) {
-      const int kc = min(my_kb + min(t, max(my_n - 1, 0)), KC - 1);
-#pragma unroll
-      for (int d = 0; d < 4; ++d)
-        rr[t][d] = *reinterpret_cast<const f16x8 *>(rrow + kc * kTileK + 32 * d);
+        rr[t][d] = *reinterpret_cast<const f16x8 *>(rrow_p + kc * kTileK + 32 * d);
     }
   }
 
-  // 4. the first PD weight tiles; tile f = t * CPW + w (k tile t, column
-  //    tile w) is issued PD tiles before it is contracted.  Tiles past the
-  //    slice or past N re-read a valid tile.
+  // 3. weight tiles; tile f = t * CPW + w (k tile t, column tile w) is issued
+  //    PDE tiles before it is contracted, the activations of k tile t just
+  //    before tile (t, 0).  Tiles past the slice or past N re-read a valid
+  //    tile.
   u32x4 wv[NW][NTILE];
   auto issue_tile = [&](int f) __attribute__((always_inline)) {
     const int t = f / CPW, w = f % CPW;
+    if (A_PROGRESSIVE && w == 0) load_a(t);
     const int kc = min(my_kb + min(t, max(my_n - 1, 0)), KC - 1);
     const size_t tile = (size_t)min(ct0 + w, NTL - 1) * KC + kc;
 #pragma unroll
@@ -244,57 +240,87 @@ stream_kernel(const GemmArgs p) {
 #pragma unroll
   for (int f = 0; f < PDE; ++f) issue_tile(f);
 
-  // 5. this wavefront's copies into its region have landed (completion is
+  // 4. this wavefront's copies into its region have landed (completion is
   //    in issue order); no other wavefront reads the region before the end
   wait_vmcnt<(AFTER_COPIES < 63 ? AFTER_COPIES : 63)>();
-  read_slots();
+  if constexpr (RES) {
+    // s = A + resid rounded once to fp16; the workgroups of column block 0
+    // write s out, each (row, k) once
+    const bool write_res = p.resid_out != nullptr && blockIdx.x == 0 && c < mrows;
+#pragma unroll
+    for (int t = 0; t < KPW; ++t)
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+        a[t][d][0] = (ALDS ? read_slot(t, d) : a[t][d][0]) + rr[t][d];
+    if (write_res) {
+      f16 *orow = p.resid_out + (size_t)(m0 + c) * p.K + 8 * kq;
+#pragma unroll
+      for (int t = 0; t < KPW; ++t)
+        if (t < my_n)
+#pragma unroll
+          for (int d = 0; d < 4; ++d)
+            *reinterpret_cast<f16x8 *>(orow + (my_kb + t) * kTileK + 32 * d) = a[t][d][0];
+    }
+  }
 
-  // 6. RMSNorm prologue on the fragments: with a residual, s = A + resid
-  //    rounded once to fp16 (the workgroups of column block 0 write s out,
-  //    each (row, k) once); then the per-lane sum of squares (row l%16, this
-  //    lane's k slots; fp16 products are exact in fp32) and x * gamma rounded
-  //    once to fp16 (the packed multiply rounds the exact product once).
-  //    The factor 1/sqrt(mean + eps) is applied in the epilogue.
+  // 5. each k tile's fragments are prepared at their first use: k tiles past
+  //    the slice are zeroed; with the RMSNorm prologue the per-lane sum of
+  //    squares (row l%16, this lane's k slots; fp16 products are exact in
+  //    fp32) and x * gamma rounded once to fp16 (the packed multiply rounds
+  //    the exact product once), 1/sqrt(mean + eps) following in the
+  //    epilogue; then the 1/16 pre-scale of the slots facing high nibbles.
   float ss = 0.f;
-  if (has_res) {
+  auto prep_tile = [&](int t, const f16x8 (&src)[4], f16x8 (&at)[4]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int t = 0; t < (RMS ? KPW : 0); ++t)
-#pragma unroll
-      for (int d = 0; d < 4; ++d) a[t][d][0] = a[t][d][0] + rr[t][d];
-  }
-  zero_tail();
-  if (has_res && p.resid_out != nullptr && blockIdx.x == 0 && c < mrows) {
-    f16 *orow = p.resid_out + (size_t)(m0 + c) * p.K + 8 * kq;
-#pragma unroll
-    for (int t = 0; t < KPW; ++t)
-      if (t < my_n)
-#pragma unroll
-        for (int d = 0; d < 4; ++d)
-          *reinterpret_cast<f16x8 *>(orow + (my_kb + t) * kTileK + 32 * d) = a[t][d][0];
-  }
-  if constexpr (RMS) {
-#pragma unroll
-    for (int t = 0; t < KPW; ++t)
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const f16x8 x = a[t][d][0];
+    for (int d = 0; d < 4; ++d) {
+      f16x8 x = src[d];
+      if constexpr (rms) {
 #pragma unroll
         for (int h = 0; h < 4; ++h) {
           const f16x2 x2 = {x[2 * h], x[2 * h + 1]};
           ss = __builtin_amdgcn_fdot2(x2, x2, ss, false);
         }
-        a[t][d][0] = x * *reinterpret_cast<const f16x8 *>(mg + (t * kTileK + 32 * d + 8 * kq) * 2);
+        x = x * *reinterpret_cast<const f16x8 *>(mg + (t * kTileK + 32 * d + 8 * kq) * 2);
       }
+      at[d] = prescale_frag(x);
+    }
+  };
+  // From LDS (M <= 8) the fragments are ready with the copies, and the whole
+  // slice is prepared before the loop (measured faster: nothing waits for
+  // them, and the loop keeps only weight work between its MFMAs); fragments
+  // loaded from memory are prepared at their first use.
+  //    (k tiles past the slice: zeroed by one uniform branch when the slice
+  //    has any, ahead of the loop; per element at first use otherwise)
+  constexpr bool PREP_AHEAD = ALDS;
+  if constexpr (PREP_AHEAD) {
+    if constexpr (!RES) {
+#pragma unroll
+      for (int t = 0; t < KPW; ++t)
+#pragma unroll
+        for (int d = 0; d < 4; ++d) a[t][d][0] = read_slot(t, d);
+    }
+    if (my_n < KPW) {
+#pragma unroll
+      for (int t = 0; t < KPW; ++t)
+        if (t >= my_n)
+#pragma unroll
+          for (int d = 0; d < 4; ++d) a[t][d][0] = f16x8{};
+    }
+#pragma unroll
+    for (int t = 0; t < KPW; ++t) {
+      f16x8 src[4], at0[4];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) src[d] = a[t][d][0];
+      prep_tile(t, src, at0);
+#pragma unroll
+      for (int d = 0; d < 4; ++d) a[t][d][0] = at0[d];
+    }
   }
 
-  // 7. contraction, k tile outer, column tile inner.  The codes enter the
+  // 6. contraction, k tile outer, column tile inner.  The codes enter the
   //    matrix core bare (q * 2^-24); the activation slots facing 16q codes
   //    are pre-scaled by 1/16, and each k tile's group row sums serve its
   //    CPW column tiles for the zero-point term.
-#pragma unroll
-  for (int t = 0; t < KPW; ++t)
-#pragma unroll
-    for (int d = 0; d < 4; ++d) a[t][d][0] = prescale_frag(a[t][d][0]);
   f32x4 acc[NW][CPW][1];
 #pragma unroll
   for (int i = 0; i < NW; ++i)
@@ -302,14 +328,23 @@ stream_kernel(const GemmArgs p) {
     for (int w = 0; w < CPW; ++w) acc[i][w][0] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int zshift = 4 * (c & 1);
   f32x4 ug[GPC];
+  f16x8 at[4];
 #pragma unroll
   for (int f = 0; f < NTILE; ++f) {
     if (f + PDE < NTILE) issue_tile(f + PDE);
     const int t = f / CPW, w = f % CPW;
-    f16x8 at[4];
+    if (w == 0) {
+      if constexpr (PREP_AHEAD) {
 #pragma unroll
-    for (int d = 0; d < 4; ++d) at[d] = a[t][d][0];
-    if (w == 0) group_row_sums<G>(ug, at, kq);
+        for (int d = 0; d < 4; ++d) at[d] = a[t][d][0];
+      } else {
+        f16x8 src[4];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) src[d] = t < my_n ? a[t][d][0] : f16x8{};
+        prep_tile(t, src, at);
+      }
+      group_row_sums<G>(ug, at, kq);
+    }
     const int gi0 = (w * KPW + t) * GPC;  // first group of the tile in the region
 #pragma unroll
     for (int i = 0; i < NW; ++i) {
@@ -327,7 +362,7 @@ stream_kernel(const GemmArgs p) {
     }
   }
 
-  // 8. slice partial sums into the wavefront's own region ([i][w][lane],
+  // 7. slice partial sums into the wavefront's own region ([i][w][lane],
   //    16 bytes per lane), row sums of squares of the slice; one barrier;
   //    wavefront w < CPW then sums column tile w over the slices in order
   f32x4 *red = reinterpret_cast<f32x4 *>(region);
@@ -358,7 +393,7 @@ stream_kernel(const GemmArgs p) {
     for (int w2 = 0; w2 < NWK; ++w2) rs += reinterpret_cast<const f32x4 *>(lRms + w2 * 16)[kq];
   const int ncol = (ct0 + wfin) * kTileN + c;
 
-  // 9. k splits across workgroups (narrow grids and very deep k only): the
+  // 8. k splits across workgroups (narrow grids and very deep k only): the
   //    finishing wavefronts store partials; the finishing wavefront of the
   //    last workgroup to arrive (counted per column tile) sums them in split
   //    order.  Partials, sums of squares and counters are agent-scope atomic
@@ -408,7 +443,7 @@ stream_kernel(const GemmArgs p) {
     if (lane == 0) reset_arrival(&p.ws_cnt[cnt]);
   }
 
-  // 10. epilogue, one fp16 write per output
+  // 9. epilogue, one fp16 write per output
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int row = 4 * kq + e;
@@ -430,7 +465,7 @@ stream_kernel(const GemmArgs p) {
   }
 }
 
-template <int CPW, int KPW, int NWK, int PD, bool ALDS, int G, bool SF32, bool GU, bool RMS>
+template <int CPW, int KPW, int NWK, int PD, bool ALDS, int G, bool SF32, bool GU, int RMS>
 hipError_t launch_t(const GemmArgs &a, const Plan &pl, hipStream_t stream) {
   auto kern = stream_kernel<CPW, KPW, NWK, PD, ALDS, G, SF32, GU, RMS>;
   // Raise the kernel's dynamic-LDS limit when a plan needs more than the
@@ -451,7 +486,7 @@ hipError_t launch_t(const GemmArgs &a, const Plan &pl, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int CPW, int KPW, int NWK, int PD, bool ALDS, int G, bool RMS>
+template <int CPW, int KPW, int NWK, int PD, bool ALDS, int G, int RMS>
 hipError_t launch_g(const GemmArgs &a, const Plan &pl, bool sf32, bool gu, hipStream_t st) {
   if (sf32) return gu ? launch_t<CPW, KPW, NWK, PD, ALDS, G, true, true, RMS>(a, pl, st)
                       : launch_t<CPW, KPW, NWK, PD, ALDS, G, true, false, RMS>(a, pl, st);
@@ -459,13 +494,13 @@ hipError_t launch_g(const GemmArgs &a, const Plan &pl, bool sf32, bool gu, hipSt
             : launch_t<CPW, KPW, NWK, PD, ALDS, G, false, false, RMS>(a, pl, st);
 }
 
-template <int CPW, int KPW, int NWK, int PD, int G, bool RMS>
+template <int CPW, int KPW, int NWK, int PD, int G, int RMS>
 hipError_t launch_a(const GemmArgs &a, const Plan &pl, bool sf32, bool gu, hipStream_t st) {
   return pl.alds ? launch_g<CPW, KPW, NWK, PD, true, G, RMS>(a, pl, sf32, gu, st)
                  : launch_g<CPW, KPW, NWK, PD, false, G, RMS>(a, pl, sf32, gu, st);
 }
 
-template <int CPW, int KPW, int NWK, int PD, bool RMS>
+template <int CPW, int KPW, int NWK, int PD, int RMS>
 hipError_t launch_c(const GemmArgs &a, const Plan &pl, int group, bool sf32, bool gu,
                     hipStream_t st) {
   switch (group) {
@@ -484,8 +519,8 @@ hipError_t launch_c(const GemmArgs &a, const Plan &pl, int group, bool sf32, boo
   X(2, 5, 8, 6)   /* 2 column tiles, for narrower N */                     \
   X(1, 5, 8, 4)   /* 1 column tile, for narrow N */
 
-// Launch the configuration the plan names, with or without the prologue.
-template <bool RMS>
+// Launch the configuration the plan names with prologue mode RMS.
+template <int RMS>
 hipError_t launch_stream_cfg(const GemmArgs &a, const Plan &pl, int group, bool scale_f32,
                              bool gate_up, hipStream_t stream) {
   int i = 0;
