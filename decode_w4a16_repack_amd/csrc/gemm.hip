@@ -39,7 +39,7 @@ int choose_split(int base, int KC, int force_split) {
 // the grid at >= 200 workgroups; k split across workgroups only when the k
 // range exceeds the workgroup's NWK x KPW tiles or the grid is short of
 // wavefronts.  Each wavefront has a private LDS region: its slice's scales
-// and zero-points, for M <= 8 its activation rows, and at the end its
+// and zero-points, for M <= 4 its activation rows, and at the end its
 // partial sums.
 bool plan_stream(Plan &p, int M, int K, int N, int group, int scale_bytes, bool gate_up,
                  int force_cfg, int force_split) {
@@ -109,7 +109,11 @@ bool plan_stream(Plan &p, int M, int K, int N, int group, int scale_bytes, bool 
   const size_t limit = 160 * 1024;
   p.alds = 0;
   size_t region = align16(meta > red ? meta : red);
-  if (M <= 8) {
+  // activation rows through LDS (unique rows, read back as fragments) up to 4
+  // rows; above that each k tile's fragments are loaded straight into
+  // registers just before its first weight tile, which measured faster
+  // (M=8: 10.6 -> 9.9 us; M=3: 9.1 against 9.5 us the other way)
+  if (M <= 4) {
     const size_t with_a = align16(meta + a_lds > red ? meta + a_lds : red);
     if ((size_t)c.nwk * with_a + (size_t)c.nwk * 64 <= limit) {
       p.alds = 1;

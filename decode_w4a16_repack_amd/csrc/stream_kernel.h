@@ -25,7 +25,7 @@
 //    and column tile inner so consecutive MFMA chains are independent;
 //  * each wavefront copies the scales and zero-points of its slice (runs of
 //    the packed layout) into a private LDS region with direct global-to-LDS
-//    loads, and for M <= 8 also its activation rows (unique data, then read
+//    loads, and for M <= 4 also its activation rows (unique data, then read
 //    back as fragments); nothing is shared between wavefronts until the
 //    final reduction, so the only barrier is the one before it;
 //  * the slice partial sums go through the same private regions; wavefront
@@ -285,7 +285,7 @@ stream_kernel(const GemmArgs p) {
       at[d] = prescale_frag(x);
     }
   };
-  // From LDS (M <= 8) the fragments are ready with the copies, and the whole
+  // From LDS (M <= 4) the fragments are ready with the copies, and the whole
   // slice is prepared before the loop (measured faster: nothing waits for
   // them, and the loop keeps only weight work between its MFMAs); fragments
   // loaded from memory are prepared at their first use.
