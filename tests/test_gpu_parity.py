@@ -72,7 +72,9 @@ def test_tiny_config_full_output():
     check_close(run_gemm(p), ref_gemm(p), "tiny")
 
 
-SMALL_M = [1, 2, 3, 7, 16, 17, 24, 32, 33, 64, 65, 128, 130]
+# (4 | 5: activation rows through LDS | loaded per k tile; 16 | 17 and 32 | 33:
+# the next kernel)
+SMALL_M = [1, 2, 3, 4, 5, 7, 8, 12, 16, 17, 24, 32, 33, 64, 65, 128, 130]
 
 
 @pytest.mark.parametrize("M", SMALL_M)
@@ -322,7 +324,8 @@ def test_gate_up_small_all_outputs(M, g, rms):
                                         (16, 1024, 512, 64, True), (20, 1152, 256, 64, False),
                                         (27, 1024, 256, 32, True),
                                         (64, 2048, 512, 16, False), (130, 1024, 256, 128, True),
-                                        (3, 1024, 256, 128, True)])
+                                        (3, 1024, 256, 128, True), (4, 1152, 256, 64, False),
+                                        (5, 1152, 256, 128, True), (12, 1024, 384, 32, False)])
 def test_skip_rmsnorm_prologue_all_outputs(M, K, N, g, gu):
     """X = RMSNorm(A + residual): every output against the oracle, and the
     residual sum written out bit-exactly (one fp16 rounding per element)."""
