@@ -444,11 +444,11 @@ def test_probes():
 # ------------------------------------------------------------ MLP chain
 
 
-def _mlp_case(M, H, I, g, seed, gamma=False, resid=False, asym=True):
+def _mlp_case(M, H, I, g, seed, gamma=False, resid=False, asym=True, sdt=F16):
     rng = np.random.default_rng(seed)
     A = rng.standard_normal((M, H)).astype(F16)
-    ws = [synth.draw_weight(rng, H, I, g, asym=asym), synth.draw_weight(rng, H, I, g, asym=asym),
-          synth.draw_weight(rng, I, H, g, asym=asym)]
+    ws = [synth.draw_weight(rng, H, I, g, sdt, asym), synth.draw_weight(rng, H, I, g, sdt, asym),
+          synth.draw_weight(rng, I, H, g, sdt, asym)]
     gm = rng.normal(1.0, 0.1, size=H).astype(F16) if gamma or resid else None
     R = rng.standard_normal((M, H)).astype(F16) if resid else None
     return A, ws, gm, R
@@ -460,16 +460,18 @@ def _mlp_ref(A, ws, gm, R, g, I, H, cols=None):
     return X, oracle.mlp(X, t[0], t[1], t[2], g, I, H, gamma=gm, cols=cols)
 
 
-@pytest.mark.parametrize("M,H,I,g,gamma,resid", [
-    (1, 512, 1024, 128, False, False), (8, 512, 1536, 64, True, False),
-    (13, 384, 768, 32, False, False), (24, 512, 1024, 128, True, True),
-    (64, 256, 512, 16, False, False), (129, 256, 384, 128, True, False),
-    (3, 1024, 256, 64, False, True)])
-def test_mlp_chain_all_outputs(M, H, I, g, gamma, resid):
+@pytest.mark.parametrize("M,H,I,g,gamma,resid,asym,sdt", [
+    (1, 512, 1024, 128, False, False, True, F16), (8, 512, 1536, 64, True, False, True, F16),
+    (13, 384, 768, 32, False, False, True, F16), (24, 512, 1024, 128, True, True, True, F16),
+    (64, 256, 512, 16, False, False, True, F16), (129, 256, 384, 128, True, False, True, F16),
+    (3, 1024, 256, 64, False, True, True, F16), (16, 512, 1024, 32, True, False, False, F32),
+    (40, 384, 768, 128, False, False, False, F32), (2, 256, 512, 16, True, True, True, F32)])
+def test_mlp_chain_all_outputs(M, H, I, g, gamma, resid, asym, sdt):
     """w4a16_mlp: the intermediate against the oracle's gate_up, the output
     against the oracle's chain (both every element), the residual sum
     bit-exact, and the output bit-identical to the two separate calls."""
-    A, ws, gm, R = _mlp_case(M, H, I, g, seed=M * 7 + I, gamma=gamma, resid=resid)
+    A, ws, gm, R = _mlp_case(M, H, I, g, seed=M * 7 + I, gamma=gamma, resid=resid, asym=asym,
+                             sdt=sdt)
     X, ref = _mlp_ref(A, ws, gm, R, g, I, H)
     pg, pu, pd = (repack_dev(w) for w in ws)
     Ad, gd, Rd = to_dev(A), to_dev(gm), to_dev(R)

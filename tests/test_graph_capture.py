@@ -54,6 +54,10 @@ CASES = [
     (130, 2048, 512, 128, "gemm"),
     (8, 1024, 256, 128, "gate_up"),       # split-K gate_up with RMSNorm
     (40, 1024, 256, 16, "gate_up"),
+    (32, 1024, 512, 64, "rms"),           # panel kernel on staged rows
+    (70, 1024, 256, 128, "skip"),         # tile kernel, staged skip + RMSNorm
+    (12, 1024, 384, 32, "skip"),          # stream kernel, staged skip + RMSNorm
+    (3, 1024, 384, 128, "skip"),          # stream kernel, skip + RMSNorm in registers
 ]
 
 
@@ -66,9 +70,13 @@ def test_graph_replay_is_bit_identical_to_eager(M, K, N, g, kind):
     ws = w4.Workspace()
     ws.get(8 << 20, "cuda")  # sized once: no reallocation can move it after capture
     out = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    R = to_dev(np.random.default_rng(M).standard_normal((M, K)).astype(np.float16))
+    S = torch.empty((M, K), dtype=torch.float16, device="cuda")
 
     def call():
-        if kind == "gate_up":
+        if kind == "skip":
+            w4.gemm(A, w, gamma=gm, residual=R, residual_out=S, out=out, workspace=ws)
+        elif kind == "gate_up":
             w4.gemm_gate_up(A, w, wu, gamma=gm, out=out, workspace=ws)
         elif kind == "rms":
             w4.gemm(A, w, gamma=gm, out=out, workspace=ws)
@@ -79,7 +87,7 @@ def test_graph_replay_is_bit_identical_to_eager(M, K, N, g, kind):
 
     call()
     torch.cuda.synchronize()
-    eager = out.clone()
+    eager, eager_s = out.clone(), S.clone()
     g_ = _capture(call)
     # other eager work on the same workspace between replays: a different
     # shape that also splits k (its counters share the workspace)
@@ -88,10 +96,47 @@ def test_graph_replay_is_bit_identical_to_eager(M, K, N, g, kind):
     ref_q = w4.gemm(Aq, wq, workspace=ws).clone()
     for r in range(4):
         out.fill_(float("nan"))
+        S.fill_(float("nan"))
         g_.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, eager), f"replay {r} differs from the eager call"
+        if kind == "skip":
+            assert torch.equal(S, eager_s), f"replay {r}: residual sum differs"
         assert torch.equal(w4.gemm(Aq, wq, workspace=ws), ref_q)
+        torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("M", [8, 24])
+def test_mlp_block_replay_is_bit_identical_to_eager(M):
+    """w4a16_mlp (gate_up with the RMSNorm prologue, staged at 24 rows, then
+    the down projection, split over k) captured and replayed: intermediate
+    and output equal the eager call every time."""
+    H, I, g = 512, 1536, 64
+    rng = np.random.default_rng(M)
+    ws_ = [synth.draw_weight(rng, H, I, g), synth.draw_weight(rng, H, I, g),
+           synth.draw_weight(rng, I, H, g)]
+    pw = [repack_dev(x) for x in ws_]
+    A = to_dev(rng.standard_normal((M, H)).astype(np.float16))
+    gm = to_dev(rng.normal(1.0, 0.1, size=H).astype(np.float16))
+    ws = w4.Workspace()
+    ws.get(8 << 20, "cuda")
+    inter = torch.empty((M, I), dtype=torch.float16, device="cuda")
+    out = torch.empty((M, H), dtype=torch.float16, device="cuda")
+
+    def call():
+        w4.mlp(A, *pw, gamma=gm, inter=inter, out=out, workspace=ws)
+
+    call()
+    torch.cuda.synchronize()
+    e_inter, e_out = inter.clone(), out.clone()
+    g_ = _capture(call)
+    for r in range(4):
+        inter.fill_(float("nan"))
+        out.fill_(float("nan"))
+        g_.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(inter, e_inter) and torch.equal(out, e_out), f"replay {r}"
+        w4.gemm(A, pw[0], gamma=gm, workspace=ws)  # other eager work on the workspace
         torch.cuda.synchronize()
 
 
