@@ -172,7 +172,7 @@ int prep_gemm(const void *A, const void *resid, void *resid_out, int M, int K, i
     return W4A16_ERR_ALIGN;
   st = plan_for(M, K, N, group, scale_dtype, false, split, c.pl);
   if (st != W4A16_OK) return st;
-  st = check_workspace(c.pl, staged_prologue(c.pl.kind, M, rms_gamma != nullptr, resid != nullptr),
+  st = check_workspace(c.pl, staged_prologue(c.pl, M, rms_gamma != nullptr, resid != nullptr),
                        workspace, workspace_bytes);
   if (st != W4A16_OK) return st;
 
@@ -212,7 +212,7 @@ int prep_gate_up(const void *A, const void *resid, void *resid_out, int M, int K
   if (rms_gamma != nullptr && !aligned16(rms_gamma)) return W4A16_ERR_ALIGN;
   st = plan_for(M, K, N, group, scale_dtype, true, split, c.pl);
   if (st != W4A16_OK) return st;
-  st = check_workspace(c.pl, staged_prologue(c.pl.kind, M, rms_gamma != nullptr, resid != nullptr),
+  st = check_workspace(c.pl, staged_prologue(c.pl, M, rms_gamma != nullptr, resid != nullptr),
                        workspace, workspace_bytes);
   if (st != W4A16_OK) return st;
 

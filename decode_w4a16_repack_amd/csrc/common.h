@@ -27,7 +27,7 @@ constexpr int kMaxSplitBlocks = 1024;  // split-K only below this many workgroup
 struct StreamCfg {
   int cpw, kpw, nwk, pd;
 };
-constexpr int kNumStreamCfgs = 3;
+constexpr int kNumStreamCfgs = 4;
 extern const StreamCfg kStreamCfgs[kNumStreamCfgs];
 
 // Tile configurations of the panel kernel (16 < M <= 32): MT 16-row tiles
@@ -111,13 +111,17 @@ struct Plan {
   size_t ws_x_off, ws_ss_off, ws_total_rms;
 };
 
+// k tiles per wavefront of a streaming-kernel plan (0 for other kernels)
+inline int stream_kpw(const Plan &p) { return p.kind == kKindStream ? kStreamCfgs[p.cfg].kpw : 0; }
+
 // Whether a call stages its RMSNorm prologue (stage.hip) instead of running
 // it inside the product kernel: always for the panel and tile kernels; for
-// the streaming kernel only with the residual and more than 4 rows, where
-// re-reading both activation slices in every column block costs more than
-// one staging pass.
-inline bool staged_prologue(int kind, int M, bool gamma, bool resid) {
-  return gamma && (kind != kKindStream || (resid && M > 4));
+// the streaming kernel only with the residual, and there with more than 4
+// rows (re-reading both activation slices in every column block costs more
+// than one staging pass) or a slice deeper than 5 k tiles (its registers
+// cannot hold the whole slice and its residual).
+inline bool staged_prologue(const Plan &p, int M, bool gamma, bool resid) {
+  return gamma && (p.kind != kKindStream || (resid && (M > 4 || stream_kpw(p) > 5)));
 }
 
 // force_kind: -1 automatic, else a PlanKind; force_cfg < 0 /

@@ -54,13 +54,19 @@ bool plan_stream(Plan &p, int M, int K, int N, int group, int scale_bytes, bool 
     // the widest column block whose grid, times the k splits the shape
     // needs (deep K, or a forced split), reaches 200 workgroups and still
     // fits in one round of resident workgroups; failing that the fullest
-    // single round; failing that the fewest workgroups
+    // single round; failing that the fewest workgroups.  A forced split
+    // considers only the configurations that can run it.
     int best = -1;
     long best_total = 0;
     for (int i = 0; i < kNumStreamCfgs; ++i) {
       const StreamCfg c = kStreamCfgs[i];
+      // deep slices with one column tile read the whole activation slice in
+      // every workgroup: worth it against a k split only up to 8 rows
+      // (K=13696 N=4096: M=8 13.7 -> 13.0 us, M=16 15.0 -> 17.3 us)
+      if (c.kpw > 5 && M > 8) continue;
       const long per = (long)c.nwk * c.kpw;
       const long smin = (KC + per - 1) / per;
+      if (force_split > 0 && force_split < smin) continue;
       const long total = (long)((NTL + c.cpw - 1) / c.cpw) * (force_split > 0 ? force_split : smin);
       if (total >= 200 && total <= kStreamSlots) { best = i; break; }
       const bool fits = total <= kStreamSlots;
@@ -71,6 +77,7 @@ bool plan_stream(Plan &p, int M, int K, int N, int group, int scale_bytes, bool 
         best_total = total;
       }
     }
+    if (best < 0) return false;
     p.cfg = best;
   }
   const StreamCfg c = kStreamCfgs[p.cfg];
@@ -113,7 +120,7 @@ bool plan_stream(Plan &p, int M, int K, int N, int group, int scale_bytes, bool 
   // rows; above that each k tile's fragments are loaded straight into
   // registers just before its first weight tile, which measured faster
   // (M=8: 10.6 -> 9.9 us; M=3: 9.1 against 9.5 us the other way)
-  if (M <= 4) {
+  if (M <= 4 && c.kpw <= 5) {
     const size_t with_a = align16(meta + a_lds > red ? meta + a_lds : red);
     if ((size_t)c.nwk * with_a + (size_t)c.nwk * 64 <= limit) {
       p.alds = 1;
@@ -224,7 +231,7 @@ void plan_tile(Plan &p, int M, int K, int N, int group, int scale_bytes, bool ga
 // inside the arrival counters at its start, which every plan shares and
 // leaves at zero (a plan without split-K has no workspace of its own).
 void add_staging(Plan &p, int M, int K) {
-  if (!staged_prologue(p.kind, M, true, true)) {
+  if (!staged_prologue(p, M, true, true)) {
     p.ws_total_rms = p.ws_total;
     return;
   }
@@ -259,7 +266,7 @@ Plan make_plan(int M, int K, int N, int group, int scale_bytes, bool gate_up, in
 
 hipError_t launch_gemm(const GemmArgs &a, const Plan &pl, int group, bool scale_f32,
                        bool gate_up, hipStream_t stream) {
-  if (staged_prologue(pl.kind, a.M, a.gamma != nullptr, a.resid != nullptr)) {
+  if (staged_prologue(pl, a.M, a.gamma != nullptr, a.resid != nullptr)) {
     // stage the normalized rows, then the plain product on them with the
     // row scale in the epilogue
     const hipError_t e = launch_rms_stage(a.A, a.resid, a.resid_out, a.gamma, a.M, a.K,

@@ -285,12 +285,14 @@ stream_kernel(const GemmArgs p) {
       at[d] = prescale_frag(x);
     }
   };
-  // From LDS (M <= 4) the fragments are ready with the copies, and the whole
-  // slice is prepared before the loop (measured faster: nothing waits for
-  // them, and the loop keeps only weight work between its MFMAs); fragments
-  // loaded from memory are prepared at their first use.
+  // From LDS (M <= 4, slices of at most 5 k tiles) the fragments are ready
+  // with the copies, and the whole slice is prepared before the loop
+  // (measured faster: nothing waits for them, and the loop keeps only weight
+  // work between its MFMAs); fragments loaded from memory are prepared at
+  // their first use.
   //    (k tiles past the slice: zeroed by one uniform branch when the slice
   //    has any, ahead of the loop; per element at first use otherwise)
+  static_assert(!ALDS || KPW <= 5, "LDS-staged rows only for shallow slices");
   constexpr bool PREP_AHEAD = ALDS;
   if constexpr (PREP_AHEAD) {
     if constexpr (!RES) {
@@ -340,7 +342,8 @@ stream_kernel(const GemmArgs p) {
       } else {
         f16x8 src[4];
 #pragma unroll
-        for (int d = 0; d < 4; ++d) src[d] = t < my_n ? a[t][d][0] : f16x8{};
+        for (int d = 0; d < 4; ++d)
+          src[d] = t < my_n ? a[t][d][0] : f16x8{};
         prep_tile(t, src, at);
       }
       group_row_sums<G>(ug, at, kq);
@@ -496,18 +499,28 @@ hipError_t launch_g(const GemmArgs &a, const Plan &pl, bool sf32, bool gu, hipSt
 
 template <int CPW, int KPW, int NWK, int PD, int G, int RMS>
 hipError_t launch_a(const GemmArgs &a, const Plan &pl, bool sf32, bool gu, hipStream_t st) {
-  return pl.alds ? launch_g<CPW, KPW, NWK, PD, true, G, RMS>(a, pl, sf32, gu, st)
-                 : launch_g<CPW, KPW, NWK, PD, false, G, RMS>(a, pl, sf32, gu, st);
+  // (deep slices never stage their rows through LDS: the planner does not
+  // choose it, and the compiler would hoist every slot read of the slice)
+  if constexpr (KPW <= 5) {
+    if (pl.alds) return launch_g<CPW, KPW, NWK, PD, true, G, RMS>(a, pl, sf32, gu, st);
+  }
+  return launch_g<CPW, KPW, NWK, PD, false, G, RMS>(a, pl, sf32, gu, st);
 }
 
 template <int CPW, int KPW, int NWK, int PD, int RMS>
 hipError_t launch_c(const GemmArgs &a, const Plan &pl, int group, bool sf32, bool gu,
                     hipStream_t st) {
-  switch (group) {
-    case 16: return launch_a<CPW, KPW, NWK, PD, 16, RMS>(a, pl, sf32, gu, st);
-    case 32: return launch_a<CPW, KPW, NWK, PD, 32, RMS>(a, pl, sf32, gu, st);
-    case 64: return launch_a<CPW, KPW, NWK, PD, 64, RMS>(a, pl, sf32, gu, st);
-    default: return launch_a<CPW, KPW, NWK, PD, 128, RMS>(a, pl, sf32, gu, st);
+  // the skip prologue in registers holds the whole slice: only shallow
+  // slices take it (staged_prologue stages the others)
+  if constexpr (RMS == 2 && KPW > 5) {
+    return hipErrorInvalidValue;
+  } else {
+    switch (group) {
+      case 16: return launch_a<CPW, KPW, NWK, PD, 16, RMS>(a, pl, sf32, gu, st);
+      case 32: return launch_a<CPW, KPW, NWK, PD, 32, RMS>(a, pl, sf32, gu, st);
+      case 64: return launch_a<CPW, KPW, NWK, PD, 64, RMS>(a, pl, sf32, gu, st);
+      default: return launch_a<CPW, KPW, NWK, PD, 128, RMS>(a, pl, sf32, gu, st);
+    }
   }
 }
 
@@ -517,7 +530,8 @@ hipError_t launch_c(const GemmArgs &a, const Plan &pl, int group, bool sf32, boo
 #define W4A16_STREAM_CFGS(X) \
   X(4, 5, 8, 8)   /* 4 column tiles x 8 slices of 5 k tiles (K <= 5120) */ \
   X(2, 5, 8, 6)   /* 2 column tiles, for narrower N */                     \
-  X(1, 5, 8, 4)   /* 1 column tile, for narrow N */
+  X(1, 5, 8, 4)   /* 1 column tile, for narrow N */                        \
+  X(1, 14, 8, 4)  /* 1 column tile x 8 slices of 14 k tiles (K <= 14336) */
 
 // Launch the configuration the plan names with prologue mode RMS.
 template <int RMS>

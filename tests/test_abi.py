@@ -191,14 +191,21 @@ def test_plan_query_matches_workspace_and_kernel_choice(L):
 
 
 def test_plan_deep_k_splits_and_forced_splits(L):
-    """K = 13696 (107 k tiles) is deeper than one workgroup covers: the
-    automatic plan splits it; a forced split below that minimum, above the
-    tile count, or on the tile kernel (M > 32) is rejected; a forced split
-    rounds so that no slice is empty."""
+    """K = 13696 (107 k tiles) is deeper than an 8 x 5-tile workgroup
+    covers.  Up to 8 rows the automatic plan takes slices of 14 k tiles with
+    one column tile per workgroup (256 workgroups, no split); above that it
+    splits k, and a forced split below that minimum, above the tile count,
+    or on the tile kernel (M > 32) is rejected; a forced split rounds so
+    that no slice is empty."""
     st, auto = plan(L, 8, 13696, 4096)
+    assert st == _lib.OK and auto.split == 1 and auto.k_tiles_per_split == 107
+    assert tuple(auto.grid) == (256, 1, 1)
+    st, f = plan(L, 8, 13696, 4096, split=1)
+    assert st == _lib.OK and f.split == 1
+    st, auto = plan(L, 16, 13696, 4096)
     assert st == _lib.OK and auto.split >= 3
     for sk in (1, 2):
-        assert plan(L, 8, 13696, 4096, split=sk)[0] == _lib.ERR_SPLIT
+        assert plan(L, 16, 13696, 4096, split=sk)[0] == _lib.ERR_SPLIT
     assert plan(L, 8, 1024, 384, split=9)[0] == _lib.ERR_SPLIT    # 8 k tiles
     st, f = plan(L, 17, 4096, 4096, split=2)                      # panel kernel, M > 16
     assert st == _lib.OK and f.kernel == _lib.KERNEL_PANEL and f.split == 2
@@ -207,7 +214,7 @@ def test_plan_deep_k_splits_and_forced_splits(L):
     st, f = plan(L, 8, 5120, 13824, split=9)   # 40 tiles: 5 per split -> 8 splits
     assert st == _lib.OK and (f.split, f.k_tiles_per_split) == (8, 5)
     for sk in (3, 4, 8, 16):
-        st, f = plan(L, 8, 13696, 4096, split=sk)
+        st, f = plan(L, 16, 13696, 4096, split=sk)
         assert st == _lib.OK and f.split <= sk and f.workspace_bytes > 0
     st, f = plan(L, 8, 4096, 4096, split=1)
     # no split-K exchange: only the skip + RMSNorm staging (after the counters)
@@ -228,7 +235,8 @@ def test_forced_split_workspace_checked_before_launch(L):
     assert split_part > 4096
     assert L.w4a16_gemm_split(FAKE, 8, 13696, 4096, 128, 0, 1, FAKE, 0, None, None, 1e-6,
                               FAKE, FAKE, split_part - 1, 8, None) == _lib.ERR_WORKSPACE
-    assert L.w4a16_gemm_split(FAKE, 8, 13696, 4096, 128, 0, 1, FAKE, 0, None, None, 1e-6,
+    # above 8 rows the 107 k tiles need at least 3 splits: 2 is refused
+    assert L.w4a16_gemm_split(FAKE, 16, 13696, 4096, 128, 0, 1, FAKE, 0, None, None, 1e-6,
                               FAKE, FAKE, 1 << 30, 2, None) == _lib.ERR_SPLIT
     assert L.w4a16_gemm_gate_up_split(FAKE, 20, 4096, 4096, 128, 0, 1, FAKE, FAKE, None, 1e-6,
                                       FAKE, FAKE, 1 << 30, 33, None) == _lib.ERR_SPLIT
@@ -289,13 +297,13 @@ def test_mlp_validation_before_any_launch(L):
     assert mlp(down=FAKE + 4) == _lib.ERR_ALIGN
     assert mlp(res=FAKE) == _lib.ERR_NULL            # residual needs gamma
     assert mlp(res_out=FAKE) == _lib.ERR_NULL        # residual_out needs residual
-    # with the skip prologue (staged above 4 rows) every byte of the reported
-    # size is needed by one of the two projections
-    assert need > 0
-    assert mlp(res=FAKE, gamma=FAKE, ws=FAKE, ws_n=need - 1) == _lib.ERR_WORKSPACE
-    # M=1 deep down projection: the down plan needs more workspace than gate_up
+    # the skip prologue of gate_up is staged above 4 rows: its staging rows
+    # (M*H fp16 after the 4096 counter bytes) are required, whatever else
+    stage = 4096 + M * H * 2 + 256
+    assert need >= stage
+    assert mlp(res=FAKE, gamma=FAKE, ws=None, ws_n=0) == _lib.ERR_WORKSPACE
+    assert mlp(res=FAKE, gamma=FAKE, ws=FAKE, ws_n=stage - 1) == _lib.ERR_WORKSPACE
+    # sizes only (no call): the decode MLP block at M=1
     d = L.w4a16_workspace_bytes(1, 13696, 4096, 128, 0)
     u = L.w4a16_workspace_bytes(1, 4096, 13696, 128, 1)
     assert L.w4a16_mlp_workspace_bytes(1, 4096, 13696, 128) == max(d, u)
-    if d > u:
-        assert mlp(M=1, H=4096, I=13696, ws_n=d - 1) == _lib.ERR_WORKSPACE

@@ -405,12 +405,40 @@ def test_forced_splits_match_oracle_and_repeat():
     A, gm = to_dev(p.A), to_dev(p.gamma)
     cols = sample_cols(N, 64, seed=3)
     ref = ref_gemm(p, cols=cols, rms=True)
-    for sk in (3, 4, 8, 16, 107):
+    # (1 and 2: the 14-tile slices of one column tile; 3 and more: 5-tile
+    # slices of 4 column tiles)
+    for sk in (1, 2, 3, 4, 8, 16, 107):
         y1 = w4.gemm(A, w, gamma=gm, out=nan_out(M, N), split=sk)
         y2 = w4.gemm(A, w, gamma=gm, out=nan_out(M, N), split=sk)
         torch.cuda.synchronize()
         assert torch.equal(y1, y2), f"split {sk} not repeatable"
         check_close(y1.cpu().numpy()[:, cols], ref, f"down_proj split={sk}")
+
+
+@pytest.mark.parametrize("M,gu", [(2, False), (3, True)])
+def test_deep_k_skip_rmsnorm_staged_sampled(M, gu):
+    """K = 13696 at M <= 4 runs on 14-tile slices, which cannot hold the
+    residual in registers: the skip + RMSNorm prologue is staged; outputs on
+    sampled columns, the sum bit-exact."""
+    K, N, g = 13696, 4096, 128
+    p = synth.make_problem(M, K, N, g, seed=60 + M, gamma=True, gate_up=gu)
+    R = np.random.default_rng(M).standard_normal((M, K)).astype(F16)
+    S = oracle.skip_sum(p.A, R)
+    s_out = torch.full((M, K), float("nan"), dtype=torch.float16, device="cuda")
+    A, Rd, gm, w = to_dev(p.A), to_dev(R), to_dev(p.gamma), repack_dev(p.w)
+    cols = sample_cols(N, 64, seed=M)
+    if gu:
+        y = w4.gemm_gate_up(A, w, repack_dev(p.w_up), gamma=gm, residual=Rd, residual_out=s_out,
+                            out=nan_out(M, N))
+        ref = oracle.gate_up(S, (p.w.qweight, p.w.scales, p.w.zeros),
+                             (p.w_up.qweight, p.w_up.scales, p.w_up.zeros), g, N,
+                             gamma=p.gamma, cols=cols)
+    else:
+        y = w4.gemm(A, w, gamma=gm, residual=Rd, residual_out=s_out, out=nan_out(M, N))
+        ref = oracle.gemm(S, p.w.qweight, p.w.scales, p.w.zeros, g, N, gamma=p.gamma, cols=cols)
+    torch.cuda.synchronize()
+    check_close(y.cpu().numpy()[:, cols], ref, f"deep-k skip rmsnorm M={M} gu={gu}")
+    assert np.array_equal(s_out.cpu().numpy().view(np.uint16), S.view(np.uint16))
 
 
 @pytest.mark.parametrize("M", [1, 8, 16, 17, 32])

@@ -48,7 +48,8 @@ def _capture(fn):
 CASES = [
     (1, 5120, 13824, 128, "gemm"),
     (1, 5120, 256, 128, "gemm"),          # split-K across workgroups
-    (8, 13696, 4096, 128, "gemm"),        # deep k: split-K
+    (8, 13696, 4096, 128, "gemm"),        # deep k: 14-tile slices, no split
+    (12, 13696, 4096, 128, "gemm"),       # deep k: split-K
     (16, 1024, 384, 32, "rms"),
     (64, 1024, 512, 64, "bias_relu"),
     (130, 2048, 512, 128, "gemm"),
