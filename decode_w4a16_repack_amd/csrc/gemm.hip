@@ -41,6 +41,17 @@ int choose_split(int base, int KC, int force_split) {
 // wavefronts.  Each wavefront has a private LDS region: its slice's scales
 // and zero-points, for M <= 4 its activation rows, and at the end its
 // partial sums.
+// One wavefront's private LDS region of the streaming kernel without staged
+// activation rows: its slice's scales and zero-points per weight stream and
+// its RMSNorm gamma, or (at the end) one stream's partial sums.
+size_t stream_region_bytes(const StreamCfg &c, int group, int scale_bytes, int NW) {
+  const int gpw = c.kpw * (kTileK / group);
+  const size_t meta = NW * ((size_t)c.cpw * gpw * 16 * scale_bytes + align16((size_t)c.cpw * gpw * 8)) +
+                      (size_t)c.kpw * kTileK * 2;
+  const size_t red = (size_t)NW * c.cpw * 1024;
+  return align16(meta > red ? meta : red);
+}
+
 bool plan_stream(Plan &p, int M, int K, int N, int group, int scale_bytes, bool gate_up,
                  int force_cfg, int force_split) {
   const int NTL = N / kTileN;
@@ -60,6 +71,11 @@ bool plan_stream(Plan &p, int M, int K, int N, int group, int scale_bytes, bool 
     long best_total = 0;
     for (int i = 0; i < kNumStreamCfgs; ++i) {
       const StreamCfg c = kStreamCfgs[i];
+      // (a configuration whose private regions exceed the LDS, e.g. group 16
+      // with fp32 scales and two weight streams on 4 column tiles, is skipped
+      // in favour of a narrower one)
+      if (stream_region_bytes(c, group, scale_bytes, NW) * c.nwk + (size_t)c.nwk * 64 > 160 * 1024)
+        continue;
       // deep slices with one column tile read the whole activation slice in
       // every workgroup: worth it against a k split only up to 8 rows
       // (K=13696 N=4096: M=8 13.7 -> 13.0 us, M=16 15.0 -> 17.3 us)

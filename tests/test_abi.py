@@ -307,3 +307,49 @@ def test_mlp_validation_before_any_launch(L):
     d = L.w4a16_workspace_bytes(1, 13696, 4096, 128, 0)
     u = L.w4a16_workspace_bytes(1, 4096, 13696, 128, 1)
     assert L.w4a16_mlp_workspace_bytes(1, 4096, 13696, 128) == max(d, u)
+
+
+def test_plan_invariants_over_many_shapes(L):
+    """Host-only sweep of the planner over M, K, N, group, scale width,
+    gate_up and forced splits: every automatic plan exists and is
+    consistent (kernel by M, LDS within the 160 KiB of a compute unit, the k
+    range covered with no empty split, the grid over every column tile, the
+    workspace at least the staging it needs), and every forced split either
+    plans with at most that many splits or is refused, never anything else."""
+    import itertools
+    KS = [128, 1024, 1152, 4096, 5120, 13696, 13824, 14336, 16384, 28672]
+    NS = [16, 256, 4096, 5120, 13824]
+    MS = [1, 2, 4, 5, 8, 9, 16, 17, 24, 32, 33, 64, 128, 129]
+    n = 0
+    for M, K, N, g, sdt, gu in itertools.product(MS, KS, NS, (16, 128), (0, 1), (0, 1)):
+        st, info = plan(L, M, K, N, g, sdt, gu)
+        assert st == _lib.OK, (M, K, N, g, sdt, gu, st)
+        KC = K // 128
+        want = (_lib.KERNEL_STREAM if M <= 16 else _lib.KERNEL_PANEL if M <= 32
+                else _lib.KERNEL_TILE)
+        # (a shape the panel kernel cannot take goes to the tile kernel)
+        assert info.kernel == want or (want == _lib.KERNEL_PANEL and info.kernel == _lib.KERNEL_TILE)
+        assert 0 < info.lds_bytes <= 160 * 1024
+        assert info.block in (256, 512)
+        assert info.split >= 1 and info.grid[1] == info.split
+        assert info.k_tiles_per_split * info.split >= KC
+        assert info.k_tiles_per_split * (info.split - 1) < KC
+        assert all(x >= 1 for x in info.grid)
+        if info.kernel != _lib.KERNEL_TILE:
+            rows = 16 if info.kernel == _lib.KERNEL_STREAM else 32
+            assert info.grid[2] == (M + rows - 1) // rows
+        stage = 4096 + M * K * 2 if M > 4 else 0
+        assert info.workspace_bytes >= stage
+        assert info.workspace_bytes == max(plan(L, M, K, N, g, s, gu)[1].workspace_bytes
+                                           for s in (sdt,))
+        n += 1
+        if M <= 32 and K in (1152, 13696) and N in (256, 4096):
+            for sk in (1, 2, 3, 5, 8, KC, KC + 1):
+                st, f = plan(L, M, K, N, g, sdt, gu, split=sk)
+                assert st in (_lib.OK, _lib.ERR_SPLIT), (M, K, N, sk, st)
+                if st == _lib.OK:
+                    assert 1 <= f.split <= sk and f.grid[1] == f.split
+                    assert f.k_tiles_per_split * f.split >= KC
+                    assert f.k_tiles_per_split * (f.split - 1) < KC
+                    assert f.kernel != _lib.KERNEL_TILE
+    assert n == len(MS) * len(KS) * len(NS) * 8

@@ -317,6 +317,17 @@ def test_gate_up_small_all_outputs(M, g, rms):
     check_close(run_gate_up(p, rms), ref_gate_up(p, rms=rms), f"gate_up M={M} g={g} rms={rms}")
 
 
+@pytest.mark.parametrize("M,rms", [(1, False), (8, True), (16, False)])
+def test_gate_up_group16_fp32_scales_narrow_config(M, rms):
+    """Group 16 with fp32 scales and two weight streams: the 4-column-tile
+    streaming configuration's metadata exceeds the LDS, so the planner takes
+    a narrower one (not the tile kernel)."""
+    p = synth.make_problem(M, 1024, 512, 16, seed=70 + M, scale_dtype=F32, gate_up=True,
+                           gamma=rms)
+    assert w4.plan(M, 1024, 512, 16, 1, True).kernel == "stream"
+    check_close(run_gate_up(p, rms), ref_gate_up(p, rms=rms), f"gate_up g16 fp32 M={M}")
+
+
 # ------------------------------------------------- skip + RMSNorm prologue
 
 
