@@ -107,13 +107,15 @@ int w4a16_repack(const uint8_t *qweight, const void *scales,
 /*
  * Workspace bytes w4a16_gemm (gate_up = 0) or w4a16_gemm_gate_up
  * (gate_up = 1) needs for this shape: fp32 split-K partial sums and
- * arrival counters, and for M > 16 the RMSNorm staging rows (fp16 [M][K]
- * x * gamma activations and fp32 [M] sums of squares, written by a staging
- * pass before the product, as the "fused RMS-norm" update on the onnx-genai
- * pull request stages the normalized activation).  Only calls with the
- * RMSNorm prologue need the staging part: a call without it on a shape
- * without split-K (w4a16_plan reports split 1) may pass a NULL workspace.
- * 0 when M <= 16 and the shape runs without split-K.  The workspace must be
+ * arrival counters, and the RMSNorm staging rows (fp16 [M][K] x * gamma
+ * activations and fp32 [M] sums of squares, written by a staging pass
+ * before the product, as the "fused RMS-norm" update on the onnx-genai pull
+ * request stages the normalized activation) for the calls that stage their
+ * prologue: every RMSNorm call above 16 rows, and the skip + RMSNorm calls
+ * above 4 rows or on deep-k shapes.  Only those calls need the staging
+ * part: a call without a prologue on a shape without split-K (w4a16_plan
+ * reports split 1) may pass a NULL workspace.  0 when M <= 4, the k range
+ * is at most 5120 and the shape runs without split-K.  The workspace must be
  * zero-filled once after allocation; the counters occupy its first 4096
  * bytes for every shape (the staging rows never do) and every call leaves
  * them at zero again, so one workspace (sized for the largest shape) serves
