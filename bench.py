@@ -534,7 +534,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=480)
-    ap.add_argument("--warmup", type=int, default=20)
+    # (2000 untimed steps, about 20 ms of GPU work: enough for the clocks of a
+    # freshly taken GPU to settle before the timed steps)
+    ap.add_argument("--warmup", type=int, default=2000)
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
@@ -648,7 +650,7 @@ def main():
         "dtype": "f16",
         "data": "synthetic",
         "config": {"workload": "decode GEMV M=1 K=5120 N=13824 group=128, asymmetric 4-bit zp, "
-                               "fp16 scales, fp16 A ~ N(0,1), 16 rotating resident input sets",
+                               f"fp16 scales, fp16 A ~ N(0,1), {R} rotating resident input sets",
                    "M": 1, "K": K, "N": N, "group": GROUP},
         "us_per_call": us_mean,
         "tflops": flops(1) / us_mean / 1e6,
