@@ -20,7 +20,7 @@ namespace w4a16 {
 // pos(j) = 4*(j%2) + j/2 of the packed word.
 __global__ void __launch_bounds__(256)
 repack_weights_kernel(const uint32_t *__restrict__ q, uint32_t *__restrict__ out,
-                      int K, int N, size_t words) {
+                      int K, int /*N: implied by words*/, size_t words) {
   size_t o = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (o >= words) return;
   const int d = (int)(o & 3);
@@ -48,7 +48,8 @@ repack_weights_kernel(const uint32_t *__restrict__ q, uint32_t *__restrict__ out
 // zero pad bytes.  One-time work (a few MB at most), kept simple.
 __global__ void __launch_bounds__(256)
 repack_meta_kernel(const uint8_t *__restrict__ scales, const uint8_t *__restrict__ zeros,
-                   int N, int G, int sb, size_t s_bytes, size_t z_off, size_t z_bytes,
+                   int /*N: implied by the byte counts*/, int G, int sb, size_t s_bytes,
+                   size_t z_off, size_t z_bytes,
                    uint8_t *__restrict__ tail, size_t tail_bytes) {
   const size_t zrow = (size_t)(G + 1) / 2;
   for (size_t b = (size_t)blockIdx.x * blockDim.x + threadIdx.x; b < tail_bytes;

@@ -190,13 +190,18 @@ def skip_sum(A, residual) -> np.ndarray:
     (SkipSimplifiedLayerNormalization, named in the "Stage 2 of
     spec-capture" update): the exact sum of two fp16 values, rounded once
     to fp16 (nearest-even).  The norm and the product then take S as the
-    activation: ``gemm(skip_sum(A, R), ..., gamma=gamma)``."""
-    return (np.asarray(A, dtype=np.float64) + np.asarray(residual, dtype=np.float64)).astype(np.float16)
+    activation: ``gemm(skip_sum(A, R), ..., gamma=gamma)``.  A sum beyond
+    the fp16 range rounds to infinity, as IEEE rounding defines."""
+    with np.errstate(over="ignore"):
+        return (np.asarray(A, dtype=np.float64) +
+                np.asarray(residual, dtype=np.float64)).astype(np.float16)
 
 
 def to_fp16(y: np.ndarray) -> np.ndarray:
-    """Round the f64 result to fp16, nearest-even (IEEE default)."""
-    return np.asarray(y, dtype=np.float64).astype(np.float16)
+    """Round the f64 result to fp16, nearest-even (IEEE default; beyond the
+    fp16 range, to infinity)."""
+    with np.errstate(over="ignore"):
+        return np.asarray(y, dtype=np.float64).astype(np.float16)
 
 
 def mlp(A, gate, up, down, group: int, I: int, H: int, *, gamma=None,
