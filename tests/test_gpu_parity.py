@@ -480,6 +480,39 @@ def test_probes():
     assert torch.equal(src, dst)
 
 
+# ------------------------------------------------------- deepest k range
+
+_DEEP = {}
+
+
+def _deep_weight():
+    """K = 28672, N = 8192, group 128 (a 70B-class down projection): drawn
+    once per module, packed once."""
+    if not _DEEP:
+        w = synth.draw_weight(np.random.default_rng(2024), 28672, 8192, 128)
+        _DEEP["w"], _DEEP["pw"] = w, repack_dev(w)
+    return _DEEP["w"], _DEEP["pw"]
+
+
+@pytest.mark.parametrize("M,rms", [(1, False), (8, True), (24, False), (40, True)])
+def test_deepest_k_sampled(M, rms):
+    """224 k tiles: the streaming and panel kernels split them 6 ways, the
+    tile kernel runs them in one workgroup; sampled columns against the
+    oracle, and a repeated call bit-identical."""
+    w, pw = _deep_weight()
+    rng = np.random.default_rng(M)
+    A = rng.standard_normal((M, w.K)).astype(F16)
+    gm = rng.normal(1.0, 0.1, size=w.K).astype(F16) if rms else None
+    Ad, gd = to_dev(A), to_dev(gm)
+    y = w4.gemm(Ad, pw, gamma=gd, out=nan_out(M, w.N))
+    y2 = w4.gemm(Ad, pw, gamma=gd, out=nan_out(M, w.N))
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2)
+    cols = sample_cols(w.N, 96, seed=M)
+    ref = oracle.gemm(A, w.qweight, w.scales, w.zeros, 128, w.N, gamma=gm, cols=cols)
+    check_close(y.cpu().numpy()[:, cols], ref, f"K=28672 M={M} rms={rms}")
+
+
 # ------------------------------------------------------------ MLP chain
 
 
