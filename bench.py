@@ -504,15 +504,15 @@ def _counter_rows(d, counter):
     return out
 
 
-def traffic_summary(fetch_dir, write_dir):
+def summarize_traffic(fetch_dir, write_dir):
     """HBM bytes per GEMM launch: FETCH_SIZE and WRITE_SIZE (KiB per
-    dispatch), each scaled by what the counter reads for the plain copy of
-    COPY_PROBE_BYTES in the same run."""
+    dispatch, median over dispatches), each scaled by what the counter reads
+    for the plain copy of COPY_PROBE_BYTES in the same run."""
     res = {"kernel_source_hash": kernel_source_hash(), "copy_probe_bytes": COPY_PROBE_BYTES}
     total = 0.0
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = _counter_rows(d, counter)
-        gemm = [n for n in rows if "stream_kernel" in n or "oneshot_kernel" in n or "ring_kernel" in n]
+        gemm = [n for n in rows if "stream_kernel" in n]
         copy = [n for n in rows if "probe_copy_kernel" in n]
         if len(gemm) != 1 or len(copy) != 1:
             raise SystemExit(f"{counter}: expected one GEMM and one copy kernel, got {sorted(rows)}")
@@ -525,6 +525,12 @@ def traffic_summary(fetch_dir, write_dir):
                         "dispatches": len(rows[gemm[0]]), "kernel": gemm[0]}
     res["bytes_per_launch"] = total
     res["algorithmic_bytes_per_launch"] = algorithmic_bytes(1)
+    return res
+
+
+def traffic_summary(fetch_dir, write_dir):
+    """Write summarize_traffic(...) to the committed traffic file."""
+    res = summarize_traffic(fetch_dir, write_dir)
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(res, f, indent=1)
     print(json.dumps(res, indent=1))
