@@ -42,13 +42,64 @@ def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else t.data_ptr()
 
 
-def _need_gpu(t: torch.Tensor, name: str, dtype=None):
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a GPU tensor")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
+def _need_gpu(t: torch.Tensor, name: str, dtype=None, device=None, shape=None):
+    _need_form(t, name, dtype, shape)
+    _need_device(t, name, device)
+
+
+def _need_form(t: torch.Tensor, name: str, dtype=None, shape=None):
+    """dtype, shape and contiguity (checked before the device, so a wrong
+    shape is reported as such on any host)."""
     if dtype is not None and t.dtype != dtype:
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _need_device(t: torch.Tensor, name: str, device=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the activations on {device}")
+
+
+def _check_operands(A: torch.Tensor, weights, *, out=None, bias=None, gamma=None,
+                    residual=None, residual_out=None):
+    """Everything the library reads or writes besides the workspace, checked
+    before the call: the library trusts its pointers, so a short ``out`` or
+    ``bias`` would be overrun on the device.  Shapes first, then devices."""
+    _need_form(A, "A", torch.float16)
+    if A.dim() != 2:
+        raise ValueError(f"A must be 2-D [M][K], got shape {tuple(A.shape)}")
+    M, K = A.shape
+    N = weights[0].N
+    for i, w in enumerate(weights):
+        _need_form(w.data, f"packed weight {i}", torch.uint8)
+        if w.data.numel() < packed_bytes(w.K, w.N, w.group, w.scale_dtype, w.has_zp):
+            raise ValueError(f"packed weight {i} is shorter than its layout")
+    if out is not None:
+        _need_form(out, "out", torch.float16, shape=(M, N))
+    if bias is not None:
+        _need_form(bias, "bias", torch.float16)
+        if bias.numel() != N:
+            raise ValueError(f"bias must have N={N} elements, got {bias.numel()}")
+    if gamma is not None:
+        _need_form(gamma, "gamma", torch.float16)
+        if gamma.numel() != K:
+            raise ValueError(f"gamma must have K={K} elements, got {gamma.numel()}")
+    for t, n in ((residual, "residual"), (residual_out, "residual_out")):
+        if t is not None:
+            _need_form(t, n, torch.float16, shape=(M, K))
+    _need_device(A, "A")
+    dev = A.device
+    for i, w in enumerate(weights):
+        _need_device(w.data, f"packed weight {i}", dev)
+    for t, n in ((out, "out"), (bias, "bias"), (gamma, "gamma"), (residual, "residual"),
+                 (residual_out, "residual_out")):
+        if t is not None:
+            _need_device(t, n, dev)
 
 
 @dataclass
@@ -84,6 +135,8 @@ class Plan:
     block: int
     lds_bytes: int
     workspace_bytes: int
+    col_tiles: int          # 16-column weight tiles per workgroup
+    k_tiles_per_wave: int   # 128-wide k tiles per wavefront and column tile
 
 
 def plan(M: int, K: int, N: int, group: int, scale_dtype: int = _lib.SCALE_F16,
@@ -95,7 +148,7 @@ def plan(M: int, K: int, N: int, group: int, scale_dtype: int = _lib.SCALE_F16,
     kind = {_lib.KERNEL_STREAM: "stream", _lib.KERNEL_PANEL: "panel"}.get(info.kernel, "tile")
     return Plan(kind, info.split,
                 info.k_tiles_per_split, tuple(info.grid), info.block, info.lds_bytes,
-                info.workspace_bytes)
+                info.workspace_bytes, info.col_tiles, info.k_tiles_per_wave)
 
 
 class Workspace:
@@ -127,16 +180,23 @@ def repack(qweight: torch.Tensor, scales: torch.Tensor, zeros: Optional[torch.Te
            K: int, N: int, group: int) -> PackedWeight:
     """Repack canonical weights (u8 [N][K/2], fp16/fp32 scales [N][G],
     u8 zeros [N][ceil(G/2)] or None) into the packed layout, on the GPU."""
-    _need_gpu(qweight, "qweight", torch.uint8)
-    _need_gpu(scales, "scales")
     if scales.dtype == torch.float16:
         sdt = _lib.SCALE_F16
     elif scales.dtype == torch.float32:
         sdt = _lib.SCALE_F32
     else:
         raise ValueError("scales must be float16 or float32")
+    if K % 2 or group <= 0 or K % group:
+        _lib.check(_lib.ERR_SHAPE, "w4a16_repack")
+    G = K // group
+    _need_form(qweight, "qweight", torch.uint8, shape=(N, K // 2))
+    _need_form(scales, "scales", shape=(N, G))
     if zeros is not None:
-        _need_gpu(zeros, "zeros", torch.uint8)
+        _need_form(zeros, "zeros", torch.uint8, shape=(N, (G + 1) // 2))
+    _need_device(qweight, "qweight")
+    _need_device(scales, "scales", qweight.device)
+    if zeros is not None:
+        _need_device(zeros, "zeros", qweight.device)
     nbytes = packed_bytes(K, N, group, sdt, zeros is not None)
     if nbytes == 0:
         _lib.check(_lib.ERR_SHAPE, "w4a16_packed_bytes")
@@ -157,18 +217,16 @@ def gemm(A: torch.Tensor, w: PackedWeight, *, epilogue: str = "none",
     or with ``residual`` X = RMSNorm(A + residual) (w4a16_gemm_skip_rmsnorm;
     the sum is written to ``residual_out`` when given).  split > 0 forces
     that split-K factor (w4a16_gemm_split)."""
-    _need_gpu(A, "A", torch.float16)
+    _check_operands(A, [w], out=out, bias=bias, gamma=gamma, residual=residual,
+                    residual_out=residual_out)
     M, K = A.shape
     if K != w.K:
         raise ValueError(f"A has K={K}, weight has K={w.K}")
-    for t, n in ((bias, "bias"), (gamma, "gamma"), (residual, "residual"),
-                 (residual_out, "residual_out")):
-        if t is not None:
-            _need_gpu(t, n, torch.float16)
+    if epilogue not in _lib.EPI:
+        raise ValueError(f"unknown epilogue {epilogue!r}")
     _check_residual(A, gamma, residual, residual_out, split)
     if out is None:
         out = torch.empty((M, w.N), dtype=torch.float16, device=A.device)
-    _need_gpu(out, "out", torch.float16)
     if split:
         ws_n = plan(M, K, w.N, w.group, w.scale_dtype, False, split).workspace_bytes
     else:
@@ -208,23 +266,18 @@ def gemm_gate_up(A: torch.Tensor, w_gate: PackedWeight, w_up: PackedWeight, *,
                  residual_out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """fp16 [M][N] = silu(X . Wg) * (X . Wu); split, residual and
     residual_out as in gemm()."""
-    _need_gpu(A, "A", torch.float16)
-    M, K = A.shape
-    for t, n in ((residual, "residual"), (residual_out, "residual_out")):
-        if t is not None:
-            _need_gpu(t, n, torch.float16)
-    _check_residual(A, gamma, residual, residual_out, split)
     for w in (w_gate, w_up):
         if (w.K, w.N, w.group, w.scale_dtype, w.has_zp) != (
                 w_gate.K, w_gate.N, w_gate.group, w_gate.scale_dtype, w_gate.has_zp):
             raise ValueError("gate and up weights must share K, N, group, scale dtype, zp")
+    _check_operands(A, [w_gate, w_up], out=out, gamma=gamma, residual=residual,
+                    residual_out=residual_out)
+    M, K = A.shape
+    _check_residual(A, gamma, residual, residual_out, split)
     if K != w_gate.K:
         raise ValueError(f"A has K={K}, weights have K={w_gate.K}")
-    if gamma is not None:
-        _need_gpu(gamma, "gamma", torch.float16)
     if out is None:
         out = torch.empty((M, w_gate.N), dtype=torch.float16, device=A.device)
-    _need_gpu(out, "out", torch.float16)
     if split:
         ws_n = plan(M, K, w_gate.N, w_gate.group, w_gate.scale_dtype, True, split).workspace_bytes
     else:
@@ -258,12 +311,10 @@ def mlp(A: torch.Tensor, w_gate: PackedWeight, w_up: PackedWeight, w_down: Packe
     then fp16 [M][H] = inter . Wd.  A is [M][H]; w_gate and w_up have K = H,
     N = I; w_down has K = I, N = H.  X, gamma, residual and residual_out as
     in gemm_gate_up().  ``inter`` receives the intermediate when given."""
-    _need_gpu(A, "A", torch.float16)
+    _need_form(A, "A", torch.float16)
+    if A.dim() != 2:
+        raise ValueError(f"A must be 2-D [M][H], got shape {tuple(A.shape)}")
     M, H = A.shape
-    for t, n in ((residual, "residual"), (residual_out, "residual_out")):
-        if t is not None:
-            _need_gpu(t, n, torch.float16)
-    _check_residual(A, gamma, residual, residual_out, 0)
     key = (w_gate.group, w_gate.scale_dtype, w_gate.has_zp)
     for w in (w_up, w_down):
         if (w.group, w.scale_dtype, w.has_zp) != key:
@@ -272,16 +323,23 @@ def mlp(A: torch.Tensor, w_gate: PackedWeight, w_up: PackedWeight, w_down: Packe
     if (w_gate.K, w_up.K, w_up.N, w_down.K, w_down.N) != (H, H, I, I, H):
         raise ValueError(f"weights do not chain: A has H={H}; gate {w_gate.K}x{w_gate.N}, "
                          f"up {w_up.K}x{w_up.N}, down {w_down.K}x{w_down.N}")
-    if gamma is not None:
-        _need_gpu(gamma, "gamma", torch.float16)
+    _need_form(w_down.data, "packed down weight", torch.uint8)
+    if w_down.data.numel() < packed_bytes(w_down.K, w_down.N, w_down.group,
+                                          w_down.scale_dtype, w_down.has_zp):
+        raise ValueError("packed down weight is shorter than its layout")
+    for t, n, shp in ((inter, "inter", (M, I)), (out, "out", (M, H))):
+        if t is not None:
+            _need_form(t, n, torch.float16, shape=shp)
+    _check_operands(A, [w_gate, w_up], gamma=gamma, residual=residual,
+                    residual_out=residual_out)
+    _need_device(w_down.data, "packed down weight", A.device)
+    _check_residual(A, gamma, residual, residual_out, 0)
     if inter is None:
         inter = torch.empty((M, I), dtype=torch.float16, device=A.device)
     if out is None:
         out = torch.empty((M, H), dtype=torch.float16, device=A.device)
-    _need_gpu(inter, "inter", torch.float16)
-    _need_gpu(out, "out", torch.float16)
-    if tuple(inter.shape) != (M, I) or tuple(out.shape) != (M, H):
-        raise ValueError("inter must be [M][I] and out [M][H]")
+    _need_device(inter, "inter", A.device)
+    _need_device(out, "out", A.device)
     ws_n = mlp_workspace_bytes(M, H, I, w_gate.group)
     ws = (workspace or _default_ws).get(ws_n, A.device)
     st = _lib.lib().w4a16_mlp(_ptr(A), _ptr(residual), _ptr(residual_out), M, H, I,
@@ -295,8 +353,16 @@ def mlp(A: torch.Tensor, w_gate: PackedWeight, w_up: PackedWeight, w_down: Packe
 
 def add_bias(x: torch.Tensor, bias: torch.Tensor, out: Optional[torch.Tensor] = None):
     """Unfused-chain pass: fp16(x + bias)."""
-    _need_gpu(x, "x", torch.float16)
+    _need_form(x, "x", torch.float16)
     M, N = x.shape
+    _need_form(bias, "bias", torch.float16)
+    if bias.numel() != N:
+        raise ValueError(f"bias must have N={N} elements, got {bias.numel()}")
+    if out is not None:
+        _need_form(out, "out", torch.float16, shape=(M, N))
+    for t, n in ((x, "x"), (bias, "bias"), (out, "out")):
+        if t is not None:
+            _need_device(t, n, x.device)
     out = torch.empty_like(x) if out is None else out
     _lib.check(_lib.lib().w4a16_add_bias(_ptr(x), _ptr(bias), M, N, _ptr(out), _stream()),
                "w4a16_add_bias")
@@ -305,8 +371,12 @@ def add_bias(x: torch.Tensor, bias: torch.Tensor, out: Optional[torch.Tensor] = 
 
 def relu(x: torch.Tensor, out: Optional[torch.Tensor] = None):
     """Unfused-chain pass: max(x, 0)."""
-    _need_gpu(x, "x", torch.float16)
+    _need_form(x, "x", torch.float16)
     M, N = x.shape
+    if out is not None:
+        _need_form(out, "out", torch.float16, shape=(M, N))
+        _need_device(out, "out", x.device)
+    _need_device(x, "x", x.device)
     out = torch.empty_like(x) if out is None else out
     _lib.check(_lib.lib().w4a16_relu(_ptr(x), M, N, _ptr(out), _stream()), "w4a16_relu")
     return out
@@ -315,8 +385,16 @@ def relu(x: torch.Tensor, out: Optional[torch.Tensor] = None):
 def rmsnorm(A: torch.Tensor, gamma: torch.Tensor, eps: float = 1e-6,
             out: Optional[torch.Tensor] = None):
     """Unfused-chain pass: fp16(A * gamma / sqrt(mean(A^2) + eps))."""
-    _need_gpu(A, "A", torch.float16)
+    _need_form(A, "A", torch.float16)
     M, K = A.shape
+    _need_form(gamma, "gamma", torch.float16)
+    if gamma.numel() != K:
+        raise ValueError(f"gamma must have K={K} elements, got {gamma.numel()}")
+    if out is not None:
+        _need_form(out, "out", torch.float16, shape=(M, K))
+    for t, n in ((A, "A"), (gamma, "gamma"), (out, "out")):
+        if t is not None:
+            _need_device(t, n, A.device)
     out = torch.empty_like(A) if out is None else out
     _lib.check(_lib.lib().w4a16_rmsnorm(_ptr(A), _ptr(gamma), float(eps), M, K, _ptr(out),
                                         _stream()), "w4a16_rmsnorm")
@@ -324,11 +402,19 @@ def rmsnorm(A: torch.Tensor, gamma: torch.Tensor, eps: float = 1e-6,
 
 
 def probe_read(buf: torch.Tensor, sink: torch.Tensor) -> None:
+    _need_gpu(buf, "buf")
+    _need_gpu(sink, "sink", device=buf.device)
+    if sink.numel() * sink.element_size() < 4096 * 4:
+        raise ValueError("sink must hold at least 4096 32-bit values")
     _lib.check(_lib.lib().w4a16_probe_read(_ptr(buf), buf.numel() * buf.element_size(),
                                            _ptr(sink), _stream()), "w4a16_probe_read")
 
 
 def probe_copy(src: torch.Tensor, dst: torch.Tensor) -> None:
+    _need_gpu(src, "src")
+    _need_gpu(dst, "dst", device=src.device)
+    if dst.numel() * dst.element_size() < src.numel() * src.element_size():
+        raise ValueError("dst is smaller than src")
     _lib.check(_lib.lib().w4a16_probe_copy(_ptr(src), _ptr(dst),
                                            src.numel() * src.element_size(), _stream()),
                "w4a16_probe_copy")

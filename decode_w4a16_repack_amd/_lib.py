@@ -27,6 +27,10 @@ ERR_ALIGN = -7
 ERR_LAUNCH = -8
 ERR_SPLIT = -9
 
+# bytes of split-K arrival counters at the start of every workspace
+# (W4A16_COUNTER_BYTES)
+COUNTER_BYTES = 16384
+
 KERNEL_STREAM = 1
 KERNEL_TILE = 2
 KERNEL_PANEL = 3
@@ -50,7 +54,8 @@ class PlanInfo(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_int), ("split", ctypes.c_int),
                 ("k_tiles_per_split", ctypes.c_int), ("grid", ctypes.c_int * 3),
                 ("block", ctypes.c_int), ("lds_bytes", ctypes.c_int),
-                ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace_bytes", ctypes.c_size_t), ("col_tiles", ctypes.c_int),
+                ("k_tiles_per_wave", ctypes.c_int)]
 
 
 class W4A16Error(RuntimeError):

@@ -368,6 +368,17 @@ int w4a16_plan(int M, int K, int N, int group, int scale_dtype, int gate_up, int
   info->block = pl.block;
   info->lds_bytes = (int)pl.lds_bytes;
   info->workspace_bytes = pl.ws_total_rms;
+  if (pl.kind == kKindStream) {
+    info->col_tiles = kStreamCfgs[pl.cfg].cpw;
+    info->k_tiles_per_wave = kStreamCfgs[pl.cfg].kpw;
+  } else if (pl.kind == kKindPanel) {
+    info->col_tiles = kPanelCfgs[pl.cfg].cpw;
+    info->k_tiles_per_wave = kPanelCfgs[pl.cfg].kpw;
+  } else {
+    // the tile kernel's two k slices take every other k tile
+    info->col_tiles = tile_columns(tile_ct(pl.cfg == 1, gate_up != 0)) / kTileN;
+    info->k_tiles_per_wave = (pl.cps + 1) / 2;
+  }
   return W4A16_OK;
 }
 

@@ -19,7 +19,11 @@ constexpr int kWave = 64;        // CDNA wavefront width
 constexpr int kTileK = 128;      // k extent of one packed weight tile
 constexpr int kTileN = 16;       // columns of one packed weight tile
 constexpr int kTileBytes = 1024; // bytes of one packed tile (64 lanes x 16 B)
-constexpr int kMaxSplitBlocks = 1024;  // split-K only below this many workgroups
+// Split-K arrival counters at the start of every workspace: one 32-bit word
+// per column tile (stream kernel) or output tile (panel kernel), so split-K
+// is possible up to this many tiles (N <= 65536 on the stream kernel).
+constexpr int kMaxSplitBlocks = 4096;
+constexpr size_t kCounterBytes = (size_t)kMaxSplitBlocks * 4;
 
 // Tile configurations of the small-M stream kernel: CPW 16-column tiles per
 // wavefront, KPW 128-k tiles per wavefront (its activation fragments stay in

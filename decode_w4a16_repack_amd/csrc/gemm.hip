@@ -152,7 +152,7 @@ bool plan_stream(Plan &p, int M, int K, int N, int group, int scale_bytes, bool 
   size_t off = 0;
   if (p.split > 1) {
     p.ws_cnt_off = 0;
-    off = align256((size_t)kMaxSplitBlocks * 4);
+    off = align256(kCounterBytes);
     p.ws_rms_off = off;
     off = align256(off + (size_t)NTL * p.gz * p.split * 16 * 4);
     p.ws_part_off = off;
@@ -216,7 +216,7 @@ bool plan_panel(Plan &p, int M, int K, int N, int group, int scale_bytes, bool g
     const size_t tiles = (size_t)p.gx * p.gz;
     if (tiles > (size_t)kMaxSplitBlocks) return false;
     p.ws_cnt_off = 0;
-    off = align256((size_t)kMaxSplitBlocks * 4);
+    off = align256(kCounterBytes);
     p.ws_rms_off = 0;
     p.ws_part_off = off;
     off = align256(off + (size_t)p.split * NW * M * N * 4);
@@ -251,7 +251,7 @@ void add_staging(Plan &p, int M, int K) {
     p.ws_total_rms = p.ws_total;
     return;
   }
-  const size_t counters = align256((size_t)kMaxSplitBlocks * 4);
+  const size_t counters = align256(kCounterBytes);
   p.ws_x_off = align256(p.ws_total > counters ? p.ws_total : counters);
   p.ws_ss_off = align256(p.ws_x_off + (size_t)M * K * 2);
   p.ws_total_rms = align256(p.ws_ss_off + (size_t)M * 4);

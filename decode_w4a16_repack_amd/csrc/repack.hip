@@ -1,10 +1,11 @@
 // One-time repack of canonical int4 weights into the packed layout
 // (layout version 1, described in include/w4a16.h).
 //
-// The onnx-genai pull request "Marlin-style fused fp16xint4 tensor-core GEMM"
-// ("What's landed") repacks the weights once into a bijective reorder built
-// for coalesced loads and keeps the device repack byte-identical to the host
-// reference.  This reorder is designed for gfx950: one 16-byte load per lane
+// Following the onnx-genai pull request "Marlin-style fused fp16xint4
+// tensor-core GEMM" ("What's landed"), the weights are reordered once,
+// without loss, so that every weight load is coalesced; the bytes written
+// here must equal those of the oracle's host repack.  The reorder itself is
+// this library's, designed for gfx950: one 16-byte load per lane
 // (1 KiB per 64-lane wavefront) delivers, in each 32-bit word, the eight codes
 // one v_mfma_f32_16x16x32_f16 B operand slot needs, in the bit order that the
 // in-register exponent-bias unpack turns into fp16 pairs with two mask

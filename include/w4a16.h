@@ -20,8 +20,9 @@
  *
  * Numerics: (q - zp) is formed exactly in fp16, products with A are exact in
  * fp32, sums are fp32, and each group's fp32 partial sum is multiplied by its
- * scale after the contraction ("per-group scale AFTER the tensor-core
- * accumulate").  The output is rounded once to fp16 (nearest even).  Results
+ * scale once the matrix-core contraction of that group is done (the scale
+ * step of "What's landed").  The output is rounded once to fp16 (nearest
+ * even).  Results
  * are run-to-run bit-identical: split-K partial sums are reduced in a fixed
  * order, never with floating-point atomics.
  *
@@ -76,9 +77,10 @@ enum { W4A16_EPI_NONE = 0, W4A16_EPI_BIAS = 1, W4A16_EPI_BIAS_RELU = 2 };
 typedef void *w4a16_stream; /* a hipStream_t */
 
 /*
- * Packed layout, version 1 (KC = K/128, G = K/group).  The page requires a
- * one-time, bijective reorder of the weights for coalesced loads, with the
- * device repack byte-identical to the host reference ("What's landed").
+ * Packed layout, version 1 (KC = K/128, G = K/group).  "What's landed" asks
+ * for a reorder of the weights that is done once, loses nothing (a
+ * bijection) and makes every load coalesced; the device repack here writes
+ * the same bytes as the oracle's host repack of this layout.
  *   Weights at offset 0, K*N/2 bytes: tile (t = n/16, kc = k/128) is 1 KiB
  *     at byte (t*KC + kc)*1024; lane l (0..63) of a 64-lane wavefront owns
  *     its 16 bytes at l*16; 32-bit word d (0..3) of lane l holds the codes
@@ -116,12 +118,13 @@ int w4a16_repack(const uint8_t *qweight, const void *scales,
  * part: a call without a prologue on a shape without split-K (w4a16_plan
  * reports split 1) may pass a NULL workspace.  0 when M <= 4, the k range
  * is at most 5120 and the shape runs without split-K.  The workspace must be
- * zero-filled once after allocation; the counters occupy its first 4096
- * bytes for every shape (the staging rows never do) and every call leaves
- * them at zero again, so one workspace (sized for the largest shape) serves
- * calls of any shape.  Calls that share a workspace must not run
- * concurrently.
+ * zero-filled once after allocation; the split-K arrival counters occupy
+ * its first W4A16_COUNTER_BYTES bytes for every shape (the staging rows never
+ * do) and every call leaves them at zero again, so one workspace (sized for
+ * the largest shape) serves calls of any shape.  Calls that share a
+ * workspace must not run concurrently.
  */
+#define W4A16_COUNTER_BYTES 16384
 size_t w4a16_workspace_bytes(int M, int K, int N, int group, int gate_up);
 
 /*
@@ -178,6 +181,10 @@ typedef struct {
   size_t workspace_bytes; /* workspace a call with the RMSNorm prologue needs
                              (see w4a16_workspace_bytes); without it, the
                              split-K part alone */
+  int col_tiles;          /* 16-column weight tiles one workgroup covers (the
+                             last workgroup of a row may cover fewer) */
+  int k_tiles_per_wave;   /* 128-wide k tiles one wavefront contracts per
+                             column tile (the kernel configuration's depth) */
 } w4a16_plan_info;
 
 /* Host-only: fill *info with the plan a call of this shape launches.

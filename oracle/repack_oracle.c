@@ -4,10 +4,10 @@
  * TEST INFRASTRUCTURE ONLY (see w4a16_oracle.c).  Written from the documented
  * packed layout below, not from the GPU kernel.
  *
- * The onnx-genai pull request "Marlin-style fused fp16xint4 tensor-core GEMM"
- * ("What's landed") repacks the int4 weights once, with a bijective reorder
- * chosen for coalesced loads, and requires the device repack to be
- * byte-identical to the host reference.  The reorder here is this library's
+ * In the onnx-genai pull request "Marlin-style fused fp16xint4 tensor-core
+ * GEMM" ("What's landed") the int4 weights are reordered once, losslessly,
+ * for coalesced loads, and the GPU's repack is checked against a host
+ * repack byte for byte.  The reorder here is this library's
  * own (one 16-byte load per lane, 1 KiB per 64-lane wavefront); only the
  * properties (a bijection of nibbles, bit-preserving for scales and
  * zero-points) come from the page.

@@ -11,6 +11,7 @@ from decode_w4a16_repack_amd import _lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "w4a16.h")
+CB = _lib.COUNTER_BYTES  # split-K arrival counters at the start of every workspace
 
 
 def header_functions():
@@ -44,6 +45,7 @@ def test_header_enums_match_binding():
         assert re.search(rf"{name}\s*=\s*{val}\b", text), name
         assert getattr(_lib, name[6:]) == val
     assert re.search(r"W4A16_EPI_BIAS_RELU\s*=\s*2", text)
+    assert re.search(rf"#define W4A16_COUNTER_BYTES {_lib.COUNTER_BYTES}\b", text)
     assert re.search(r"W4A16_SCALE_F32\s*=\s*1", text)
 
 
@@ -129,16 +131,16 @@ def test_workspace_only_for_narrow_grids(L):
     # streaming kernel, RMSNorm prologue in registers): no workspace.  Above
     # that the workspace holds only the RMSNorm staging (fp16 [M][K] rows,
     # fp32 [M] sums of squares, each 256-byte aligned), which only calls that
-    # stage their prologue need.  It starts after the 4096 bytes of split-K arrival
-    # counters that every plan shares (and leaves at zero): staged rows
-    # written there would corrupt the next split-K call.
+    # stage their prologue need.  It starts after the split-K arrival
+    # counters (W4A16_COUNTER_BYTES) that every plan shares (and leaves at
+    # zero): staged rows written there would corrupt the next split-K call.
     a256 = lambda v: (v + 255) // 256 * 256
     for M in (1, 2, 4):
         assert L.w4a16_workspace_bytes(M, 5120, 13824, 128, 0) == 0
         assert L.w4a16_workspace_bytes(M, 5120, 13824, 128, 1) == 0
     # M = 5..16: the streaming kernel stages only the skip + RMSNorm prologue
     for M in (5, 16, 17, 32, 64, 128):
-        stage = 4096 + a256(M * 5120 * 2) + a256(M * 4)
+        stage = CB + a256(M * 5120 * 2) + a256(M * 4)
         assert L.w4a16_workspace_bytes(M, 5120, 13824, 128, 0) == stage
         assert L.w4a16_workspace_bytes(M, 5120, 13824, 128, 1) == stage
         # a call that stages checks for the staging before any launch
@@ -185,7 +187,7 @@ def test_plan_query_matches_workspace_and_kernel_choice(L):
         ws = max(plan(L, M, K, N, sdt=s, gu=gu)[1].workspace_bytes for s in (0, 1))
         assert ws == L.w4a16_workspace_bytes(M, K, N, 128, gu)
         # split-K exchange, plus the RMSNorm staging rows above M = 16
-        stage = 0 if M <= 4 else 4096 + (M * K * 2 + 255) // 256 * 256 + (M * 4 + 255) // 256 * 256
+        stage = 0 if M <= 4 else CB + (M * K * 2 + 255) // 256 * 256 + (M * 4 + 255) // 256 * 256
         assert (info.workspace_bytes > stage) == (info.split > 1)
         assert info.workspace_bytes >= stage
 
@@ -218,7 +220,7 @@ def test_plan_deep_k_splits_and_forced_splits(L):
         assert st == _lib.OK and f.split <= sk and f.workspace_bytes > 0
     st, f = plan(L, 8, 4096, 4096, split=1)
     # no split-K exchange: only the skip + RMSNorm staging (after the counters)
-    assert st == _lib.OK and f.split == 1 and f.workspace_bytes == 4096 + 8 * 4096 * 2 + 256
+    assert st == _lib.OK and f.split == 1 and f.workspace_bytes == CB + 8 * 4096 * 2 + 256
     assert L.w4a16_plan(8, 4096, 4096, 128, 0, 0, 0, None) == _lib.ERR_NULL
     assert plan(L, 8, 4000, 4096)[0] == _lib.ERR_SHAPE
 
@@ -232,7 +234,7 @@ def test_forced_split_workspace_checked_before_launch(L):
     # without that prologue needs the split-K part before them
     staging = (8 * 13696 * 2 + 255) // 256 * 256 + 256
     split_part = f.workspace_bytes - staging
-    assert split_part > 4096
+    assert split_part > CB
     assert L.w4a16_gemm_split(FAKE, 8, 13696, 4096, 128, 0, 1, FAKE, 0, None, None, 1e-6,
                               FAKE, FAKE, split_part - 1, 8, None) == _lib.ERR_WORKSPACE
     # above 8 rows the 107 k tiles need at least 3 splits: 2 is refused
@@ -298,8 +300,8 @@ def test_mlp_validation_before_any_launch(L):
     assert mlp(res=FAKE) == _lib.ERR_NULL            # residual needs gamma
     assert mlp(res_out=FAKE) == _lib.ERR_NULL        # residual_out needs residual
     # the skip prologue of gate_up is staged above 4 rows: its staging rows
-    # (M*H fp16 after the 4096 counter bytes) are required, whatever else
-    stage = 4096 + M * H * 2 + 256
+    # (M*H fp16 after the counter bytes) are required, whatever else
+    stage = CB + M * H * 2 + 256
     assert need >= stage
     assert mlp(res=FAKE, gamma=FAKE, ws=None, ws_n=0) == _lib.ERR_WORKSPACE
     assert mlp(res=FAKE, gamma=FAKE, ws=FAKE, ws_n=stage - 1) == _lib.ERR_WORKSPACE
@@ -317,8 +319,8 @@ def test_plan_invariants_over_many_shapes(L):
     workspace at least the staging it needs), and every forced split either
     plans with at most that many splits or is refused, never anything else."""
     import itertools
-    KS = [128, 1024, 1152, 4096, 5120, 13696, 13824, 14336, 16384, 28672]
-    NS = [16, 256, 4096, 5120, 13824]
+    KS = [128, 1024, 1152, 4096, 5120, 8192, 13696, 13824, 14336, 16384, 28672]
+    NS = [16, 256, 4096, 5120, 13824, 22016, 28672]
     MS = [1, 2, 4, 5, 8, 9, 16, 17, 24, 32, 33, 64, 128, 129]
     n = 0
     for M, K, N, g, sdt, gu in itertools.product(MS, KS, NS, (16, 128), (0, 1), (0, 1)):
@@ -327,8 +329,14 @@ def test_plan_invariants_over_many_shapes(L):
         KC = K // 128
         want = (_lib.KERNEL_STREAM if M <= 16 else _lib.KERNEL_PANEL if M <= 32
                 else _lib.KERNEL_TILE)
-        # (a shape the panel kernel cannot take goes to the tile kernel)
-        assert info.kernel == want or (want == _lib.KERNEL_PANEL and info.kernel == _lib.KERNEL_TILE)
+        # every M <= 16 shape runs on the streaming kernel (the split-K
+        # counters cover N up to 65536), never on the 64-row tile kernel; the
+        # panel kernel takes every 16 < M <= 32 shape but one whose scale
+        # tables exceed its LDS (group 16, fp32 scales, two weight streams)
+        panel_lds = g == 16 and sdt == 1 and gu == 1
+        assert info.kernel == want or (want == _lib.KERNEL_PANEL and panel_lds
+                                       and info.kernel == _lib.KERNEL_TILE), \
+            (M, K, N, g, sdt, gu, info.kernel)
         assert 0 < info.lds_bytes <= 160 * 1024
         assert info.block in (256, 512)
         assert info.split >= 1 and info.grid[1] == info.split
@@ -338,7 +346,7 @@ def test_plan_invariants_over_many_shapes(L):
         if info.kernel != _lib.KERNEL_TILE:
             rows = 16 if info.kernel == _lib.KERNEL_STREAM else 32
             assert info.grid[2] == (M + rows - 1) // rows
-        stage = 4096 + M * K * 2 if M > 4 else 0
+        stage = CB + M * K * 2 if M > 4 else 0
         assert info.workspace_bytes >= stage
         assert info.workspace_bytes == max(plan(L, M, K, N, g, s, gu)[1].workspace_bytes
                                            for s in (sdt,))
