@@ -26,7 +26,7 @@ __all__ = [
     "PackedWeight", "repack", "gemm", "gemm_gate_up", "packed_bytes",
     "workspace_bytes", "layout_version", "add_bias", "relu", "rmsnorm",
     "probe_read", "probe_copy", "Workspace", "plan", "Plan", "W4A16Error",
-    "mlp", "mlp_workspace_bytes",
+    "mlp", "mlp_workspace_bytes", "gemm_noalloc",
 ]
 
 
@@ -242,6 +242,28 @@ def gemm(A: torch.Tensor, w: PackedWeight, *, epilogue: str = "none",
     else:
         st = _lib.lib().w4a16_gemm(*args, _stream())
     _lib.check(st, "w4a16_gemm")
+    return out
+
+
+def gemm_noalloc(A: torch.Tensor, w: PackedWeight, *, epilogue: str = "none",
+                 bias: Optional[torch.Tensor] = None, gamma: Optional[torch.Tensor] = None,
+                 eps: float = 1e-6, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """gemm() through w4a16_gemm_noalloc: no workspace argument; the library's
+    static per-device scratch holds what the workspace would (calls that
+    overlap on one GPU race).  Raises W4A16Error (W4A16_ERR_SCRATCH) for a
+    shape that needs more than that scratch."""
+    _check_operands(A, [w], out=out, bias=bias, gamma=gamma)
+    M, K = A.shape
+    if K != w.K:
+        raise ValueError(f"A has K={K}, weight has K={w.K}")
+    if epilogue not in _lib.EPI:
+        raise ValueError(f"unknown epilogue {epilogue!r}")
+    if out is None:
+        out = torch.empty((M, w.N), dtype=torch.float16, device=A.device)
+    st = _lib.lib().w4a16_gemm_noalloc(_ptr(A), M, K, w.N, w.group, w.scale_dtype,
+                                       int(w.has_zp), _ptr(w.data), _lib.EPI[epilogue],
+                                       _ptr(bias), _ptr(gamma), float(eps), _ptr(out), _stream())
+    _lib.check(st, "w4a16_gemm_noalloc")
     return out
 
 

@@ -26,10 +26,13 @@ ERR_WORKSPACE = -6
 ERR_ALIGN = -7
 ERR_LAUNCH = -8
 ERR_SPLIT = -9
+ERR_SCRATCH = -10
 
 # bytes of split-K arrival counters at the start of every workspace
 # (W4A16_COUNTER_BYTES)
 COUNTER_BYTES = 16384
+# the static scratch of w4a16_gemm_noalloc (W4A16_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 8 << 20
 
 KERNEL_STREAM = 1
 KERNEL_TILE = 2
@@ -45,7 +48,7 @@ EXPORTS = [
     "w4a16_add_bias", "w4a16_relu", "w4a16_rmsnorm", "w4a16_probe_read",
     "w4a16_probe_copy", "w4a16_plan", "w4a16_gemm_split", "w4a16_gemm_gate_up_split",
     "w4a16_gemm_skip_rmsnorm", "w4a16_gemm_gate_up_skip_rmsnorm",
-    "w4a16_mlp_workspace_bytes", "w4a16_mlp",
+    "w4a16_mlp_workspace_bytes", "w4a16_mlp", "w4a16_gemm_noalloc",
 ]
 
 
@@ -97,6 +100,7 @@ def lib() -> ctypes.CDLL:
         "w4a16_gemm_gate_up_skip_rmsnorm": (I, [P, P, P, I, I, I, I, I, I, P, P, P, F, P, P, Z, P]),
         "w4a16_mlp_workspace_bytes": (Z, [I, I, I, I]),
         "w4a16_mlp": (I, [P, P, P, I, I, I, I, I, I, P, P, P, P, F, P, P, P, Z, P]),
+        "w4a16_gemm_noalloc": (I, [P, I, I, I, I, I, I, P, I, P, P, F, P, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)

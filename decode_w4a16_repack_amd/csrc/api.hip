@@ -2,6 +2,8 @@
 // validation, launch planning and the kernel launches.  Validation always
 // runs before any HIP call, so every error status can be produced without a
 // GPU.
+#include <mutex>
+
 #include "../../include/w4a16.h"
 #include "common.h"
 
@@ -347,6 +349,86 @@ int w4a16_mlp(const void *A, const void *residual, void *residual_out, int M, in
   return st != W4A16_OK ? st : run(down, stream);
 }
 
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// The no-allocation entry point: w4a16_gemm with its workspace taken from a
+// fixed device array of the library instead of the caller.
+namespace {
+
+constexpr size_t kScratchBytes = (size_t)W4A16_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+
+// Split-K counters (first W4A16_COUNTER_BYTES), partial sums and RMSNorm
+// staging rows of w4a16_gemm_noalloc.  Each GPU the library runs on holds
+// its own copy for the life of the process.  In host code `scratch` is only
+// a stand-in for the symbol: its device address comes from
+// hipGetSymbolAddress (scratch_ptr below), never from the name itself.
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+__global__ void __launch_bounds__(256) zero_words_kernel(uint32_t *p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch`, looked up once per device (with
+// that device current); on the first lookup its split-K counters are
+// cleared by a fill kernel on `stream` (in stream order before the GEMM
+// that follows; no memset node, so the call stays capture-safe).
+int scratch_ptr(hipStream_t stream, void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return W4A16_ERR_LAUNCH;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+      (void)hipGetLastError();
+      return W4A16_ERR_LAUNCH;
+    }
+    const int words = (int)(kCounterBytes / 4);
+    hipLaunchKernelGGL(zero_words_kernel, dim3((words + 255) / 256), dim3(256), 0, stream,
+                       static_cast<uint32_t *>(ptr), words);
+    if (hipGetLastError() != hipSuccess) return W4A16_ERR_LAUNCH;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return W4A16_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int w4a16_gemm_noalloc(const void *A, int M, int K, int N, int group, int scale_dtype,
+                       int has_zp, const void *packed, int epilogue, const void *bias,
+                       const void *rms_gamma, float rms_eps, void *out, w4a16_stream stream) {
+  // validate and plan without a workspace first: every argument error is
+  // reported before any HIP call, and a call that needs a workspace
+  // stops at the workspace check with its plan filled in
+  Call c;
+  int st = prep_gemm(A, nullptr, nullptr, M, K, N, group, scale_dtype, has_zp, packed,
+                     epilogue, bias, rms_gamma, rms_eps, out, nullptr, 0, 0, c);
+  if (st != W4A16_OK && st != W4A16_ERR_WORKSPACE) return st;
+  const bool staged = staged_prologue(c.pl, M, rms_gamma != nullptr, false);
+  const size_t need = staged ? c.pl.ws_total_rms : c.pl.ws_total;
+  if (need > kScratchBytes) return W4A16_ERR_SCRATCH;
+  if (need > 0) {
+    void *ws = nullptr;
+    st = scratch_ptr(static_cast<hipStream_t>(stream), &ws);
+    if (st != W4A16_OK) return st;
+    st = prep_gemm(A, nullptr, nullptr, M, K, N, group, scale_dtype, has_zp, packed, epilogue,
+                   bias, rms_gamma, rms_eps, out, ws, kScratchBytes, 0, c);
+    if (st != W4A16_OK) return st;
+  }
+  return run(c, stream);
+}
+
 int w4a16_plan(int M, int K, int N, int group, int scale_dtype, int gate_up, int split,
                w4a16_plan_info *info) {
   if (info == nullptr) return W4A16_ERR_NULL;
@@ -394,6 +476,8 @@ const char *w4a16_status_string(int status) {
     case W4A16_ERR_ALIGN: return "device pointer not 16-byte aligned";
     case W4A16_ERR_LAUNCH: return "kernel launch failed";
     case W4A16_ERR_SPLIT: return "forced split-K factor not possible for this shape";
+    case W4A16_ERR_SCRATCH:
+      return "shape needs more workspace than the no-allocation entry point's static scratch";
     default: return "unknown status";
   }
 }

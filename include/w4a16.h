@@ -67,7 +67,9 @@ typedef enum {
   W4A16_ERR_WORKSPACE = -6, /* workspace NULL or smaller than required */
   W4A16_ERR_ALIGN = -7,     /* a device pointer is not 16-byte aligned */
   W4A16_ERR_LAUNCH = -8,    /* the HIP launch failed (hipGetLastError) */
-  W4A16_ERR_SPLIT = -9      /* a forced split-K factor the shape cannot use */
+  W4A16_ERR_SPLIT = -9,     /* a forced split-K factor the shape cannot use */
+  W4A16_ERR_SCRATCH = -10   /* the call needs more workspace than the static
+                               scratch of w4a16_gemm_noalloc holds */
 } w4a16_status;
 
 enum { W4A16_SCALE_F16 = 0, W4A16_SCALE_F32 = 1 };
@@ -266,6 +268,30 @@ int w4a16_mlp(const void *A, const void *residual, void *residual_out, int M,
               const void *packed_down, const void *rms_gamma, float rms_eps,
               void *inter, void *out, void *workspace, size_t workspace_bytes,
               w4a16_stream stream);
+
+/*
+ * w4a16_gemm without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Arguments, results and errors are
+ * those of w4a16_gemm.  The split-K partial sums, arrival counters and
+ * RMSNorm staging rows that w4a16_gemm keeps in the caller's workspace are
+ * kept instead in a fixed device array of the library,
+ * W4A16_NOALLOC_SCRATCH_BYTES long; each GPU the library runs on holds its
+ * own copy until the process ends.  A shape whose workspace need
+ * (w4a16_workspace_bytes, or the split-K part alone without a prologue)
+ * exceeds that size is refused with W4A16_ERR_SCRATCH before anything is
+ * enqueued.  The first call on a device looks up that device's copy and
+ * clears its counters with a fill kernel on `stream`; no call allocates,
+ * frees or synchronizes.  Every call on one GPU shares that GPU's array:
+ * calls that may overlap on one GPU (different streams, or host threads
+ * without ordering) race and must not be issued; calls ordered on one
+ * stream are safe, and each leaves the counters at zero.
+ */
+#define W4A16_NOALLOC_SCRATCH_BYTES (8u << 20)
+int w4a16_gemm_noalloc(const void *A, int M, int K, int N, int group, int scale_dtype,
+                       int has_zp, const void *packed, int epilogue, const void *bias,
+                       const void *rms_gamma, float rms_eps, void *out,
+                       w4a16_stream stream);
 
 /* Static, human-readable text for a w4a16_status value. */
 const char *w4a16_status_string(int status);

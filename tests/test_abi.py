@@ -41,7 +41,7 @@ def test_header_enums_match_binding():
                       ("W4A16_ERR_GROUP", -3), ("W4A16_ERR_DTYPE", -4),
                       ("W4A16_ERR_EPILOGUE", -5), ("W4A16_ERR_WORKSPACE", -6),
                       ("W4A16_ERR_ALIGN", -7), ("W4A16_ERR_LAUNCH", -8),
-                      ("W4A16_ERR_SPLIT", -9)]:
+                      ("W4A16_ERR_SPLIT", -9), ("W4A16_ERR_SCRATCH", -10)]:
         assert re.search(rf"{name}\s*=\s*{val}\b", text), name
         assert getattr(_lib, name[6:]) == val
     assert re.search(r"W4A16_EPI_BIAS_RELU\s*=\s*2", text)
@@ -51,7 +51,7 @@ def test_header_enums_match_binding():
 
 def test_layout_version_and_status_strings(L):
     assert L.w4a16_layout_version() == 1
-    for st in range(-9, 1):
+    for st in range(-10, 1):
         assert len(L.w4a16_status_string(st)) > 0
     assert L.w4a16_status_string(-99) == b"unknown status"
 
@@ -361,3 +361,25 @@ def test_plan_invariants_over_many_shapes(L):
                     assert f.k_tiles_per_split * (f.split - 1) < KC
                     assert f.kernel != _lib.KERNEL_TILE
     assert n == len(MS) * len(KS) * len(NS) * 8
+
+
+def test_noalloc_validates_and_refuses_before_any_hip_call(L):
+    """w4a16_gemm_noalloc reports argument errors like w4a16_gemm, and a shape
+    whose workspace need exceeds its static scratch with W4A16_ERR_SCRATCH,
+    all on the host (FAKE pointers are never dereferenced)."""
+    f = L.w4a16_gemm_noalloc
+    assert re.search(rf"#define W4A16_NOALLOC_SCRATCH_BYTES \(8u << 20\)", open(HEADER).read())
+    assert _lib.NOALLOC_SCRATCH_BYTES == 8 << 20
+    assert f(None, 2, 512, 512, 32, 0, 1, FAKE, 0, None, None, 1e-6, FAKE, None) == _lib.ERR_NULL
+    assert f(FAKE, 2, 500, 512, 32, 0, 1, FAKE, 0, None, None, 1e-6, FAKE, None) == _lib.ERR_SHAPE
+    assert f(FAKE, 2, 512, 512, 32, 0, 1, FAKE, 1, None, None, 1e-6, FAKE, None) == _lib.ERR_EPILOGUE
+    assert f(FAKE + 4, 2, 512, 512, 32, 0, 1, FAKE, 0, None, None, 1e-6, FAKE, None) == _lib.ERR_ALIGN
+    # staged RMSNorm rows of 640 x 8192 fp16 (10 MiB) exceed the 8 MiB scratch
+    M, K, N = 640, 8192, 256
+    assert L.w4a16_workspace_bytes(M, K, N, 128, 0) > _lib.NOALLOC_SCRATCH_BYTES
+    assert f(FAKE, M, K, N, 128, 0, 1, FAKE, 0, None, FAKE, 1e-6, FAKE, None) == _lib.ERR_SCRATCH
+    # split-K partials of 16 x 65536 over 2 splits (8 MiB + counters) exceed it too
+    st, info = plan(L, 16, 8192, 65536)
+    assert st == _lib.OK and info.split > 1 and info.workspace_bytes > _lib.NOALLOC_SCRATCH_BYTES
+    assert f(FAKE, 16, 8192, 65536, 128, 0, 1, FAKE, 0, None, None, 1e-6, FAKE, None) \
+        == _lib.ERR_SCRATCH
