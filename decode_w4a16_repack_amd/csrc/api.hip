@@ -357,7 +357,6 @@ int w4a16_mlp(const void *A, const void *residual, void *residual_out, int M, in
 namespace {
 
 constexpr size_t kScratchBytes = (size_t)W4A16_NOALLOC_SCRATCH_BYTES;
-constexpr int kMaxDevices = 64;
 
 // Split-K counters (first W4A16_COUNTER_BYTES), partial sums and RMSNorm
 // staging rows of w4a16_gemm_noalloc.  Each GPU the library runs on holds

@@ -23,6 +23,7 @@ constexpr int kTileBytes = 1024; // bytes of one packed tile (64 lanes x 16 B)
 // per column tile (stream kernel) or output tile (panel kernel), so split-K
 // is possible up to this many tiles (N <= 65536 on the stream kernel).
 constexpr int kMaxSplitBlocks = 4096;
+constexpr int kMaxDevices = 64;  // per-device host state (LDS limits, static scratch)
 constexpr size_t kCounterBytes = (size_t)kMaxSplitBlocks * 4;
 
 // Tile configurations of the small-M stream kernel: CPW 16-column tiles per

@@ -1,11 +1,38 @@
 // Device-side building blocks shared by the GEMM kernels.
 #pragma once
 
+#include <atomic>
 #include <type_traits>
 
 #include "common.h"
 
 namespace w4a16 {
+
+// Raises a kernel's dynamic-LDS limit on the current device to `bytes` when a
+// plan needs more than the default 64 KiB.  `limit` is the kernel's own
+// per-device record of the largest size already set, so repeated launches
+// (also under stream capture) make no attribute call; concurrent first
+// launches from several host threads may both set it, which is harmless.
+inline hipError_t raise_lds_limit(const void *kern, size_t bytes,
+                                  std::atomic<size_t> (&limit)[kMaxDevices]) {
+  if (bytes <= 64 * 1024) return hipSuccess;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return hipErrorInvalidDevice;
+  }
+  if (limit[dev].load(std::memory_order_acquire) >= bytes) return hipSuccess;
+  const hipError_t e =
+      hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();  // leave no sticky error for the caller's next launch
+    return e;
+  }
+  size_t cur = limit[dev].load(std::memory_order_acquire);
+  while (cur < bytes && !limit[dev].compare_exchange_weak(cur, bytes, std::memory_order_acq_rel)) {
+  }
+  return hipSuccess;
+}
 
 // Calls f(std::integral_constant<int, i>) for i = 0 .. N-1, unrolled at
 // compile time whatever the body's size (a #pragma unroll may give up on a

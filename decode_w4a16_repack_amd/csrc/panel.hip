@@ -273,9 +273,16 @@ panel_kernel(const GemmArgs p) {
     for (int j = 0; j < PPW; ++j) {
       const int pr = wk + NWK * j;
       f32x4 v = {0.f, 0.f, 0.f, 0.f};
-      if (pr < NPAIR)
+      if (pr < NPAIR) {
+        // every slice's partial read before any is added (one LDS round
+        // trip), then summed in slice order
+        f32x4 part[NWK];
+#pragma unroll
         for (int w2 = 0; w2 < NWK; ++w2)
-          v += reinterpret_cast<const f32x4 *>(smem + w2 * p.lds_s)[pr * 64 + lane];
+          part[w2] = reinterpret_cast<const f32x4 *>(smem + w2 * p.lds_s)[pr * 64 + lane];
+#pragma unroll
+        for (int w2 = 0; w2 < NWK; ++w2) v += part[w2];
+      }
       fin[i][j] = v;
     }
   }
@@ -368,19 +375,9 @@ panel_kernel(const GemmArgs p) {
 template <int MT, int CPW, int KPW, int NWK, int PD, bool ADB, int G, bool SF32, bool GU>
 hipError_t launch_t(const GemmArgs &a, const Plan &pl, hipStream_t stream) {
   auto kern = panel_kernel<MT, CPW, KPW, NWK, PD, ADB, G, SF32, GU>;
-  // Raise the kernel's dynamic-LDS limit above the default 64 KiB once; later
-  // launches (also under stream capture) make no attribute call.
-  static size_t lds_limit = 64 * 1024;
-  if (pl.lds_bytes > lds_limit) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)pl.lds_bytes);
-    if (e != hipSuccess) {
-      (void)hipGetLastError();  // leave no sticky error for the caller's next launch
-      return e;
-    }
-    lds_limit = pl.lds_bytes;
-  }
+  static std::atomic<size_t> lds_limit[kMaxDevices];
+  const hipError_t e = raise_lds_limit(reinterpret_cast<const void *>(kern), pl.lds_bytes, lds_limit);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(pl.gx, pl.gy, pl.gz), dim3(64 * NWK), pl.lds_bytes, stream, a);
   return hipGetLastError();
 }

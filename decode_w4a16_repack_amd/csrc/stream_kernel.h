@@ -379,22 +379,48 @@ stream_kernel(const GemmArgs p) {
     ss += __shfl_xor(ss, 32);
     if (lane < 16) lRms[wk * 16 + lane] = ss;
   }
-  lds_barrier();
   const int wfin = wk;  // the column tile this wavefront finishes (if < CPW)
-  if (wfin >= CPW || ct0 + wfin >= NTL) return;
+  const bool finisher = wfin < CPW && ct0 + wfin < NTL;
+  const int ncol = (ct0 + wfin) * kTileN + c;
+  // The epilogue's own inputs (bias, the staged rows' sums of squares) are
+  // loaded before the barrier, so that their latency overlaps the wait for
+  // the slowest slice instead of following the reduction: everything after
+  // the barrier is on the kernel's critical path.
+  float bias_v = 0.f;
+  f32x4 row_ss = {0.f, 0.f, 0.f, 0.f};
+  if (finisher) {
+    if (!GU && p.epilogue != 0) bias_v = (float)p.bias[ncol];
+    if (!rms && p.row_ss != nullptr) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (4 * kq + e < mrows) row_ss[e] = p.row_ss[m0 + 4 * kq + e];
+    }
+  }
+  lds_barrier();
+  if (!finisher) return;
+  // all NWK slice partials are read before any is added (one LDS round
+  // trip instead of a chain of them), then summed in slice order
   f32x4 fin[NW];
 #pragma unroll
   for (int i = 0; i < NW; ++i) {
-    f32x4 v = {0.f, 0.f, 0.f, 0.f};
+    f32x4 part[NWK];
+#pragma unroll
     for (int w2 = 0; w2 < NWK; ++w2)
-      v += reinterpret_cast<const f32x4 *>(smem + w2 * p.lds_s)[(i * CPW + wfin) * 64 + lane];
+      part[w2] = reinterpret_cast<const f32x4 *>(smem + w2 * p.lds_s)[(i * CPW + wfin) * 64 + lane];
+    f32x4 v = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w2 = 0; w2 < NWK; ++w2) v += part[w2];
     fin[i] = v;
   }
   // sums of squares of this lane's output rows 4*(l/16) + e
   f32x4 rs = {0.f, 0.f, 0.f, 0.f};
-  if (rms)
-    for (int w2 = 0; w2 < NWK; ++w2) rs += reinterpret_cast<const f32x4 *>(lRms + w2 * 16)[kq];
-  const int ncol = (ct0 + wfin) * kTileN + c;
+  if (rms) {
+    f32x4 part[NWK];
+#pragma unroll
+    for (int w2 = 0; w2 < NWK; ++w2) part[w2] = reinterpret_cast<const f32x4 *>(lRms + w2 * 16)[kq];
+#pragma unroll
+    for (int w2 = 0; w2 < NWK; ++w2) rs += part[w2];
+  }
 
   // 8. k splits across workgroups (narrow grids and very deep k only): the
   //    finishing wavefronts store partials; the finishing wavefront of the
@@ -454,13 +480,13 @@ stream_kernel(const GemmArgs p) {
       float rsc = 1.0f;
       if (rms) rsc = 1.0f / sqrtf(rs[e] / (float)p.K + p.eps);
       else if (p.row_ss != nullptr)  // rows staged by stage.hip
-        rsc = 1.0f / sqrtf(p.row_ss[m0 + row] / (float)p.K + p.eps);
+        rsc = 1.0f / sqrtf(row_ss[e] / (float)p.K + p.eps);
       float y;
       if constexpr (GU) {
         y = silu(fin[0][e] * rsc) * (fin[1][e] * rsc);
       } else {
         y = fin[0][e] * rsc;
-        if (p.epilogue != 0) y += (float)p.bias[ncol];
+        if (p.epilogue != 0) y += bias_v;
         if (p.epilogue == 2) y = y > 0.f ? y : 0.f;
       }
       p.out[(size_t)(m0 + row) * p.N + ncol] = (f16)y;
@@ -471,20 +497,9 @@ stream_kernel(const GemmArgs p) {
 template <int CPW, int KPW, int NWK, int PD, bool ALDS, int G, bool SF32, bool GU, int RMS>
 hipError_t launch_t(const GemmArgs &a, const Plan &pl, hipStream_t stream) {
   auto kern = stream_kernel<CPW, KPW, NWK, PD, ALDS, G, SF32, GU, RMS>;
-  // Raise the kernel's dynamic-LDS limit when a plan needs more than the
-  // default 64 KiB; only the first launch that needs a larger size makes the
-  // attribute call, so repeated launches (also under stream capture) make none.
-  static size_t lds_limit = 64 * 1024;
-  if (pl.lds_bytes > lds_limit) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)pl.lds_bytes);
-    if (e != hipSuccess) {
-      (void)hipGetLastError();  // leave no sticky error for the caller's next launch
-      return e;
-    }
-    lds_limit = pl.lds_bytes;
-  }
+  static std::atomic<size_t> lds_limit[kMaxDevices];
+  const hipError_t e = raise_lds_limit(reinterpret_cast<const void *>(kern), pl.lds_bytes, lds_limit);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(pl.gx, pl.gy, pl.gz), dim3(64 * NWK), pl.lds_bytes, stream, a);
   return hipGetLastError();
 }

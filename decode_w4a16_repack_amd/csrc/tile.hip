@@ -388,19 +388,9 @@ tile_kernel(const GemmArgs p) {
 template <int CT, int G, bool SF32, bool GU>
 hipError_t launch_t(const GemmArgs &a, const Plan &pl, hipStream_t stream) {
   auto kern = tile_kernel<CT, G, SF32, GU>;
-  // Raise the kernel's dynamic-LDS limit above the default 64 KiB once; later
-  // launches (also under stream capture) make no attribute call.
-  static size_t lds_limit = 64 * 1024;
-  if (pl.lds_bytes > lds_limit) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)pl.lds_bytes);
-    if (e != hipSuccess) {
-      (void)hipGetLastError();  // leave no sticky error for the caller's next launch
-      return e;
-    }
-    lds_limit = pl.lds_bytes;
-  }
+  static std::atomic<size_t> lds_limit[kMaxDevices];
+  const hipError_t e = raise_lds_limit(reinterpret_cast<const void *>(kern), pl.lds_bytes, lds_limit);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(pl.gx, pl.gy, pl.gz), dim3(64 * kTileNWave), pl.lds_bytes,
                      stream, a);
   return hipGetLastError();

@@ -86,6 +86,8 @@ def test_plan_reports_the_kernel_configuration():
     case to the configuration it is meant to cover."""
     p = w4.plan(1, 5120, 13824, 128)
     assert (p.kernel, p.col_tiles, p.k_tiles_per_wave, p.grid) == ("stream", 4, 5, (216, 1, 1))
+    p = w4.plan(8, 5120, 13824, 128, gate_up=True)
+    assert (p.kernel, p.col_tiles, p.k_tiles_per_wave, p.block) == ("stream", 4, 5, 512)
     p = w4.plan(1, 5120, 8192, 128)
     assert (p.kernel, p.col_tiles, p.k_tiles_per_wave, p.grid) == ("stream", 2, 5, (256, 1, 1))
     p = w4.plan(8, 13696, 4096, 128)

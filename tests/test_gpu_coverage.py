@@ -82,10 +82,22 @@ def test_stream_four_tile_blocks_ragged_last_block(M):
     """4 column tiles per workgroup at N = 13808 (863 tiles): 216 workgroups,
     the last one covering 3 tiles.  Rows through LDS (M <= 4) and loaded per
     k tile (M > 4); every output."""
-    expect_plan(M, 5120, 13808, 128, kernel="stream", col_tiles=4, grid=(216, 1, 1), split=1)
+    expect_plan(M, 5120, 13808, 128, kernel="stream", col_tiles=4, grid=(216, 1, 1), split=1,
+                kpw=5)
     assert ragged(13808, 4) == 3
     p = synth.make_problem(M, 5120, 13808, 128, seed=500 + M, bias=True)
     check_close(run(p, epilogue="bias"), ref(p, epilogue="bias"), f"N=13808 M={M}")
+
+
+@pytest.mark.parametrize("M", [2, 7])
+def test_stream_four_tiles_group16_gate_up(M):
+    """The four-tile configuration with two weight streams and group 16 (the
+    largest scale tables it takes), rows through LDS (M <= 4) and in
+    registers, with the ragged last block; every output."""
+    expect_plan(M, 5120, 13808, 16, kernel="stream", col_tiles=4, grid=(216, 1, 1), split=1,
+                kpw=5, gate_up=True)
+    p = synth.make_problem(M, 5120, 13808, 16, seed=600 + M, gate_up=True)
+    check_close(run(p, gate_up=True), ref(p, gate_up=True), f"k-sliced g16 gate_up M={M}")
 
 
 @pytest.mark.parametrize("M,K,N,grid", [(1, 4096, 8192, (256, 1, 1)), (1, 5120, 8192, (256, 1, 1)),
