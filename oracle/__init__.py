@@ -68,6 +68,8 @@ def _load():
         lib.oracle_packed_layout.argtypes = [I, I, I, I, I, P, P, P]
         lib.oracle_weight_nibble_index.argtypes = [I, I, I]
         lib.oracle_weight_nibble_index.restype = ctypes.c_long
+        lib.oracle_max_threads.argtypes = []
+        lib.oracle_max_threads.restype = ctypes.c_int
         lib.oracle_repack.argtypes = [P, P, P, I, I, I, I, P]
         lib.oracle_unrepack.argtypes = [P, I, I, I, I, I, P, P, P]
         for f in (lib.oracle_dequant, lib.oracle_gemm, lib.oracle_gate_up,
@@ -92,6 +94,11 @@ def _u8(a):
 def _check(rc, what):
     if rc != 0:
         raise ValueError(f"oracle {what} rejected its arguments (rc={rc})")
+
+
+def max_threads() -> int:
+    """OpenMP threads the oracle's parallel loops use in this process."""
+    return int(_load().oracle_max_threads())
 
 
 def dequant(qweight, scales, zeros, K: int, N: int, group: int) -> np.ndarray:

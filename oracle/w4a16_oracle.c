@@ -30,6 +30,9 @@
  */
 #include <math.h>
 #include <stddef.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 #include <stdint.h>
 #include <string.h>
 
@@ -110,6 +113,15 @@ static double dot_column(const double *x, const uint8_t *qweight,
 }
 
 static double silu(double v) { return v / (1.0 + exp(-v)); }
+
+/* Threads the OpenMP loops over output columns use (1 without OpenMP). */
+int oracle_max_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
 
 /*
  * Fused GEMM with optional RMSNorm prologue and bias / bias+ReLU epilogue.

@@ -80,3 +80,56 @@ def test_traffic_reported_only_for_the_current_kernel_sources(tmp_path, monkeypa
                              "bytes_per_launch": 37e6}))
     assert bench.load_traffic() == 37e6
 
+
+
+def test_sample_statistics():
+    st = bench.stats([5.0, 1.0, 3.0, 2.0, 4.0])
+    assert (st["median"], st["min"], st["max"], st["n"]) == (3.0, 1.0, 5.0, 5)
+    assert st["p10"] == pytest.approx(1.4) and st["p90"] == pytest.approx(4.6)
+
+
+def test_sweep_covers_the_variants():
+    """The M sweep holds the sizes of the metric, the odd edge tiles and the
+    symmetric and fp32-scale variants."""
+    import numpy as np
+    ms = {m for m, _, _ in bench.SWEEP}
+    assert {1, 2, 4, 7, 8, 16, 32, 33, 64, 128} <= ms
+    assert (1, np.float16, False) in bench.SWEEP and (128, np.float32, True) in bench.SWEEP
+
+
+def test_fusion_bytes_from_counter_csvs(tmp_path):
+    """summarize_fusion walks the library's dispatches in order (repacks and
+    other kernels skipped): per group, each path's kernels per call (1, 3, 1,
+    2), then the calibration copies."""
+    cb = bench.COPY_PROBE_BYTES
+    iters = 2
+    for counter, d, copy_kib in (("FETCH_SIZE", tmp_path / "f", cb / 1024 / 2),
+                                 ("WRITE_SIZE", tmp_path / "w", cb / 1024)):
+        d.mkdir()
+        rows, disp = [], 0
+
+        def add(name, kib):
+            nonlocal disp
+            disp += 1
+            rows.append((name, disp, [kib]))
+        add("w4a16::repack_weights_kernel(...)", 999)          # skipped
+        add("at::native::fill_kernel", 999)                    # not the library's
+        for g in bench.FUSION_GROUPS:
+            for name, k in bench.FUSION_PATHS:
+                for _ in range(iters):
+                    for j in range(k):
+                        add(f"w4a16::kernel_{name}_{j}", 10 * (j + 1) + g)
+        for _ in range(4):
+            add("w4a16::probe_copy_kernel(...)", copy_kib)
+        _counter_csv(d / "c_counter_collection.csv", counter, rows)
+    r = bench.summarize_fusion(str(tmp_path / "f"), str(tmp_path / "w"))
+    # FETCH scale 2, WRITE scale 1: a path of k kernels reads sum(10(j+1)+g) KiB each
+    for g in bench.FUSION_GROUPS:
+        for name, k in bench.FUSION_PATHS:
+            kib = sum(10 * (j + 1) + g for j in range(k))
+            assert r["groups"][str(g)][name] == pytest.approx(kib * 1024 * 2 + kib * 1024)
+    # a dispatch count that does not fit the sequence is refused
+    _counter_csv(tmp_path / "w" / "c_counter_collection.csv", "WRITE_SIZE",
+                 [("w4a16::kernel_x", 1, [1.0]), ("w4a16::probe_copy_kernel", 2, [cb / 1024])])
+    with pytest.raises(SystemExit):
+        bench.summarize_fusion(str(tmp_path / "f"), str(tmp_path / "w"))
