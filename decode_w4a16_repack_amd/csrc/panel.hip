@@ -319,27 +319,39 @@ panel_kernel(const GemmArgs p) {
     if (tid == 0) *flag = count_arrival(&p.ws_cnt[tile_id]) == (unsigned)(S - 1);
     __syncthreads();
     if (*flag == 0) return;
+    // split by split, in order, all of the wavefront's outputs at once: one
+    // round trip to memory per split (rows past M and columns past N read a
+    // clamped slot and are never written)
+    f32x4 sum[NW][PPW];
 #pragma unroll
-    for (int j = 0; j < PPW; ++j) {
-      const int pr = wk + NWK * j;
-      if (pr >= NPAIR) break;
-      const int mt = pr / CPW, w = pr % CPW;
-      const int ncol = min(ct0 + w, NTL - 1) * kTileN + c;
+    for (int i = 0; i < NW; ++i)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = 16 * mt + 4 * kq + e;
-        if (row < mrows && ct0 + w < NTL) {
+      for (int j = 0; j < PPW; ++j) sum[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int s2 = 0; s2 < S; ++s2) {
+      f32x4 v[NW][PPW];
 #pragma unroll
-          for (int i = 0; i < NW; ++i) {
-            float v = 0.f;
-            for (int s2 = 0; s2 < S; ++s2)
-              v += (s2 == s) ? fin[i][j][e]
-                             : load_agent(&p.ws_part[(((size_t)s2 * NW + i) * p.M + m0 + row) * p.N + ncol]);
-            fin[i][j][e] = v;
-          }
+      for (int j = 0; j < PPW; ++j) {
+        const int pr = min(wk + NWK * j, NPAIR - 1);
+        const int mt = pr / CPW, w = pr % CPW;
+        const int ncol = min(ct0 + w, NTL - 1) * kTileN + c;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int row = min(16 * mt + 4 * kq + e, mrows - 1);
+#pragma unroll
+          for (int i = 0; i < NW; ++i)
+            v[i][j][e] = (s2 == s) ? fin[i][j][e]
+                                   : load_agent(&p.ws_part[(((size_t)s2 * NW + i) * p.M + m0 + row) * p.N + ncol]);
         }
       }
+#pragma unroll
+      for (int i = 0; i < NW; ++i)
+#pragma unroll
+        for (int j = 0; j < PPW; ++j) sum[i][j] += v[i][j];
     }
+#pragma unroll
+    for (int i = 0; i < NW; ++i)
+#pragma unroll
+      for (int j = 0; j < PPW; ++j) fin[i][j] = sum[i][j];
     if (tid == 0) reset_arrival(&p.ws_cnt[tile_id]);
   }
 
