@@ -68,6 +68,8 @@ def _load():
         lib.oracle_packed_layout.argtypes = [I, I, I, I, I, P, P, P]
         lib.oracle_weight_nibble_index.argtypes = [I, I, I]
         lib.oracle_weight_nibble_index.restype = ctypes.c_long
+        lib.oracle_rmsnorm.argtypes = [P, I, I, P, D, P, P]
+        lib.oracle_rmsnorm.restype = ctypes.c_int
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = ctypes.c_int
         lib.oracle_repack.argtypes = [P, P, P, I, I, I, I, P]
@@ -147,6 +149,52 @@ def gate_up(A, gate, up, group: int, N: int, *, gamma=None, eps: float = 1e-6,
                             float(eps), _ptr(c), nc, _ptr(xw), _ptr(out))
     _check(rc, "gate_up")
     return out
+
+
+def rmsnorm(A, gamma, eps: float = 1e-6):
+    """(X, r): the f64 RMSNorm prologue X[m][k] = A[m][k] * gamma[k] * r[m],
+    r[m] = 1 / sqrt(mean_k A[m][k]^2 + eps) (eps inside the root, mean over
+    the whole row)."""
+    lib = _load()
+    A = _f64(A)
+    M, K = A.shape
+    g = _f64(gamma)
+    X = np.empty((M, K), dtype=np.float64)
+    r = np.empty(M, dtype=np.float64)
+    _check(lib.oracle_rmsnorm(_ptr(A), M, K, _ptr(g), float(eps), _ptr(X), _ptr(r)), "rmsnorm")
+    return X, r
+
+
+def gemm_rms_staged(A, qweight, scales, zeros, group: int, N: int, gamma, *,
+                    eps: float = 1e-6, staging: str = "normalized",
+                    epilogue: str = "none", bias=None, cols=None) -> np.ndarray:
+    """The fused GEMM with the RMSNorm prologue under the staged readings
+    of the "fused RMS-norm epilogue" update, which keeps the prologue's
+    result in fp16 scratch between the norm and the product:
+
+    * ``staging="normalized"``: X16 = fp16(X) (X as in :func:`rmsnorm`),
+      then the product and epilogue on X16;
+    * ``staging="scaled"``: X16 = fp16(A * gamma) (each product rounded
+      once), the product on X16, each row times r[m], then the epilogue.
+
+    Every other step is the canonical oracle's, in f64; only the one fp16
+    rounding of the staged row differs, so the gap to :func:`gemm` with
+    ``gamma`` is bounded by that rounding (pinned in the tests)."""
+    A64 = _f64(A)
+    X, r = rmsnorm(A64, gamma, eps)
+    if staging == "normalized":
+        return gemm(to_fp16(X), qweight, scales, zeros, group, N, epilogue=epilogue,
+                    bias=bias, cols=cols)
+    if staging != "scaled":
+        raise ValueError(f"unknown staging {staging!r}")
+    xg = to_fp16(A64 * _f64(gamma)[None, :])
+    y = gemm(xg, qweight, scales, zeros, group, N, cols=cols) * r[:, None]
+    if epilogue == "none":
+        return y
+    b = _f64(bias)
+    b = b if cols is None else b[np.asarray(cols)]
+    y = y + b[None, :]
+    return np.maximum(y, 0.0) if epilogue == "bias_relu" else y
 
 
 def packed_layout(K: int, N: int, group: int, esize: int, has_zp: bool):

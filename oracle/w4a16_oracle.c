@@ -97,6 +97,27 @@ static void rmsnorm_row(const double *a, const double *gamma, double eps,
   for (int k = 0; k < K; ++k) x[k] = a[k] * gamma[k] * inv;
 }
 
+/*
+ * The RMSNorm prologue alone (the same rmsnorm_row per row):
+ *   A f64[M][K], gamma f64[K], x f64[M][K] out.  Also returns, when r is not
+ *   NULL, the row factor r[m] = 1 / sqrt((1/K) * sum_k A[m][k]^2 + eps).
+ * The staged readings of the prologue (the normalized row, or A * gamma,
+ * kept as fp16 between the norm and the product) are built from these.
+ */
+int oracle_rmsnorm(const double *A, int M, int K, const double *gamma, double eps,
+                   double *x, double *r) {
+  if (A == NULL || gamma == NULL || x == NULL || M < 1 || K < 1) return ORACLE_ERR;
+  for (int m = 0; m < M; ++m) {
+    rmsnorm_row(A + (long)m * K, gamma, eps, K, x + (long)m * K);
+    if (r != NULL) {
+      double ss = 0.0;
+      for (int k = 0; k < K; ++k) ss += A[(long)m * K + k] * A[(long)m * K + k];
+      r[m] = 1.0 / sqrt(ss / (double)K + eps);
+    }
+  }
+  return ORACLE_OK;
+}
+
 /* y = sum_k x[k] * w[k][n] for one column, dequantizing as it goes. */
 static double dot_column(const double *x, const uint8_t *qweight,
                          const double *scales, const uint8_t *zeros, int K,

@@ -208,6 +208,48 @@ def test_rmsnorm_scale_invariant_at_zero_eps(oracle_lib):
     assert np.allclose(y, (A[:, k0] * r)[:, None] * W[k0][None, :], rtol=1e-14, atol=0)
 
 
+@pytest.mark.parametrize("staging", ["normalized", "scaled"])
+def test_rms_staged_exact_when_the_staged_row_is_representable(oracle_lib, staging):
+    """A row of +-1 with eps = 0 has mean square exactly 1, so X = +-gamma
+    and A * gamma = +-gamma are fp16 values already: the staged readings
+    round nothing and equal the canonical oracle bit for bit."""
+    rng = np.random.default_rng(41)
+    K, N, group = 256, 32, 64
+    p = synth.make_problem(1, K, N, group, seed=42, gamma=True, bias=True)
+    A = rng.choice([-1.0, 1.0], size=(3, K)).astype(np.float16)
+    w = (p.w.qweight, p.w.scales, p.w.zeros)
+    for epi in ("none", "bias_relu"):
+        ref = oracle.gemm(A, *w, group, N, gamma=p.gamma, eps=0.0, epilogue=epi, bias=p.bias)
+        got = oracle.gemm_rms_staged(A, *w, group, N, p.gamma, eps=0.0, staging=staging,
+                                     epilogue=epi, bias=p.bias)
+        assert np.array_equal(got, ref), (staging, epi)
+
+
+@pytest.mark.parametrize("staging", ["normalized", "scaled"])
+def test_rms_staged_gap_within_the_fp16_rounding_bound(oracle_lib, staging):
+    """The staged row differs from the exact one only by one round-to-nearest
+    to fp16: relative error at most 2^-11 for a normal result, absolute at
+    most 2^-25 below 2^-14.  So |Y_staged - Y| <= sum_k (2^-11 |X_k| +
+    2^-25) |W_kn| (for the scaled reading the row factor r > 0 carries the
+    bound over unchanged), and the gap must also be far inside the parity
+    tolerance 2e-2 max|Y| (a twentieth of it here; about a hundredth is
+    measured); a staging that rounds nothing would show no gap at all."""
+    K, N, group = 1024, 64, 128
+    p = synth.make_problem(4, K, N, group, seed=43, gamma=True)
+    w = (p.w.qweight, p.w.scales, p.w.zeros)
+    ref = oracle.gemm(p.A, *w, group, N, gamma=p.gamma, eps=1e-6)
+    got = oracle.gemm_rms_staged(p.A, *w, group, N, p.gamma, eps=1e-6, staging=staging)
+    X, r = oracle.rmsnorm(p.A, p.gamma, 1e-6)
+    assert np.allclose(X, p.A.astype(np.float64) * p.gamma.astype(np.float64) * r[:, None],
+                       rtol=1e-15, atol=0)
+    W = np.abs(oracle.dequant(p.w.qweight, p.w.scales, p.w.zeros, K, N, group))
+    bound = (2.0 ** -11) * (np.abs(X) @ W) + (2.0 ** -25) * W.sum(axis=0)[None, :]
+    gap = np.abs(got - ref)
+    assert (gap <= bound * (1 + 1e-9) + 1e-12).all(), staging
+    assert gap.max() > 0.0
+    assert gap.max() < 0.05 * 2e-2 * np.abs(ref).max()
+
+
 # --------------------------------------------------------------------- gate_up
 
 
@@ -388,6 +430,47 @@ def test_repack_round_trip(oracle_lib, sdt, asym, K, N, group):
         zn = np.stack([zb & 15, zb >> 4], axis=1).reshape(N // 16, G, 16)
         assert np.array_equal(zn.transpose(0, 2, 1).reshape(N, G), p.w.zp)
     assert not packed[K * N // 2: so].any()
+
+
+@pytest.mark.parametrize("esize", [2, 4])
+@pytest.mark.parametrize("has_zp", [True, False])
+def test_repack_metadata_positions_golden(oracle_lib, esize, has_zp):
+    """Scale and zero-point positions worked out by hand from the layout's
+    text (tests/golden/repack_meta_index.json): one marked scale and one
+    marked zero-point at a time, every other byte of both regions zero."""
+    g = _load("repack_meta_index.json")
+    K, N, group = g["K"], g["N"], g["group"]
+    G = K // group
+    lay = next(x for x in g["layout"] if x["esize"] == esize and x["has_zp"] == has_zp)
+    so, zo, total = oracle.packed_layout(K, N, group, esize, has_zp)
+    assert so == lay["scales_offset"] and total == lay["total"]
+    if has_zp:
+        assert zo == lay["zeros_offset"]
+    sdt = np.float16 if esize == 2 else np.float32
+    q = np.zeros((N, K // 2), np.uint8)
+    marker = np.array(1.5, sdt)  # 0x3E00 / 0x3FC00000: nonzero high byte
+    for c in g["scales"]:
+        s = np.zeros((N, G), sdt)
+        s[c["n"], c["i"]] = marker
+        z = np.zeros((N, (G + 1) // 2), np.uint8) if has_zp else None
+        packed = oracle.repack(q, s, z, K, N, group)
+        at = so + c["index"] * esize
+        assert packed[at: at + esize].tobytes() == marker.tobytes(), c
+        region = packed[so: so + N * G * esize].copy()
+        region[c["index"] * esize: (c["index"] + 1) * esize] = 0
+        assert not region.any(), c
+    if not has_zp:
+        return
+    for c in g["zeros"]:
+        z = np.zeros((N, (G + 1) // 2), np.uint8)
+        i = c["i"]
+        z[c["n"], i // 2] = 0xA << (4 * (i % 2))  # zero-point 10 in its canonical nibble
+        packed = oracle.repack(q, np.zeros((N, G), sdt), z, K, N, group)
+        b = packed[zo + c["byte"]]
+        assert b == (0xA0 if c["high"] else 0x0A), c
+        region = packed[zo: zo + N * G // 2].copy()
+        region[c["byte"]] = 0
+        assert not region.any(), c
 
 
 def test_packed_sizes_decode_shape(oracle_lib):
