@@ -23,7 +23,7 @@ all host cores and on one, and its result checks the timed GPU output.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
                        [--profile-kernel M [--eager] [--gate-up]] [--profile-mlp M]
-                       [--profile-fusion]
+                       [--profile-fusion] [--probes]
                        [--traffic-summary FETCH_DIR WRITE_DIR]
                        [--fusion-summary FETCH_DIR WRITE_DIR]
                        [--counter-summary DIR [--kernel-filter S]]
@@ -38,6 +38,8 @@ sources are unchanged).  --profile-fusion and --fusion-summary do the same for
 the fused and unfused chains of the group sweep
 (profiles/fusion_bytes_m16_k4096_n4096.json).  --counter-summary prints the
 mean per dispatch of every counter in a rocprofv3 --pmc output directory.
+--probes runs only the streaming-read HBM probe and the two compute-unit
+probes (LDS read rate, L2 -> LDS copy rate) and prints them as JSON.
 """
 from __future__ import annotations
 
@@ -653,6 +655,45 @@ def hbm_probe(nbytes=1 << 30, reps=20):
     return nbytes / float(np.median(times)) / 1e9
 
 
+def cu_probes():
+    """One compute unit's data paths, the limits of the MFMA-tile kernel: the
+    LDS read rate (1024 workgroups of 512 threads, 2000 x 16 KiB read per
+    wavefront) and the global-to-LDS copy rate of a 64 x 5120 fp16 matrix
+    held in L2 (216 workgroups, the tile kernel's grid at M=128, 160 steps
+    of 32 KiB each), both per compute unit (256 CUs for the first: 1024
+    workgroups spread over all of them; 216 for the second, one workgroup
+    each).  Medians of 5 timed launches with HIP events."""
+    import torch
+    import decode_w4a16_repack_amd as w4
+    sink = torch.zeros(1024 * 512, dtype=torch.int32, device="cuda")
+    rows = torch.randn(64, 5120, device="cuda").half()
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(5):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            b.synchronize()
+            ts.append(a.elapsed_time(b) * 1e-3)
+        return float(np.median(ts))
+
+    t_read = timed(lambda: w4.probe_lds_read(1024, 2000, sink))
+    read_bytes = 1024 * 512 * 2000 * 256
+    t_copy = timed(lambda: w4.probe_lds_copy(rows, 216, 160, sink))
+    copy_bytes = 216 * 161 * 32 * 1024
+    return {"lds_read_GBps_per_cu": read_bytes / t_read / 1e9 / 256,
+            "lds_read_seconds": t_read,
+            "l2_to_lds_copy_GBps_per_cu": copy_bytes / t_copy / 1e9 / 216,
+            "l2_to_lds_copy_seconds": t_copy,
+            "what": "LDS read: 1024 workgroups x 512 threads, 2000 x 16 KiB per wavefront; "
+                    "L2 -> LDS copy: 216 workgroups, 161 x 32 KiB each of a 640 KiB fp16 "
+                    "matrix, two steps in flight, one barrier per step"}
+
+
 def cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -862,6 +903,8 @@ def main():
                     help="only run the fusion comparison's paths eagerly (for rocprofv3 --pmc)")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--fusion-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--probes", action="store_true",
+                    help="only the HBM and compute-unit probes (JSON on stdout)")
     ap.add_argument("--counter-summary", metavar="DIR")
     ap.add_argument("--kernel-filter", default="")
     args = ap.parse_args()
@@ -890,6 +933,9 @@ def main():
 
     if args.profile_fusion:
         profile_fusion()
+        return
+    if args.probes:
+        print(json.dumps({"hbm_probe_GBps": hbm_probe(), "cu_probes": cu_probes()}, indent=1))
         return
     if args.profile_mlp:
         M = args.profile_mlp
@@ -980,6 +1026,9 @@ def main():
     extra = None if args.no_extras else extras(ws)
     probe = hbm_probe()
     log(f"[bench] streaming-read probe: {probe:.1f} GB/s")
+    cu = cu_probes()
+    log(f"[bench] compute-unit probes: LDS read {cu['lds_read_GBps_per_cu']:.0f} GB/s per CU, "
+        f"L2 -> LDS copy {cu['l2_to_lds_copy_GBps_per_cu']:.0f} GB/s per CU")
     cpu = None if args.no_cpu else cpu_baseline(gpu_out)
     if cpu:
         log(f"[bench] cpu oracle: {cpu['value']:.3f} GB/s on {cpu['cores']} threads"
@@ -1009,6 +1058,7 @@ def main():
         "tflops": flops(1) / us_mean / 1e6,
         "pct_hbm_peak": 100 * value / HBM_PEAK_GBS,
         "hbm_probe_GBps": probe,
+        "cu_probes": cu,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": load_traffic(),
                      "algorithmic_bytes_per_launch": b1, "avg_launch_us": us_mean},

@@ -25,7 +25,7 @@ from ._lib import W4A16Error
 __all__ = [
     "PackedWeight", "repack", "gemm", "gemm_gate_up", "packed_bytes",
     "workspace_bytes", "layout_version", "add_bias", "relu", "rmsnorm",
-    "probe_read", "probe_copy", "Workspace", "plan", "Plan", "W4A16Error",
+    "probe_read", "probe_copy", "probe_lds_read", "probe_lds_copy", "Workspace", "plan", "Plan", "W4A16Error",
     "mlp", "mlp_workspace_bytes", "gemm_noalloc",
 ]
 
@@ -440,3 +440,27 @@ def probe_copy(src: torch.Tensor, dst: torch.Tensor) -> None:
     _lib.check(_lib.lib().w4a16_probe_copy(_ptr(src), _ptr(dst),
                                            src.numel() * src.element_size(), _stream()),
                "w4a16_probe_copy")
+
+
+def probe_lds_read(workgroups: int, iters: int, sink: torch.Tensor) -> None:
+    """w4a16_probe_lds_read: workgroups x 512 threads read iters x 16 KiB of
+    LDS per wavefront; sink (device, >= workgroups * 512 int32) gets one word
+    per thread."""
+    _need_gpu(sink, "sink")
+    if sink.numel() * sink.element_size() < workgroups * 512 * 4:
+        raise ValueError("sink needs workgroups * 512 * 4 bytes")
+    _lib.check(_lib.lib().w4a16_probe_lds_read(int(workgroups), int(iters), _ptr(sink), _stream()),
+               "w4a16_probe_lds_read")
+
+
+def probe_lds_copy(buf: torch.Tensor, workgroups: int, steps: int, sink: torch.Tensor) -> None:
+    """w4a16_probe_lds_copy: copies of the 64-row fp16 matrix in buf
+    (device, a multiple of 16 KiB) into LDS, 32 KiB per workgroup and step."""
+    _need_gpu(buf, "buf")
+    _need_gpu(sink, "sink", device=buf.device)
+    if sink.numel() * sink.element_size() < workgroups * 512 * 4:
+        raise ValueError("sink needs workgroups * 512 * 4 bytes")
+    _lib.check(_lib.lib().w4a16_probe_lds_copy(_ptr(buf), buf.numel() * buf.element_size(),
+                                               int(workgroups), int(steps), _ptr(sink), _stream()),
+               "w4a16_probe_lds_copy")
+

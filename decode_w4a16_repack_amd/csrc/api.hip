@@ -526,4 +526,23 @@ int w4a16_probe_copy(const void *src, void *dst, size_t bytes, w4a16_stream stre
   return launched(launch_probe_copy(src, dst, bytes, static_cast<hipStream_t>(stream)));
 }
 
+int w4a16_probe_lds_read(int workgroups, int iters, void *sink, w4a16_stream stream) {
+  if (sink == nullptr) return W4A16_ERR_NULL;
+  if (workgroups < 1 || workgroups > 65535 || iters < 1 || iters > (1 << 20)) return W4A16_ERR_SHAPE;
+  if (!aligned16(sink)) return W4A16_ERR_ALIGN;
+  return launched(launch_probe_lds_read(workgroups, iters, static_cast<uint32_t *>(sink),
+                                        static_cast<hipStream_t>(stream)));
+}
+
+int w4a16_probe_lds_copy(const void *buf, size_t bytes, int workgroups, int steps, void *sink,
+                         w4a16_stream stream) {
+  if (buf == nullptr || sink == nullptr) return W4A16_ERR_NULL;
+  if (bytes < 16384 || bytes % 16384 != 0 || bytes / 16384 > (size_t)kMaxDim || workgroups < 1 ||
+      workgroups > 65535 || steps < 1 || steps > (1 << 20))
+    return W4A16_ERR_SHAPE;
+  if (!aligned16(buf) || !aligned16(sink)) return W4A16_ERR_ALIGN;
+  return launched(launch_probe_lds_copy(buf, bytes, workgroups, steps, static_cast<uint32_t *>(sink),
+                                        static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -1,5 +1,7 @@
-// Measurement aids: the separate passes of the unfused chain, and streaming
-// probes for the achievable HBM rate.
+// Measurement aids: the separate passes of the unfused chain, streaming
+// probes for the achievable HBM rate, and two probes of a compute unit's
+// own data paths (LDS reads, and global-to-LDS copies of data held in L2)
+// that bound the MFMA-tile kernel.
 //
 // The "Fusion benchmark" page measures a fused kernel against the unfused
 // chain at the same shape: matmul, then a bias pass, then a ReLU pass, each
@@ -108,6 +110,68 @@ probe_copy_kernel(const u32x4 *__restrict__ src, u32x4 *__restrict__ dst,
     dst[v] = src[v];
 }
 
+// LDS read rate: each 512-thread workgroup fills 64 KiB of LDS, then every
+// wavefront reads 16 chunks of 16 bytes per iteration (lane l of read r:
+// chunk (l + 64 * ((r + wave + it) mod 64)) mod 4096, conflict-free) and
+// folds them into one word per thread, written to sink[workgroup * 512 +
+// thread].
+__global__ void __launch_bounds__(512) probe_lds_read_kernel(int iters, uint32_t *sink) {
+  __shared__ u32x4 buf[4096];
+  const int t = threadIdx.x;
+  for (int i = t; i < 4096; i += 512) buf[i] = u32x4{(uint32_t)i, 1u, 2u, 3u};
+  __syncthreads();
+  u32x4 acc = {0, 0, 0, 0};
+  const int lane = t & 63, w = t >> 6;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc ^= buf[(lane + 64 * ((r + w + it) & 63)) & 4095];
+  }
+  sink[(size_t)blockIdx.x * 512 + t] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+}
+
+// Global-to-LDS copy rate of activation-like rows held in L2: buf is a
+// 64-row fp16 matrix of K = bytes / 128 columns.  Per step, wavefront
+// (wc, ks) of a 512-thread workgroup copies a quarter (four 1 KiB copies of
+// four whole 256-byte row segments each, the MFMA-tile kernel's activation
+// copy) of the 64 x 128 k tile 2 * step + ks + workgroup (mod K / 128) into a
+// two-step ring, waits for the previous step's copies, meets the workgroup,
+// and reads 16 bytes per lane back; one word per thread goes to sink.
+__global__ void __launch_bounds__(512) probe_lds_copy_kernel(const uint8_t *buf, int KC, int steps,
+                                                             uint32_t *sink) {
+  __shared__ __attribute__((aligned(16))) uint8_t ring[8 * 2 * 4096];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, wc = w & 3, ks = w >> 2;
+  const size_t K = (size_t)KC * 128;
+  uint32_t off[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int sl = (wc + 4 * q) * 64 + lane;
+    const int row = sl >> 4, chunk = (sl & 15) ^ (row & 15);
+    off[q] = (uint32_t)((row * K + 8 * chunk) * 2);
+  }
+  uint8_t *mine = ring + w * 2 * 4096;
+  auto issue = [&](int step, int slot) {
+    const int kt = (int)((2u * (unsigned)step + (unsigned)ks + blockIdx.x) % (unsigned)KC);
+    const uint8_t *base = buf + (size_t)kt * 256;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1))) *)(base + off[q]),
+                                       (void __attribute__((address_space(3))) *)(mine + slot * 4096 + q * 1024),
+                                       16, 0, 0);
+  };
+  u32x4 acc = {0, 0, 0, 0};
+  issue(0, 0);
+  for (int s = 0; s < steps; ++s) {
+    issue(s + 1, (s + 1) & 1);  // (the last step's extra copy is waited for below)
+    __builtin_amdgcn_s_waitcnt((4 & 15) | (7 << 4) | (15 << 8));  // vmcnt(4): step s landed
+    __builtin_amdgcn_s_barrier();
+    acc ^= *reinterpret_cast<const u32x4 *>(mine + (s & 1) * 4096 + lane * 16);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): read back before the slot is refilled
+    __builtin_amdgcn_s_barrier();
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  sink[(size_t)blockIdx.x * 512 + t] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+}
+
 unsigned grid_for(size_t vecs, unsigned cap) {
   size_t b = (vecs + 255) / 256;
   if (b > cap) b = cap;
@@ -154,6 +218,18 @@ hipError_t launch_probe_copy(const void *src, void *dst, size_t bytes,
   hipLaunchKernelGGL(probe_copy_kernel, dim3(grid_for(vecs / 4, 8192)), dim3(256),
                      0, stream, reinterpret_cast<const u32x4 *>(src),
                      reinterpret_cast<u32x4 *>(dst), vecs);
+  return hipGetLastError();
+}
+
+hipError_t launch_probe_lds_read(int workgroups, int iters, uint32_t *sink, hipStream_t stream) {
+  hipLaunchKernelGGL(probe_lds_read_kernel, dim3(workgroups), dim3(512), 0, stream, iters, sink);
+  return hipGetLastError();
+}
+
+hipError_t launch_probe_lds_copy(const void *buf, size_t bytes, int workgroups, int steps,
+                                 uint32_t *sink, hipStream_t stream) {
+  hipLaunchKernelGGL(probe_lds_copy_kernel, dim3(workgroups), dim3(512), 0, stream,
+                     static_cast<const uint8_t *>(buf), (int)(bytes / 16384), steps, sink);
   return hipGetLastError();
 }
 

@@ -325,6 +325,29 @@ int w4a16_probe_read(const void *buf, size_t bytes, void *sink,
 int w4a16_probe_copy(const void *src, void *dst, size_t bytes,
                      w4a16_stream stream);
 
+/*
+ * Probes of one compute unit's data paths, the limits of the MFMA-tile
+ * kernel (M > 32), which moves each step's 64-row activation tile from L2
+ * into LDS and reads it back from LDS once per wavefront.  Both launch
+ * `workgroups` workgroups of 512 threads and write one 32-bit value per
+ * thread to sink (at least workgroups * 512 * 4 bytes), so nothing is
+ * elided.
+ *   w4a16_probe_lds_read: 64 KiB of LDS per workgroup, then every
+ *     wavefront reads iters * 16 KiB from it (16-byte conflict-free reads):
+ *     workgroups * 512 * iters * 256 bytes in all.
+ *   w4a16_probe_lds_copy: buf holds a 64-row fp16 matrix of bytes / 128
+ *     columns (bytes a multiple of 16384, read-only, small enough to stay in
+ *     L2); per step every workgroup copies one 64 x 128 k tile per pair of
+ *     wavefronts (32 KiB) into LDS with direct global-to-LDS loads of whole
+ *     256-byte row segments, two steps in flight, one barrier per step:
+ *     workgroups * (steps + 1) * 32 KiB in all.
+ * W4A16_ERR_SHAPE for workgroups outside 1..65535, iters or steps outside
+ * 1..2^20, or a bad byte count.
+ */
+int w4a16_probe_lds_read(int workgroups, int iters, void *sink, w4a16_stream stream);
+int w4a16_probe_lds_copy(const void *buf, size_t bytes, int workgroups, int steps, void *sink,
+                         w4a16_stream stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -124,6 +124,16 @@ def test_aux_validation(L):
     assert L.w4a16_rmsnorm(FAKE, FAKE, 1e-6, 2, 100, FAKE, None) == _lib.ERR_SHAPE
     assert L.w4a16_probe_read(FAKE, 15, FAKE, None) == _lib.ERR_SHAPE
     assert L.w4a16_probe_copy(FAKE, FAKE + 4, 16, None) == _lib.ERR_ALIGN
+    assert L.w4a16_probe_lds_read(4, 10, None, None) == _lib.ERR_NULL
+    assert L.w4a16_probe_lds_read(0, 10, FAKE, None) == _lib.ERR_SHAPE
+    assert L.w4a16_probe_lds_read(4, 0, FAKE, None) == _lib.ERR_SHAPE
+    assert L.w4a16_probe_lds_read(4, 10, FAKE + 4, None) == _lib.ERR_ALIGN
+    assert L.w4a16_probe_lds_copy(None, 16384, 4, 10, FAKE, None) == _lib.ERR_NULL
+    assert L.w4a16_probe_lds_copy(FAKE, 16000, 4, 10, FAKE, None) == _lib.ERR_SHAPE
+    assert L.w4a16_probe_lds_copy(FAKE, 8192, 4, 10, FAKE, None) == _lib.ERR_SHAPE
+    assert L.w4a16_probe_lds_copy(FAKE, 16384, 70000, 10, FAKE, None) == _lib.ERR_SHAPE
+    assert L.w4a16_probe_lds_copy(FAKE, 16384, 4, 0, FAKE, None) == _lib.ERR_SHAPE
+    assert L.w4a16_probe_lds_copy(FAKE + 4, 16384, 4, 10, FAKE, None) == _lib.ERR_ALIGN
 
 
 def test_workspace_only_for_narrow_grids(L):

@@ -478,6 +478,12 @@ def test_probes():
     w4.probe_read(src, sink)
     torch.cuda.synchronize()
     assert torch.equal(src, dst)
+    # the compute-unit probes: small launches that must complete cleanly
+    sink2 = torch.zeros(8 * 512, dtype=torch.int32, device="cuda")
+    w4.probe_lds_read(8, 4, sink2)
+    rows = torch.randn(64, 1024, device="cuda").half()
+    w4.probe_lds_copy(rows, 8, 5, sink2)
+    torch.cuda.synchronize()
 
 
 # ------------------------------------------------------- deepest k range
