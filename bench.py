@@ -385,8 +385,10 @@ def summarize_fusion(fetch_dir, write_dir):
     res = {"kernel_source_hash": kernel_source_hash(), "copy_probe_bytes": COPY_PROBE_BYTES,
            "groups": {}}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        # (the library's kernels: demangled "w4a16::..." names, or mangled
+        # "_ZN5w4a16..." ones where rocprofv3 leaves them so)
         ds = [(n, v) for _, n, v in _dispatches(d, counter)
-              if "w4a16::" in n and "repack" not in n]
+              if "w4a16" in n and "repack" not in n]
         copies = [v for n, v in ds if "probe_copy_kernel" in n]
         ds = [(n, v) for n, v in ds if "probe_copy_kernel" not in n]
         if not copies:
