@@ -449,30 +449,26 @@ stream_kernel(const GemmArgs p) {
     if (lane == 0) last = count_arrival(&p.ws_cnt[cnt]) == (unsigned)(S - 1);
     last = __shfl(last, 0);
     if (!last) return;
-    // split by split, in order, all of the lane's outputs at once: one
-    // round trip to memory per split (rows past M read row M - 1's slot and
-    // are never written)
-    f32x4 sum[NW], rsum = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < NW; ++i) sum[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int s2 = 0; s2 < S; ++s2) {
-      f32x4 v[NW], rv;
+    for (int e = 0; e < 4; ++e) {
+      const int row = 4 * kq + e;
+      if (row < mrows) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = min(4 * kq + e, mrows - 1);
-#pragma unroll
-        for (int i = 0; i < NW; ++i)
-          v[i][e] = (s2 == s) ? fin[i][e]
-                              : load_agent(&p.ws_part[(((size_t)s2 * NW + i) * p.M + m0 + row) * p.N + ncol]);
-        if (rms) rv[e] = (s2 == s) ? rs[e] : load_agent(&p.ws_rms[(cnt * S + s2) * 16 + row]);
+        for (int i = 0; i < NW; ++i) {
+          float v = 0.f;
+          for (int s2 = 0; s2 < S; ++s2)
+            v += (s2 == s) ? fin[i][e]
+                           : load_agent(&p.ws_part[(((size_t)s2 * NW + i) * p.M + m0 + row) * p.N + ncol]);
+          fin[i][e] = v;
+        }
+        if (rms) {
+          float v = 0.f;
+          for (int s2 = 0; s2 < S; ++s2)
+            v += (s2 == s) ? rs[e] : load_agent(&p.ws_rms[(cnt * S + s2) * 16 + row]);
+          rs[e] = v;
+        }
       }
-#pragma unroll
-      for (int i = 0; i < NW; ++i) sum[i] += v[i];
-      if (rms) rsum += rv;
     }
-#pragma unroll
-    for (int i = 0; i < NW; ++i) fin[i] = sum[i];
-    if (rms) rs = rsum;
     if (lane == 0) reset_arrival(&p.ws_cnt[cnt]);
   }
 
