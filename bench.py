@@ -718,11 +718,14 @@ def host_cores():
 # OMP_NUM_THREADS takes effect before the oracle's OpenMP runtime starts;
 # each reports the threads its OpenMP runtime actually used.
 _ORACLE_TIMING = r"""
-import sys, time, json
+import os, sys, time, json
 sys.path.insert(0, {root!r})
+if {one_core}:
+    os.sched_setaffinity(0, {{min(os.sched_getaffinity(0))}})
 import oracle
 from decode_w4a16_repack_amd import synth
 oracle.build(force=False)
+oracle.set_threads({threads})
 p = synth.make_problem(1, {K}, {N}, {G}, seed=0)
 ts = []
 t_start = time.perf_counter()
@@ -732,20 +735,23 @@ while True:
     ts.append(time.perf_counter() - t0)
     if len(ts) >= {min_reps} and (time.perf_counter() - t_start > {budget} or len(ts) >= 400):
         break
-print(json.dumps({{"times": ts, "threads": oracle.max_threads()}}))
+print(json.dumps({{"times": ts, "threads": oracle.max_threads(),
+                  "cores": len(os.sched_getaffinity(0))}}))
 """
 
 
 def _time_oracle(threads, budget_s, min_reps):
     import subprocess
     env = dict(os.environ, OMP_NUM_THREADS=str(threads))
-    code = _ORACLE_TIMING.format(root=ROOT, K=K, N=N, G=GROUP, budget=budget_s, min_reps=min_reps)
+    code = _ORACLE_TIMING.format(root=ROOT, K=K, N=N, G=GROUP, budget=budget_s, min_reps=min_reps,
+                                 threads=int(threads), one_core=threads == 1)
     r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
                        timeout=900, check=True)
     out = json.loads(r.stdout.strip().splitlines()[-1])
     ts = out["times"]
     t = float(np.median(ts))
-    return {"value": algorithmic_bytes(1) / t / 1e9, "unit": "GB/s", "cores": out["threads"],
+    return {"value": algorithmic_bytes(1) / t / 1e9, "unit": "GB/s",
+            "cores": min(out["threads"], out["cores"]), "threads": out["threads"],
             "us_per_call": t * 1e6, "calls": len(ts), "cpu_seconds": float(sum(ts))}
 
 

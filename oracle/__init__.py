@@ -70,6 +70,8 @@ def _load():
         lib.oracle_weight_nibble_index.restype = ctypes.c_long
         lib.oracle_rmsnorm.argtypes = [P, I, I, P, D, P, P]
         lib.oracle_rmsnorm.restype = ctypes.c_int
+        lib.oracle_set_threads.argtypes = [I]
+        lib.oracle_set_threads.restype = None
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = ctypes.c_int
         lib.oracle_repack.argtypes = [P, P, P, I, I, I, I, P]
@@ -96,6 +98,11 @@ def _u8(a):
 def _check(rc, what):
     if rc != 0:
         raise ValueError(f"oracle {what} rejected its arguments (rc={rc})")
+
+
+def set_threads(n: int) -> None:
+    """Threads for the oracle's parallel loops in this process."""
+    _load().oracle_set_threads(int(n))
 
 
 def max_threads() -> int:

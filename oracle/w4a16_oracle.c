@@ -135,6 +135,16 @@ static double dot_column(const double *x, const uint8_t *qweight,
 
 static double silu(double v) { return v / (1.0 + exp(-v)); }
 
+/* Sets the threads the OpenMP loops over output columns use (no effect
+ * without OpenMP). */
+void oracle_set_threads(int n) {
+#ifdef _OPENMP
+  if (n >= 1) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 /* Threads the OpenMP loops over output columns use (1 without OpenMP). */
 int oracle_max_threads(void) {
 #ifdef _OPENMP
