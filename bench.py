@@ -261,20 +261,28 @@ def time_graph(call, sets, steps=200, warmup=10):
     return time_calls(calls, steps, warmup, samples=0)["us_per_call"]
 
 
-def ab_samples(paths, sets, rounds=24, warmup=2):
+AB_TIMING = ("medians of 24 interleaved replays of a graph of at least 192 calls per path "
+             "over the rotating sets")
+
+
+def ab_samples(paths, sets, rounds=24, warmup=2, min_calls=192):
     """Interleaved A/B samples ("Fusion benchmark" page, "Two paths on one
-    rig"): each path is one HIP graph over the rotating sets; a round replays
-    every path once in turn, each replay bracketed by its own event pair.
-    Returns {name: stats of us per call}."""
+    rig"): each path is one HIP graph of at least ``min_calls`` calls
+    cycling over the rotating sets (so one graph launch and one event pair
+    are a small part of a sample); a round replays every path once in turn,
+    each replay bracketed by its own event pair.  Returns {name: stats of
+    us per call}."""
     import torch
     stream = torch.cuda.Stream()
+    R = len(sets)
+    n_calls = R * math.ceil(min_calls / R)
     graphs = {}
     for name, call in paths.items():
         calls = [(lambda st=st: call(st)) for st in sets]
         for c in calls:
             c()
         torch.cuda.synchronize()
-        graphs[name] = capture(calls, stream)
+        graphs[name] = capture([calls[i % R] for i in range(n_calls)], stream)
     per = {name: [] for name in paths}
     with torch.cuda.stream(stream):
         for _ in range(warmup):
@@ -291,7 +299,7 @@ def ab_samples(paths, sets, rounds=24, warmup=2):
                 evs.append((name, a, b))
         torch.cuda.synchronize()
     for name, a, b in evs:
-        per[name].append(a.elapsed_time(b) * 1e3 / len(sets))
+        per[name].append(a.elapsed_time(b) * 1e3 / n_calls)
     return {name: stats(v) for name, v in per.items()}
 
 
@@ -433,10 +441,12 @@ def extras(ws):
         R = max(2, math.ceil(2 * INFINITY_CACHE / byt))
         pr = DevProblem(M, K_, N_, g, R, seed=200 + g)
         sets = pr.sets
-        t_plain = time_graph(lambda st: w4.gemm(st["A"], st["w"][0], out=st["out"], workspace=ws), sets)
-        # fused and unfused chains sampled in alternation on the same buffers
-        ab = ab_samples(fusion_paths(pr, ws), sets)
+        # the plain GEMM and the fused and unfused chains sampled in
+        # alternation on the same buffers
+        ab = ab_samples({"gemm": lambda st: w4.gemm(st["A"], st["w"][0], out=st["out"], workspace=ws),
+                         **fusion_paths(pr, ws)}, sets)
         med = {k: v["median"] for k, v in ab.items()}
+        t_plain = med["gemm"]
         row = {
             "group": g, "rotating_sets": R, "level": "HBM (rotated inputs), graph replay",
             "gemm_us": t_plain, "gemm_GBps": byt / t_plain / 1e3,
@@ -473,15 +483,18 @@ def extras(ws):
     byt = algorithmic_bytes(M, K, N, g, n_weights=2)
     R = max(2, math.ceil(2 * INFINITY_CACHE / byt))
     pr = DevProblem(M, K, N, g, R, n_weights=2, seed=300)
-    t_gu = time_graph(lambda st: w4.gemm_gate_up(st["A"], st["w"][0], st["w"][1], out=st["out"],
-                                                 workspace=ws), pr.sets)
-    t_two = time_graph(lambda st: (w4.gemm(st["A"], st["w"][0], out=pr.tmp, workspace=ws),
-                                   w4.gemm(st["A"], st["w"][1], out=pr.tmp2, workspace=ws)), pr.sets)
+    ab = ab_samples({
+        "gate_up": lambda st: w4.gemm_gate_up(st["A"], st["w"][0], st["w"][1], out=st["out"],
+                                              workspace=ws),
+        "two_gemms": lambda st: (w4.gemm(st["A"], st["w"][0], out=pr.tmp, workspace=ws),
+                                 w4.gemm(st["A"], st["w"][1], out=pr.tmp2, workspace=ws))}, pr.sets)
+    t_gu, t_two = ab["gate_up"]["median"], ab["two_gemms"]["median"]
     res["gate_up_m32_k5120_n13824_g128"] = {
         "rotating_sets": R, "level": "HBM (rotated inputs), graph replay",
         "us": t_gu, "GBps": byt / t_gu / 1e3, "pct_hbm_peak": 100 * byt / t_gu / 1e3 / HBM_PEAK_GBS,
         "TFLOPs": flops(M, n_weights=2) / t_gu / 1e6, "algorithmic_bytes": byt,
         "two_plain_gemms_us": t_two,
+        "timing": AB_TIMING,
     }
     log(f"[bench] C5 gate_up M=32: {t_gu:.2f} us ({res['gate_up_m32_k5120_n13824_g128']['pct_hbm_peak']:.1f}% HBM); "
         f"two plain GEMMs {t_two:.2f} us")
@@ -501,7 +514,8 @@ SPLIT_SWEEP_SHAPES = [("o_q_proj", 4096, 4096, False), ("down_proj", 13696, 4096
 
 def split_sweep(ws, M=8, group=128):
     """Each shape at M=8: the automatic plan's time and %HBM, beside every
-    forced split-K factor in {1, 2, 3, 4, 6, 8} the shape can run."""
+    forced split-K factor in {1, 2, 3, 4, 6, 8} the shape can run (medians of
+    interleaved replays, ``ab_samples``)."""
     import torch
     import decode_w4a16_repack_amd as w4
     rows = []
@@ -518,23 +532,27 @@ def split_sweep(ws, M=8, group=128):
             else:
                 w4.gemm(st["A"], st["w"][0], out=st["out"], workspace=ws, split=split)
         auto = w4.plan(M, K_, N_, group, gate_up=gu)
-        t_auto = time_graph(lambda st: call(st, 0), pr.sets)
-        forced = {}
+        paths = {"auto": lambda st: call(st, 0)}
         for sk in (1, 2, 3, 4, 6, 8):
             try:
                 fp = w4.plan(M, K_, N_, group, gate_up=gu, split=sk)
             except w4.W4A16Error:
                 continue
-            if fp.split in forced:
-                continue
-            forced[fp.split] = time_graph(lambda st: call(st, sk), pr.sets)
+            if f"sk{fp.split}" not in paths:
+                paths[f"sk{fp.split}"] = (lambda st, sk=sk: call(st, sk))
+        # Interleaved: a path timed first after the inputs were made would
+        # also pay for the clocks ramping back up.
+        res = ab_samples(paths, pr.sets)
+        t_auto = res["auto"]["median"]
+        forced = {int(k[2:]): v["median"] for k, v in res.items() if k != "auto"}
         best = min(forced, key=forced.get) if forced else auto.split
         row = {"shape": name, "M": M, "K": K_, "N": N_, "gate_up": gu, "group": group,
                "rotating_sets": R, "algorithmic_bytes": byt,
                "auto_kernel": auto.kernel, "auto_split": auto.split, "auto_us": t_auto,
                "auto_pct_hbm_peak": 100 * byt / t_auto / 1e3 / HBM_PEAK_GBS,
                "forced_split_us": {str(k): v for k, v in sorted(forced.items())},
-               "best_forced_split": best}
+               "best_forced_split": best,
+               "timing": AB_TIMING}
         rows.append(row)
         log(f"[bench] split sweep {name:12s} M={M} K={K_} N={N_}{' x2' if gu else ''}: auto sk{auto.split} "
             f"{t_auto:6.2f} us ({row['auto_pct_hbm_peak']:4.1f}% HBM); forced "
@@ -598,21 +616,23 @@ def mlp_chain(ws, Ms=(1, 8, 32), group=128):
         for M in Ms:
             mlp_inputs(gen, sets, M)
             byt = wbytes + 2 * M * H + 2 * 2 * M * I + 2 * M * H
-            t_mlp = time_graph(lambda st: w4.mlp(st["A"], *st["w"], gamma=st["gamma"],
-                                                 inter=st["inter"], out=st["out"], workspace=ws),
-                               sets)
-            t_gu = time_graph(lambda st: w4.gemm_gate_up(st["A"], st["w"][0], st["w"][1],
-                                                         gamma=st["gamma"], out=st["inter"],
-                                                         workspace=ws), sets)
-            t_dn = time_graph(lambda st: w4.gemm(st["inter"], st["w"][2], out=st["out"],
-                                                 workspace=ws), sets)
+            res = ab_samples({
+                "mlp": lambda st: w4.mlp(st["A"], *st["w"], gamma=st["gamma"], inter=st["inter"],
+                                         out=st["out"], workspace=ws),
+                "gate_up": lambda st: w4.gemm_gate_up(st["A"], st["w"][0], st["w"][1],
+                                                      gamma=st["gamma"], out=st["inter"],
+                                                      workspace=ws),
+                "down": lambda st: w4.gemm(st["inter"], st["w"][2], out=st["out"], workspace=ws),
+            }, sets)
+            t_mlp, t_gu, t_dn = (res[k]["median"] for k in ("mlp", "gate_up", "down"))
             row = {"shape": name, "M": M, "H": H, "I": I, "group": group, "rotating_sets": R,
                    "algorithmic_bytes": byt, "mlp_us": t_mlp,
                    "mlp_GBps": byt / t_mlp / 1e3,
                    "mlp_pct_hbm_peak": 100 * byt / t_mlp / 1e3 / HBM_PEAK_GBS,
                    "gate_up_alone_us": t_gu, "down_alone_us": t_dn,
                    "gate_up_plan": w4.plan(M, H, I, group, gate_up=True).__dict__,
-                   "down_plan": w4.plan(M, I, H, group).__dict__}
+                   "down_plan": w4.plan(M, I, H, group).__dict__,
+                   "timing": AB_TIMING}
             rows.append(row)
             log(f"[bench] {name} M={M:2d}: mlp {t_mlp:6.2f} us ({row['mlp_pct_hbm_peak']:4.1f}% HBM); "
                 f"gate_up alone {t_gu:6.2f} + down alone {t_dn:6.2f} us")
@@ -694,6 +714,32 @@ def cu_probes():
             "what": "LDS read: 1024 workgroups x 512 threads, 2000 x 16 KiB per wavefront; "
                     "L2 -> LDS copy: 216 workgroups, 161 x 32 KiB each of a 640 KiB fp16 "
                     "matrix, two steps in flight, one barrier per step"}
+
+
+def tile_read_probe(steps=480, warmup=2000):
+    """Plain reads of the headline shape's packed weight tiles (K=5120,
+    N=13824: 864 column tiles x 40 k tiles of 1 KiB, 35.4 MB) under two
+    decompositions: the streaming kernel's (216 workgroups of 4 column tiles,
+    8 k slices each) and the same tiles split evenly over all 256 compute
+    units (256 workgroups of 135 tiles).  Rotating resident copies (twice
+    the Infinity Cache), graph replay, HIP events, like the headline."""
+    import torch
+    import decode_w4a16_repack_amd as w4
+    nbytes = K * N // 2
+    R = max(2, math.ceil(2 * INFINITY_CACHE / nbytes))
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(11)
+    ws_ = [w4.PackedWeight(torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device="cuda",
+                                         generator=gen), K, N, GROUP, 0, False) for _ in range(R)]
+    sink = torch.zeros(256 * 512, dtype=torch.int32, device="cuda")
+    res = {"bytes_per_call": nbytes, "rotating_sets": R, "level": "HBM (rotated inputs), graph replay"}
+    for name, mode, wgs in (("stream_kernel_grid_216", 0, 0), ("even_256", 1, 256)):
+        calls = [(lambda w=w, mode=mode, wgs=wgs: w4.probe_read_tiles(w, mode, wgs, sink)) for w in ws_]
+        us = time_calls(calls, steps, warmup, samples=0)["us_per_call"]
+        res[name] = {"us_per_call": us, "GBps": nbytes / us / 1e3}
+    del ws_
+    torch.cuda.empty_cache()
+    return res
 
 
 def cpu_model():
@@ -943,7 +989,8 @@ def main():
         profile_fusion()
         return
     if args.probes:
-        print(json.dumps({"hbm_probe_GBps": hbm_probe(), "cu_probes": cu_probes()}, indent=1))
+        print(json.dumps({"hbm_probe_GBps": hbm_probe(), "cu_probes": cu_probes(),
+                          "tile_read_probe": tile_read_probe()}, indent=1))
         return
     if args.profile_mlp:
         M = args.profile_mlp
@@ -1013,7 +1060,9 @@ def main():
     if not args.no_sweep:
         for Ms, sdt, asym in SWEEP:
             s2 = InputSets(Ms, rotations_needed(Ms), seed=Ms, sdt=sdt, asym=asym)
-            r = time_calls(s2.calls(ws), 160, 16, samples=40)
+            # the headline's call count and warmup: a short warmup leaves
+            # the first rows paying for clocks that ramp back up
+            r = time_calls(s2.calls(ws), args.steps, args.warmup, samples=40)
             t = r["us_per_call"]
             byt = algorithmic_bytes(Ms, scale_bytes=np.dtype(sdt).itemsize, has_zp=asym)
             fl = flops(Ms)
@@ -1035,6 +1084,10 @@ def main():
     probe = hbm_probe()
     log(f"[bench] streaming-read probe: {probe:.1f} GB/s")
     cu = cu_probes()
+    trp = tile_read_probe()
+    log(f"[bench] tile-read probe (35.4 MB of weight tiles, no arithmetic): streaming kernel's grid "
+        f"{trp['stream_kernel_grid_216']['us_per_call']:.2f} us, even over 256 workgroups "
+        f"{trp['even_256']['us_per_call']:.2f} us")
     log(f"[bench] compute-unit probes: LDS read {cu['lds_read_GBps_per_cu']:.0f} GB/s per CU, "
         f"L2 -> LDS copy {cu['l2_to_lds_copy_GBps_per_cu']:.0f} GB/s per CU")
     cpu = None if args.no_cpu else cpu_baseline(gpu_out)
@@ -1067,6 +1120,7 @@ def main():
         "pct_hbm_peak": 100 * value / HBM_PEAK_GBS,
         "hbm_probe_GBps": probe,
         "cu_probes": cu,
+        "tile_read_probe": trp,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": load_traffic(),
                      "algorithmic_bytes_per_launch": b1, "avg_launch_us": us_mean},

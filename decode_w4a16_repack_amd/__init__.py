@@ -25,7 +25,7 @@ from ._lib import W4A16Error
 __all__ = [
     "PackedWeight", "repack", "gemm", "gemm_gate_up", "packed_bytes",
     "workspace_bytes", "layout_version", "add_bias", "relu", "rmsnorm",
-    "probe_read", "probe_copy", "probe_lds_read", "probe_lds_copy", "Workspace", "plan", "Plan", "W4A16Error",
+    "probe_read", "probe_copy", "probe_lds_read", "probe_lds_copy", "probe_read_tiles", "Workspace", "plan", "Plan", "W4A16Error",
     "mlp", "mlp_workspace_bytes", "gemm_noalloc",
 ]
 
@@ -464,3 +464,14 @@ def probe_lds_copy(buf: torch.Tensor, workgroups: int, steps: int, sink: torch.T
                                                int(workgroups), int(steps), _ptr(sink), _stream()),
                "w4a16_probe_lds_copy")
 
+
+def probe_read_tiles(w: PackedWeight, mode: int, workgroups: int, sink: torch.Tensor) -> None:
+    """w4a16_probe_read_tiles: plain reads of w's packed weight tiles, in the
+    streaming kernel's decomposition (mode 0) or split evenly over
+    `workgroups` workgroups (mode 1); sink gets one word per thread."""
+    _need_gpu(w.data, "w.data")
+    _need_gpu(sink, "sink", device=w.data.device)
+    _lib.check(_lib.lib().w4a16_probe_read_tiles(_ptr(w.data), int(w.K), int(w.N), int(mode),
+                                                 int(workgroups), _ptr(sink),
+                                                 sink.numel() * sink.element_size(), _stream()),
+               "w4a16_probe_read_tiles")

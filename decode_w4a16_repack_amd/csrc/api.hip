@@ -349,6 +349,19 @@ int w4a16_mlp(const void *A, const void *residual, void *residual_out, int M, in
   return st != W4A16_OK ? st : run(down, stream);
 }
 
+int w4a16_probe_read_tiles(const void *w, int K, int N, int mode, int workgroups, void *sink,
+                           size_t sink_bytes, w4a16_stream stream) {
+  if (w == nullptr || sink == nullptr) return W4A16_ERR_NULL;
+  if (K < kTileK || K % kTileK != 0 || N < kTileN || N % kTileN != 0 || K > kMaxDim || N > kMaxDim ||
+      (size_t)(N / kTileN) * (size_t)(K / kTileK) > ((size_t)1 << 30) || (mode != 0 && mode != 1) ||
+      (mode == 1 && (workgroups < 1 || workgroups > 65535)))
+    return W4A16_ERR_SHAPE;
+  if ((size_t)probe_tiles_grid(N, mode, workgroups) * 512 * 4 > sink_bytes) return W4A16_ERR_SHAPE;
+  if (!aligned16(w) || !aligned16(sink)) return W4A16_ERR_ALIGN;
+  return launched(launch_probe_tiles(w, K, N, mode, workgroups, static_cast<uint32_t *>(sink),
+                                     static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"
 
 // ---------------------------------------------------------------------------

@@ -172,6 +172,65 @@ __global__ void __launch_bounds__(512) probe_lds_copy_kernel(const uint8_t *buf,
   sink[(size_t)blockIdx.x * 512 + t] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
 }
 
+// Plain reads of one packed weight matrix (KC = K/128 tiles of 1 KiB per
+// 16-column tile, tile u = t*KC + kc at u*1024) under two decompositions of
+// its NT*KC tiles over 512-thread workgroups, with the same load loop (one
+// 16-byte load per lane per tile, eight tiles per batch, the next batch in
+// flight while one is folded):
+//  MODE 0: the streaming kernel's: workgroup g takes column tiles 4g..4g+3
+//          over all of K, wavefront w the k tiles w*KPW .. w*KPW + KPW - 1
+//          (KPW = ceil(KC/8)) of each;
+//  MODE 1: the tiles split evenly over nwg workgroups: workgroup g takes the
+//          contiguous range [g*U/nwg, (g+1)*U/nwg) of U = NT*KC, its
+//          wavefronts dealt the range round-robin.
+// One word per thread goes to sink[g * 512 + thread].
+template <int MODE>
+__global__ void __launch_bounds__(512) probe_tiles_kernel(const uint8_t *w, int NT, int KC, int nwg,
+                                                          uint32_t *sink) {
+  const int t = threadIdx.x, lane = t & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int g = blockIdx.x;
+  int n, nk = 1, ct0 = 0, kb = 0;
+  size_t u0 = 0;
+  if constexpr (MODE == 0) {
+    const int kpw = (KC + 7) / 8;
+    kb = wv * kpw;
+    const int nkr = max(0, min(kpw, KC - kb));  // k tiles of this slice (none past K)
+    nk = max(nkr, 1);
+    ct0 = 4 * g;
+    n = nkr > 0 ? min(4, NT - ct0) * nkr : 0;
+  } else {
+    const size_t U = (size_t)NT * KC;
+    u0 = (size_t)g * U / (size_t)nwg;
+    const size_t cnt = (size_t)(g + 1) * U / (size_t)nwg - u0;
+    n = cnt > (size_t)wv ? (int)((cnt - wv + 7) / 8) : 0;
+  }
+  auto unit = [&](int j) __attribute__((always_inline)) -> size_t {
+    if constexpr (MODE == 0)
+      return (size_t)(ct0 + j / nk) * KC + kb + j % nk;
+    else
+      return u0 + wv + (size_t)8 * j;
+  };
+  auto load8 = [&](int base, u32x4 (&v)[8]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      v[i] = base + i < n ? __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(w + unit(base + i) * 1024) + lane)
+                          : u32x4{0, 0, 0, 0};
+  };
+  u32x4 cur[8], nxt[8];
+  u32x4 acc = {0, 0, 0, 0};
+  load8(0, cur);
+  for (int b = 0; b < n; b += 8) {
+    load8(b + 8, nxt);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      acc ^= cur[i];
+      cur[i] = nxt[i];
+    }
+  }
+  sink[(size_t)g * 512 + t] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+}
+
 unsigned grid_for(size_t vecs, unsigned cap) {
   size_t b = (vecs + 255) / 256;
   if (b > cap) b = cap;
@@ -230,6 +289,22 @@ hipError_t launch_probe_lds_copy(const void *buf, size_t bytes, int workgroups, 
                                  uint32_t *sink, hipStream_t stream) {
   hipLaunchKernelGGL(probe_lds_copy_kernel, dim3(workgroups), dim3(512), 0, stream,
                      static_cast<const uint8_t *>(buf), (int)(bytes / 16384), steps, sink);
+  return hipGetLastError();
+}
+
+unsigned probe_tiles_grid(int N, int mode, int workgroups) {
+  return mode == 0 ? (unsigned)((N / kTileN + 3) / 4) : (unsigned)workgroups;
+}
+
+hipError_t launch_probe_tiles(const void *w, int K, int N, int mode, int workgroups, uint32_t *sink,
+                              hipStream_t stream) {
+  const uint8_t *b = static_cast<const uint8_t *>(w);
+  const int NT = N / kTileN, KC = K / kTileK;
+  const unsigned grid = probe_tiles_grid(N, mode, workgroups);
+  if (mode == 0)
+    hipLaunchKernelGGL(probe_tiles_kernel<0>, dim3(grid), dim3(512), 0, stream, b, NT, KC, 0, sink);
+  else
+    hipLaunchKernelGGL(probe_tiles_kernel<1>, dim3(grid), dim3(512), 0, stream, b, NT, KC, workgroups, sink);
   return hipGetLastError();
 }
 

@@ -180,5 +180,8 @@ hipError_t launch_probe_copy(const void *src, void *dst, size_t bytes,
 hipError_t launch_probe_lds_read(int workgroups, int iters, uint32_t *sink, hipStream_t stream);
 hipError_t launch_probe_lds_copy(const void *buf, size_t bytes, int workgroups, int steps,
                                  uint32_t *sink, hipStream_t stream);
+unsigned probe_tiles_grid(int N, int mode, int workgroups);
+hipError_t launch_probe_tiles(const void *w, int K, int N, int mode, int workgroups, uint32_t *sink,
+                              hipStream_t stream);
 
 }  // namespace w4a16

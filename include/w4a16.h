@@ -348,6 +348,28 @@ int w4a16_probe_lds_read(int workgroups, int iters, void *sink, w4a16_stream str
 int w4a16_probe_lds_copy(const void *buf, size_t bytes, int workgroups, int steps, void *sink,
                          w4a16_stream stream);
 
+
+/*
+ * Probe of how the streaming kernel's tiles are spread over the chip: plain
+ * reads of the K*N/2-byte weight region of a packed matrix (w, as written by
+ * w4a16_repack), one 16-byte load per lane per 1 KiB tile, eight tiles per
+ * batch with the next batch in flight, no arithmetic, in one of two
+ * decompositions over workgroups of 512 threads:
+ *   mode 0: the streaming kernel's own (its widest configuration):
+ *     ceil(N/64) workgroups; workgroup g reads column tiles 4g..4g+3 over
+ *     all of K, its wavefront w the k tiles w*P .. w*P+P-1 of each
+ *     (P = ceil(K/1024)); `workgroups` is ignored;
+ *   mode 1: the (N/16)*(K/128) tiles split evenly over `workgroups`
+ *     workgroups (1..65535), each taking a contiguous range of the layout
+ *     and dealing it round-robin to its 8 wavefronts.
+ * One 32-bit value per thread goes to sink (at least grid * 2048 bytes,
+ * sink_bytes), so nothing is elided.  W4A16_ERR_SHAPE for K or N not a
+ * multiple of 128 / 16, more than 2^30 tiles, another mode, workgroups
+ * outside 1..65535 in mode 1, or a sink too small.
+ */
+int w4a16_probe_read_tiles(const void *w, int K, int N, int mode, int workgroups, void *sink,
+                           size_t sink_bytes, w4a16_stream stream);
+
 #ifdef __cplusplus
 }
 #endif

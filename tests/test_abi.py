@@ -134,6 +134,17 @@ def test_aux_validation(L):
     assert L.w4a16_probe_lds_copy(FAKE, 16384, 70000, 10, FAKE, None) == _lib.ERR_SHAPE
     assert L.w4a16_probe_lds_copy(FAKE, 16384, 4, 0, FAKE, None) == _lib.ERR_SHAPE
     assert L.w4a16_probe_lds_copy(FAKE + 4, 16384, 4, 10, FAKE, None) == _lib.ERR_ALIGN
+    big = 1 << 30
+    assert L.w4a16_probe_read_tiles(None, 5120, 13824, 0, 0, FAKE, big, None) == _lib.ERR_NULL
+    assert L.w4a16_probe_read_tiles(FAKE, 5000, 13824, 0, 0, FAKE, big, None) == _lib.ERR_SHAPE
+    assert L.w4a16_probe_read_tiles(FAKE, 5120, 13820, 0, 0, FAKE, big, None) == _lib.ERR_SHAPE
+    assert L.w4a16_probe_read_tiles(FAKE, 5120, 13824, 2, 0, FAKE, big, None) == _lib.ERR_SHAPE
+    assert L.w4a16_probe_read_tiles(FAKE, 5120, 13824, 1, 0, FAKE, big, None) == _lib.ERR_SHAPE
+    assert L.w4a16_probe_read_tiles(FAKE, 5120, 13824, 1, 70000, FAKE, big, None) == _lib.ERR_SHAPE
+    # the sink holds one word per thread of the grid: 216 workgroups in mode 0
+    assert L.w4a16_probe_read_tiles(FAKE, 5120, 13824, 0, 0, FAKE, 216 * 2048 - 4, None) == _lib.ERR_SHAPE
+    assert L.w4a16_probe_read_tiles(FAKE, 5120, 13824, 1, 256, FAKE, 255 * 2048, None) == _lib.ERR_SHAPE
+    assert L.w4a16_probe_read_tiles(FAKE + 4, 5120, 13824, 0, 0, FAKE, big, None) == _lib.ERR_ALIGN
 
 
 def test_workspace_only_for_narrow_grids(L):

@@ -486,6 +486,27 @@ def test_probes():
     torch.cuda.synchronize()
 
 
+
+@pytest.mark.parametrize("K,N,mode,wgs", [(5120, 13824, 0, 0), (5120, 13824, 1, 256),
+                                          (1024, 400, 0, 0), (1024, 400, 1, 7), (384, 48, 1, 300)])
+def test_probe_read_tiles_reads_every_tile_once(K, N, mode, wgs):
+    # each 16-byte chunk of the weight region is folded by exactly one lane,
+    # so the xor of every word the probe writes is the xor of every word of
+    # the region (ragged shapes: a 1-tile last column block, fewer k tiles
+    # than wavefronts, more workgroups than tiles)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(K + N + mode)
+    wreg = torch.randint(0, 256, (K * N // 2,), dtype=torch.uint8, device="cuda", generator=g)
+    pw = w4.PackedWeight(wreg, K, N, 128, 0, False)
+    grid = (N // 16 + 3) // 4 if mode == 0 else wgs
+    sink = torch.zeros(grid * 512, dtype=torch.int32, device="cuda")
+    w4.probe_read_tiles(pw, mode, wgs, sink)
+    torch.cuda.synchronize()
+    want = np.bitwise_xor.reduce(wreg.cpu().numpy().view(np.uint32))
+    got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+    assert got == want
+
+
 # ------------------------------------------------------- deepest k range
 
 _DEEP = {}
