@@ -161,10 +161,17 @@ __device__ __forceinline__ void group_row_sums(f32x4 (&ug)[128 / G], const f16x8
   }
 }
 
+// An empty asm that reads and writes an accumulator: the scaled group sums
+// are added where they are made.  Left to itself the compiler may defer the
+// adds of a whole loop to its end, keep every group sum and scale alive until
+// then and spill them (two weight streams, or many groups per k tile).
+__device__ __forceinline__ void pin_acc(f32x4 &acc) { asm volatile("" : "+v"(acc)); }
+
 // Contract one packed k tile of one 16-column weight tile with one 16-row
 // tile of pre-scaled activation fragments a[d] (d = 32-k step), given the
 // tile's group row sums ug; zp_of(gl) / scale_of(gl) as for contract_tile.
-template <int G, class ZpOf, class ScaleOf>
+// PIN: pin the accumulator after each group (pin_acc).
+template <int G, bool PIN = false, class ZpOf, class ScaleOf>
 __device__ __forceinline__ void contract_tile_sub(f32x4 &acc, const u32x4 &w, const f16x8 (&a)[4],
                                                   const f32x4 (&ug)[128 / G], int kq, ZpOf zp_of,
                                                   ScaleOf scale_of) {
@@ -176,6 +183,7 @@ __device__ __forceinline__ void contract_tile_sub(f32x4 &acc, const u32x4 &w, co
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       acc[e] = __builtin_fmaf(ug[gl][e], sz, __builtin_fmaf(part[e], s24, acc[e]));
+    if constexpr (PIN) pin_acc(acc);
   };
   if constexpr (G >= 32) {
     constexpr int SPG = G / 32;

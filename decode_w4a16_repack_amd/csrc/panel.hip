@@ -229,6 +229,8 @@ panel_kernel(const GemmArgs p) {
 #pragma unroll
               for (int e = 0; e < 4; ++e)
                 acc[i][w][mt][e] = __builtin_fmaf(accg[mt][e], sc, acc[i][w][mt][e]);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) pin_acc(acc[i][w][mt]);
           }
         }
       } else {
@@ -251,6 +253,8 @@ panel_kernel(const GemmArgs p) {
               acc[i][w][mt][e] =
                   __builtin_fmaf(p1[e], s1, __builtin_fmaf(p0[e], s0, acc[i][w][mt][e]));
           }
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) pin_acc(acc[i][w][mt]);
         }
       }
     }

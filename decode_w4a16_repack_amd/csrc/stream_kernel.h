@@ -353,7 +353,7 @@ stream_kernel(const GemmArgs p) {
     for (int i = 0; i < NW; ++i) {
       const uint8_t *st = ms + i * MS_BYTES + (gi0 * 16 + c) * SB;
       const uint8_t *zt = mz + i * MZ_PAD + gi0 * 8 + (c >> 1);
-      contract_tile_sub<G>(
+      contract_tile_sub<G, GU>(
           acc[i][w][0], wv[i][f], at, ug, kq,
           [&](int gl) __attribute__((always_inline)) { return (zt[gl * 8] >> zshift) & 15; },
           [&](int gl) __attribute__((always_inline)) {

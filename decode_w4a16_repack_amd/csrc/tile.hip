@@ -269,6 +269,10 @@ tile_kernel(const GemmArgs p) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                   acc[i][mt][ct][e] = __builtin_fmaf(accg[mt][e], sc, acc[i][mt][ct][e]);
+              if constexpr (G < 64) {
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) pin_acc(acc[i][mt][ct]);
+              }
             }
           }
         } else {
@@ -290,6 +294,7 @@ tile_kernel(const GemmArgs p) {
               for (int e = 0; e < 4; ++e)
                 acc[i][mt][ct][e] =
                     __builtin_fmaf(p1[e], s1, __builtin_fmaf(p0[e], s0, acc[i][mt][ct][e]));
+              pin_acc(acc[i][mt][ct]);
             }
           }
         }
