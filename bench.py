@@ -430,7 +430,8 @@ def extras(ws):
     """The pages' other workloads: the group sweep at M=16 K=N=4096 with the
     fused bias+ReLU epilogue and the fused RMSNorm prologue against their
     unfused chains (analytic bytes beside measured time, "Fusion benchmark"
-    page), and the fused gate_up SwiGLU at M=32 K=5120 N=13824."""
+    page), the fused gate_up SwiGLU at M=32 K=5120 N=13824, the split-K
+    sweep at M=8, the MLP block, and the cost of the RMSNorm prologues."""
     import torch
     import decode_w4a16_repack_amd as w4
     res = {"group_sweep_m16_k4096_n4096": [], "gate_up_m32_k5120_n13824_g128": None}
@@ -502,8 +503,56 @@ def extras(ws):
     torch.cuda.empty_cache()
     res["split_sweep_m8"] = split_sweep(ws)
     res["mlp_chain"] = mlp_chain(ws)
+    res["rmsnorm_prologue_k5120_n13824"] = rmsnorm_prologue_cost(ws)
     return res
 
+
+def rmsnorm_prologue_cost(ws, Ms=(1, 8, 16, 32, 64, 128), group=128):
+    """The RMSNorm prologue's cost at K=5120 N=13824: the plain product, the
+    product with the RMSNorm prologue and with the residual + RMSNorm
+    prologue, for the GEMM and for gate_up, at each M (medians of
+    interleaved replays, ``ab_samples``)."""
+    import torch
+    import decode_w4a16_repack_amd as w4
+    rows = []
+    for M in Ms:
+        byt = algorithmic_bytes(M, K, N, group, n_weights=2)
+        R = max(2, math.ceil(2 * INFINITY_CACHE / byt))
+        pr = DevProblem(M, K, N, group, R, n_weights=2, seed=600 + M)
+        g = torch.Generator(device="cuda")
+        g.manual_seed(700 + M)
+        for st in pr.sets:
+            st["resid"] = torch.randn((M, K), device="cuda", generator=g).half()
+            st["sum"] = torch.empty((M, K), dtype=torch.float16, device="cuda")
+        paths = {
+            "gemm_plain": lambda st: w4.gemm(st["A"], st["w"][0], out=st["out"], workspace=ws),
+            "gemm_rms": lambda st: w4.gemm(st["A"], st["w"][0], gamma=st["gamma"], out=st["out"],
+                                           workspace=ws),
+            "gemm_skip_rms": lambda st: w4.gemm(st["A"], st["w"][0], gamma=st["gamma"],
+                                                residual=st["resid"], residual_out=st["sum"],
+                                                out=st["out"], workspace=ws),
+            "gate_up_plain": lambda st: w4.gemm_gate_up(st["A"], st["w"][0], st["w"][1],
+                                                        out=st["out"], workspace=ws),
+            "gate_up_rms": lambda st: w4.gemm_gate_up(st["A"], st["w"][0], st["w"][1],
+                                                      gamma=st["gamma"], out=st["out"], workspace=ws),
+            "gate_up_skip_rms": lambda st: w4.gemm_gate_up(st["A"], st["w"][0], st["w"][1],
+                                                           gamma=st["gamma"], residual=st["resid"],
+                                                           residual_out=st["sum"], out=st["out"],
+                                                           workspace=ws),
+        }
+        res = ab_samples(paths, pr.sets)
+        row = {"M": M, "K": K, "N": N, "group": group, "rotating_sets": R, "timing": AB_TIMING,
+               "us": {k: v["median"] for k, v in res.items()},
+               "gemm_plan": w4.plan(M, K, N, group).kernel,
+               "gate_up_plan": w4.plan(M, K, N, group, gate_up=True).kernel}
+        rows.append(row)
+        u = row["us"]
+        log(f"[bench] RMSNorm prologue M={M:3d}: gemm {u['gemm_plain']:6.2f} / {u['gemm_rms']:6.2f} / "
+            f"{u['gemm_skip_rms']:6.2f} us, gate_up {u['gate_up_plain']:6.2f} / {u['gate_up_rms']:6.2f} / "
+            f"{u['gate_up_skip_rms']:6.2f} us (plain / RMSNorm / residual + RMSNorm)")
+        del pr
+        torch.cuda.empty_cache()
+    return rows
 
 # The M=8 decode shapes the "Small-M split-K retune" update tunes: (name, K,
 # N per projection, gate_up).  The gate_up rows are paired projections of
