@@ -120,13 +120,17 @@ struct Plan {
 inline int stream_kpw(const Plan &p) { return p.kind == kKindStream ? kStreamCfgs[p.cfg].kpw : 0; }
 
 // Whether a call stages its RMSNorm prologue (stage.hip) instead of running
-// it inside the product kernel: always for the panel and tile kernels; for
-// the streaming kernel only with the residual, and there with more than 4
-// rows (re-reading both activation slices in every column block costs more
-// than one staging pass) or a slice deeper than 5 k tiles (its registers
-// cannot hold the whole slice and its residual).
+// it inside the product kernel: always for the tile kernel; for the panel
+// kernel with the residual or a k split across workgroups; for the
+// streaming kernel only with the residual, and there with more than 4 rows
+// (re-reading both activation slices in every column block costs more than
+// one staging pass) or a slice deeper than 5 k tiles (its registers cannot
+// hold the whole slice and its residual).
 inline bool staged_prologue(const Plan &p, int M, bool gamma, bool resid) {
-  return gamma && (p.kind != kKindStream || (resid && (M > 4 || stream_kpw(p) > 5)));
+  if (!gamma) return false;
+  if (p.kind == kKindStream) return resid && (M > 4 || stream_kpw(p) > 5);
+  if (p.kind == kKindPanel) return resid || p.split > 1;
+  return true;
 }
 
 // force_kind: -1 automatic, else a PlanKind; force_cfg < 0 /

@@ -198,13 +198,16 @@ bool plan_panel(Plan &p, int M, int K, int N, int group, int scale_bytes, bool g
   p.gy = p.split;
   const int gpw = c.kpw * (kTileK / group);
   // per wavefront: its slice's scales and zero-points per weight stream
-  const size_t meta = NW * ((size_t)c.cpw * gpw * 16 * scale_bytes + align16((size_t)c.cpw * gpw * 8));
+  // then the slice's RMSNorm gamma (reserved whether or not a call has one)
+  const size_t meta = NW * ((size_t)c.cpw * gpw * 16 * scale_bytes + align16((size_t)c.cpw * gpw * 8)) +
+                      (size_t)c.kpw * kTileK * 2;
   const size_t red = (size_t)c.cpw * c.mt * 1024;  // one weight stream's partial sums
   const size_t region = align16(meta > red ? meta : red);
   p.lds_s = (int)region;
   p.lds_r = (int)(c.nwk * region);
-  // (+ one int: the workgroup's "last to arrive" flag of the split path)
-  p.lds_bytes = (size_t)p.lds_r + 16;
+  // (+ one int: the workgroup's "last to arrive" flag of the split path;
+  // then the slices' row sums of squares of the RMSNorm prologue)
+  p.lds_bytes = (size_t)p.lds_r + 16 + (size_t)c.nwk * 16 * c.mt * 4;
   if (p.lds_bytes > 160 * 1024) return false;
   p.rows_pow2 = 0;
   p.alds = 0;

@@ -37,7 +37,10 @@ namespace w4a16 {
 namespace {
 
 // (occupancy NWK / 4 wavefronts per SIMD, as for the streaming kernel)
-template <int MT, int CPW, int KPW, int NWK, int PD, bool ADB, int G, bool SF32, bool GU>
+// RMS: the RMSNorm prologue in the kernel (no residual, no k split across
+// workgroups): x * gamma rounded once to fp16 in the fragments, the row
+// sums of squares in fp32, 1/sqrt(mean + eps) in the epilogue.
+template <int MT, int CPW, int KPW, int NWK, int PD, bool ADB, int G, bool SF32, bool GU, bool RMS>
 __global__ void __launch_bounds__(64 * NWK) __attribute__((amdgpu_waves_per_eu(NWK / 4, NWK / 4)))
 panel_kernel(const GemmArgs p) {
   constexpr int NW = GU ? 2 : 1;
@@ -85,6 +88,9 @@ panel_kernel(const GemmArgs p) {
   uint8_t *region = smem + wk * p.lds_s;
   uint8_t *ms = region;                  // [NW] x MS_BYTES
   uint8_t *mz = region + NW * MS_BYTES;  // [NW] x MZ_PAD
+  uint8_t *mg = mz + NW * MZ_PAD;        // RMS: the slice's gamma, [KPW][128] fp16
+  // RMS: the slices' row sums of squares, [NWK][16 * MT], after the split flag
+  float *lRms = reinterpret_cast<float *>(smem + p.lds_r + 16);
 
   // 1. this slice's scales and zero-points of the CPW column tiles, copied
   //    straight into the private region (reads clamped to the column tile's
@@ -121,6 +127,17 @@ panel_kernel(const GemmArgs p) {
     } else {
       for (int e = lane; e * 4 < MZ_BYTES; e += 64)  // symmetric: every zero-point is 8
         reinterpret_cast<uint32_t *>(mzi)[e] = 0x88888888u;
+    }
+  }
+  if constexpr (RMS) {
+    // the slice's gamma (positions past the slice copy a valid tile)
+#pragma unroll
+    for (int q = 0; q < (KPW * 16 + 63) / 64; ++q) {
+      const int u = q * 64 + lane;
+      if (u < KPW * 16) {
+        const int kc = min(my_kb + min(u >> 4, max(my_n - 1, 0)), KC - 1);
+        copy16_to_lds(p.gamma + kc * kTileK + (u & 15) * 8, mg + q * 1024);
+      }
     }
   }
 
@@ -177,6 +194,9 @@ panel_kernel(const GemmArgs p) {
       for (int mt = 0; mt < MT; ++mt) acc[i][w][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int zshift = 4 * (c & 1);
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+  float ss[MT];  // RMS: this lane's part of the sums of squares of rows 16 mt + l%16
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) ss[mt] = 0.f;
   static_for<NTILE>([&](auto fc) __attribute__((always_inline)) {
     constexpr int f = decltype(fc)::value;
     constexpr int t = f / CPW, w = f % CPW;
@@ -195,6 +215,25 @@ panel_kernel(const GemmArgs p) {
       if constexpr (ADB && t > 0 && t + 1 < KPW) load_a(t + 1, a[(t + 1) % NAB]);
     }
     if constexpr (f + PDE < NTILE) issue_tile(f + PDE);
+    if constexpr (RMS && w == 0) {
+      // the k tile's fragments, once for its CPW column tiles: sums of
+      // squares (fp16 products are exact in fp32), then x * gamma rounded
+      // once to fp16 (tiles past the slice add nothing: their scales are 0)
+      if (t < my_n) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            const f16x8 x = at[mt][d];
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+              const f16x2 x2 = {x[2 * h], x[2 * h + 1]};
+              ss[mt] = __builtin_amdgcn_fdot2(x2, x2, ss[mt], false);
+            }
+            at[mt][d] = x * *reinterpret_cast<const f16x8 *>(mg + (t * kTileK + 32 * d + 8 * kq) * 2);
+          }
+      }
+    }
     const float on = t < my_n ? 1.0f : 0.0f;
     const int gi0 = (w * KPW + t) * GPC;  // first group of the tile in the region
 #pragma unroll
@@ -263,6 +302,17 @@ panel_kernel(const GemmArgs p) {
   // 6. the slice partial sums, one weight stream per pass, through the
   //    private regions; wavefront wk finishes output blocks wk, wk + NWK, ...
   //    (block = mt * CPW + w) in slice order
+  if constexpr (RMS) {
+    // row 16 mt + l%16's k slots of this slice are spread over lanes
+    // l%16 + 16j; the first lds_barrier below publishes them
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      float v = ss[mt];
+      v += __shfl_xor(v, 16);
+      v += __shfl_xor(v, 32);
+      if (lane < 16) lRms[wk * (16 * MT) + 16 * mt + lane] = v;
+    }
+  }
   f32x4 fin[NW][PPW];
   f32x4 *red = reinterpret_cast<f32x4 *>(region);
 #pragma unroll
@@ -373,7 +423,15 @@ panel_kernel(const GemmArgs p) {
       const int row = 16 * mt + 4 * kq + e;
       if (row < mrows) {
         float rsc = 1.0f;
-        if (p.row_ss != nullptr) rsc = 1.0f / sqrtf(p.row_ss[m0 + row] / (float)p.K + p.eps);
+        if constexpr (RMS) {
+          // the slices' sums in slice order
+          float rs = 0.f;
+#pragma unroll
+          for (int w2 = 0; w2 < NWK; ++w2) rs += lRms[w2 * (16 * MT) + row];
+          rsc = 1.0f / sqrtf(rs / (float)p.K + p.eps);
+        } else if (p.row_ss != nullptr) {
+          rsc = 1.0f / sqrtf(p.row_ss[m0 + row] / (float)p.K + p.eps);
+        }
         float y;
         if constexpr (GU) {
           y = silu(fin[0][j][e] * rsc) * (fin[1][j][e] * rsc);
@@ -388,9 +446,9 @@ panel_kernel(const GemmArgs p) {
   }
 }
 
-template <int MT, int CPW, int KPW, int NWK, int PD, bool ADB, int G, bool SF32, bool GU>
+template <int MT, int CPW, int KPW, int NWK, int PD, bool ADB, int G, bool SF32, bool GU, bool RMS>
 hipError_t launch_t(const GemmArgs &a, const Plan &pl, hipStream_t stream) {
-  auto kern = panel_kernel<MT, CPW, KPW, NWK, PD, ADB, G, SF32, GU>;
+  auto kern = panel_kernel<MT, CPW, KPW, NWK, PD, ADB, G, SF32, GU, RMS>;
   static std::atomic<size_t> lds_limit[kMaxDevices];
   const hipError_t e = raise_lds_limit(reinterpret_cast<const void *>(kern), pl.lds_bytes, lds_limit);
   if (e != hipSuccess) return e;
@@ -398,13 +456,24 @@ hipError_t launch_t(const GemmArgs &a, const Plan &pl, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int MT, int CPW, int KPW, int NWK, int PD, bool ADB, int G, bool RMS>
+hipError_t launch_r(const GemmArgs &a, const Plan &pl, bool sf32, bool gu, hipStream_t st) {
+  if (gu)
+    return sf32 ? launch_t<MT, CPW, KPW, NWK, PD, ADB, G, true, true, RMS>(a, pl, st)
+                : launch_t<MT, CPW, KPW, NWK, PD, ADB, G, false, true, RMS>(a, pl, st);
+  return sf32 ? launch_t<MT, CPW, KPW, NWK, PD, ADB, G, true, false, RMS>(a, pl, st)
+              : launch_t<MT, CPW, KPW, NWK, PD, ADB, G, false, false, RMS>(a, pl, st);
+}
+
+// with a gamma (and so, by the plan, no residual and no k split across
+// workgroups) the RMSNorm prologue runs in the kernel
 template <int MT, int CPW, int KPW, int NWK, int PD, bool ADB, int G>
 hipError_t launch_g(const GemmArgs &a, const Plan &pl, bool sf32, bool gu, hipStream_t st) {
-  if (gu)
-    return sf32 ? launch_t<MT, CPW, KPW, NWK, PD, ADB, G, true, true>(a, pl, st)
-                : launch_t<MT, CPW, KPW, NWK, PD, ADB, G, false, true>(a, pl, st);
-  return sf32 ? launch_t<MT, CPW, KPW, NWK, PD, ADB, G, true, false>(a, pl, st)
-              : launch_t<MT, CPW, KPW, NWK, PD, ADB, G, false, false>(a, pl, st);
+  if (a.gamma != nullptr) {
+    if (a.resid != nullptr || pl.split > 1) return hipErrorInvalidValue;
+    return launch_r<MT, CPW, KPW, NWK, PD, ADB, G, true>(a, pl, sf32, gu, st);
+  }
+  return launch_r<MT, CPW, KPW, NWK, PD, ADB, G, false>(a, pl, sf32, gu, st);
 }
 
 template <int MT, int CPW, int KPW, int NWK, int PD, bool ADB>

@@ -159,13 +159,15 @@ def test_workspace_only_for_narrow_grids(L):
     for M in (1, 2, 4):
         assert L.w4a16_workspace_bytes(M, 5120, 13824, 128, 0) == 0
         assert L.w4a16_workspace_bytes(M, 5120, 13824, 128, 1) == 0
-    # M = 5..16: the streaming kernel stages only the skip + RMSNorm prologue
+    # M = 5..32: the streaming and panel kernels stage only the skip + RMSNorm
+    # prologue (the panel kernel also with a k split across workgroups, which
+    # wide N does not need); the tile kernel (M > 32) stages every prologue
     for M in (5, 16, 17, 32, 64, 128):
         stage = CB + a256(M * 5120 * 2) + a256(M * 4)
         assert L.w4a16_workspace_bytes(M, 5120, 13824, 128, 0) == stage
         assert L.w4a16_workspace_bytes(M, 5120, 13824, 128, 1) == stage
         # a call that stages checks for the staging before any launch
-        if M > 16:
+        if M > 32:
             assert gemm(L, M=M, K=5120, N=13824, group=128, gamma=FAKE) == _lib.ERR_WORKSPACE
             assert gemm(L, M=M, K=5120, N=13824, group=128, gamma=FAKE, ws=FAKE,
                         ws_n=stage - 1) == _lib.ERR_WORKSPACE

@@ -181,6 +181,24 @@ def test_panel_gate_up_ragged(M):
                 f"panel gate_up ragged M={M}")
 
 
+@pytest.mark.parametrize("M,K,N,g,gu", [(24, 1152, 13808, 64, False), (17, 1024, 13824, 128, True),
+                                        (32, 1024, 13824, 16, True), (32, 5120, 13824, 128, False),
+                                        (32, 5120, 13824, 128, True)])
+def test_panel_rmsnorm_prologue_in_kernel(M, K, N, g, gu):
+    """The panel kernel's own RMSNorm prologue (no k split across workgroups,
+    so nothing is staged): x * gamma in the fragments, the slices' sums of
+    squares through LDS, the row scale in the epilogue.  K = 1152 has 9 k
+    tiles, so one slice ends past K; N = 13808 a ragged last block; every
+    output at K <= 1152, a sample of them at K = 5120."""
+    expect_plan(M, K, N, g, kernel="panel", col_tiles=4, gate_up=gu, split=1)
+    p = synth.make_problem(M, K, N, g, seed=M * 7 + K + g, gamma=True, gate_up=gu)
+    got = run(p, gate_up=gu, rms=True)
+    cols = None if K <= 1152 else np.unique(np.concatenate([np.arange(N - 32, N),
+                                                            sample_cols(N, 160, seed=K)]))
+    want = ref(p, gate_up=gu, rms=True, cols=cols)
+    check_close(got if cols is None else got[:, cols], want, f"panel rmsnorm M={M} K={K} gu={gu}")
+
+
 # ------------------------------------------------ the tile kernel (M > 32)
 
 
