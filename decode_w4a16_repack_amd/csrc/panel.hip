@@ -23,13 +23,16 @@
 //  * each 32-bit word of codes is unpacked once into the exact integers
 //    q - z as fp16 and feeds MT matrix-core operations, so the unpack cost
 //    per MFMA falls as 1/MT;
-//  * scales and zero-points of the slice are copied once into a private LDS
-//    region per wavefront; no barrier sits in the loop, only the one before
-//    the slice reduction;
+//  * scales and zero-points of the slice (and, with the RMSNorm prologue,
+//    its gamma) are copied once into a private LDS region per wavefront; no
+//    barrier sits in the loop, only the one before the slice reduction;
+//  * with the RMSNorm prologue each k tile's fragments are turned into
+//    x * gamma once, and their sums of squares kept per row;
 //  * the (row tile, column tile) output blocks are shared out over the
 //    wavefronts for the final sum: slice sum in slice order, the RMSNorm
-//    row scale (rows staged by stage.hip), epilogue, one fp16 write.  Wide reductions (gate_up) go in one pass per
-//    weight stream so the LDS need not hold both at once.
+//    row scale (from the slices' sums of squares, or from rows staged by
+//    stage.hip), epilogue, one fp16 write.  Wide reductions (gate_up) go in
+//    one pass per weight stream so the LDS need not hold both at once.
 #include "device.h"
 
 namespace w4a16 {
