@@ -45,6 +45,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import math
 import os
@@ -84,10 +85,15 @@ def flops(M, K=K, N=N, n_weights=1):
 
 
 def kernel_source_hash():
+    """Hash of the kernel sources' code: comments and blank space removed,
+    so that an edit of a comment does not retire the counter figures."""
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)   # block comments
+        text = re.sub(r"//[^\n]*", " ", text)                  # line comments
+        h.update(rel.encode() + b"\0" + " ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
