@@ -1,5 +1,7 @@
-// Activation staging for the RMSNorm prologue of the multi-row kernels
-// (panel and tile, M > 16).
+// Activation staging for the RMSNorm prologue where the product kernel does
+// not run it itself: the tile kernel (M > 32), the panel kernel with a
+// residual or a k split across workgroups, and the streaming kernel with a
+// residual above 4 rows or a deep slice.
 //
 // The onnx-genai pull request's "fused RMS-norm" update normalizes the
 // activation before the fused product, staging the normalized rows through
@@ -11,11 +13,11 @@
 // row is first replaced by A + residual, rounded once to fp16, which is also
 // written out.
 //
-// Why not inside the product kernels: there the prologue ran on every k tile
-// of every wavefront and its extra live values pushed the loop past the
-// register file (spills to scratch on every workgroup); one pass over the
-// M x K activations costs far less than that at every M above 16.  The M <= 16
-// streaming kernel keeps its own in-register prologue.
+// Why not inside the tile kernel: its wavefronts read every activation
+// fragment from the shared LDS stage, so each of the four column quarters
+// would repeat the x * gamma multiply and the sums of squares of every row;
+// one pass over the M x K activations costs less.  The streaming and panel
+// kernels, which load each fragment once, run the prologue themselves.
 #include "common.h"
 
 namespace w4a16 {
