@@ -469,8 +469,15 @@ def probe_read_tiles(w: PackedWeight, mode: int, workgroups: int, sink: torch.Te
     """w4a16_probe_read_tiles: plain reads of w's packed weight tiles, in the
     streaming kernel's decomposition (mode 0) or split evenly over
     `workgroups` workgroups (mode 1); sink gets one word per thread."""
-    _need_gpu(w.data, "w.data")
-    _need_gpu(sink, "sink", device=w.data.device)
+    _need_form(w.data, "w.data", torch.uint8)
+    if w.data.numel() < w.K * w.N // 2:
+        raise ValueError("w.data is shorter than the weight tiles of a K x N matrix")
+    _need_form(sink, "sink")
+    grid = (w.N // 16 + 3) // 4 if mode == 0 else int(workgroups)
+    if sink.numel() * sink.element_size() < grid * 512 * 4:
+        raise ValueError(f"sink needs {grid * 512 * 4} bytes")
+    _need_device(w.data, "w.data")
+    _need_device(sink, "sink", device=w.data.device)
     _lib.check(_lib.lib().w4a16_probe_read_tiles(_ptr(w.data), int(w.K), int(w.N), int(mode),
                                                  int(workgroups), _ptr(sink),
                                                  sink.numel() * sink.element_size(), _stream()),

@@ -78,6 +78,12 @@ def test_ops_refuse_wrong_shapes_before_any_call():
         w4.repack(q, s[:, :1], None, 256, 32, 128)
     with pytest.raises(ValueError, match="zeros must have shape"):
         w4.repack(q, s, torch.zeros((32, 2), dtype=torch.uint8), 256, 32, 128)
+    # the tile-read probe: the weight region and the sink are checked too
+    tiny = w4.PackedWeight(torch.zeros(100, dtype=torch.uint8), 256, 32, 128, _lib.SCALE_F16, True)
+    with pytest.raises(ValueError, match="shorter than the weight tiles"):
+        w4.probe_read_tiles(tiny, 0, 0, torch.zeros(512, dtype=torch.int32))
+    with pytest.raises(ValueError, match="sink needs 8192 bytes"):
+        w4.probe_read_tiles(pw, 1, 4, torch.zeros(100, dtype=torch.int32))
 
 
 def test_plan_reports_the_kernel_configuration():
