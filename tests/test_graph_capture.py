@@ -72,7 +72,9 @@ CASES = [
     (130, 2048, 512, 128, "gemm"),
     (8, 1024, 256, 128, "gate_up"),       # split-K gate_up with RMSNorm
     (40, 1024, 256, 16, "gate_up"),
-    (32, 1024, 512, 64, "rms"),           # panel kernel on staged rows
+    (32, 1024, 512, 64, "rms"),           # panel kernel on staged rows (split over k)
+    (24, 1024, 13824, 128, "rms"),        # panel kernel, its own RMSNorm prologue
+    (32, 1152, 13808, 64, "gate_up"),     # panel gate_up, its own prologue, ragged block
     (70, 1024, 256, 128, "skip"),         # tile kernel, staged skip + RMSNorm
     (12, 1024, 384, 32, "skip"),          # stream kernel, staged skip + RMSNorm
     (3, 1024, 384, 128, "skip"),          # stream kernel, skip + RMSNorm in registers
