@@ -235,6 +235,29 @@ __device__ __forceinline__ void copy4_to_lds(const void *src, void *lds_base) {
                                    (void __attribute__((address_space(3))) *)lds_base, 4, 0, 0);
 }
 
+// The same copies as buffer loads (buffer_load_dword[x4] ... lds) from a
+// raw byte range: lane l's bytes at base + voff + soff land at lds_base +
+// size * l.  A kernel that keeps issuing copies while it uses registers
+// loaded by plain loads takes these: the compiler counts a buffer copy in
+// order with the plain loads and waits for exactly the load a register needs,
+// whereas a global_load_lds still in flight makes it wait for every load
+// (vmcnt(0)) before each such use.  Offsets are 32-bit; a read at or past
+// `bytes` returns zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void *base, uint32_t bytes) {
+  // word 3: 32-bit data format, the raw (unswizzled, stride 0) form
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                              void *lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (void __attribute__((address_space(3))) *)lds_base, 16,
+                                           voff, soff, 0, 0);
+}
+__device__ __forceinline__ void copy4_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                             void *lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (void __attribute__((address_space(3))) *)lds_base, 4,
+                                           voff, soff, 0, 0);
+}
+
 // s_waitcnt with only the vector-memory counter limited to n (< 64); the
 // other counters at their maximum (no wait).  GFX9 encoding: vmcnt[3:0] in
 // bits 3:0, expcnt in 6:4, lgkmcnt in 11:8, vmcnt[5:4] in 15:14.

@@ -157,19 +157,35 @@ tile_kernel(const GemmArgs p) {
   constexpr int SUS = PSS / 16;  // 16-byte scale units per step
   constexpr int ZUS = PSZ / 4;   // 4-byte zero-point units per step
   const bool s_on = lane < MBS * SUS, z_on = lane < MBS * ZUS;
-  uint32_t s_lane, z_lane;
+  uint32_t s_lane, z_lane;  // from this wavefront's first column tile (clamped to the last)
   int s_step, z_step;
+  const int ct_base = min(ctw, NTL - 1);
   {
     const int u = min(lane, MBS * SUS - 1);
     s_step = u / SUS;
     const int r = u - s_step * SUS, w = r / (GPC * SB), o = r - w * (GPC * SB);
-    s_lane = (uint32_t)min(ctw + w, NTL - 1) * (uint32_t)(Gall * 16 * SB) + (uint32_t)o * 16u;
+    s_lane = (uint32_t)(min(ctw + w, NTL - 1) - ct_base) * (uint32_t)(Gall * 16 * SB) + (uint32_t)o * 16u;
     const int uz = min(lane, MBS * ZUS - 1);
     z_step = uz / ZUS;
     const int rz = uz - z_step * ZUS, wz = rz / (GPC * 2), oz = rz - wz * (GPC * 2);
-    z_lane = (uint32_t)min(ctw + wz, NTL - 1) * (uint32_t)(Gall * 8) + (uint32_t)oz * 4u;
+    z_lane = (uint32_t)(min(ctw + wz, NTL - 1) - ct_base) * (uint32_t)(Gall * 8) + (uint32_t)oz * 4u;
   }
-  const uint8_t *a_rows = reinterpret_cast<const uint8_t *>(p.A + (size_t)m0 * p.K);
+  // sources of the copies as buffer ranges (the workgroup's 64 rows; this
+  // wavefront's column tiles of each metadata stream), so that the compiler
+  // keeps exact waits for the weight tiles in registers while copies are in
+  // flight; every offset stays below 2^31 (K <= 2^24, CT <= 2 column tiles)
+  const __amdgpu_buffer_rsrc_t a_src =
+      raw_rsrc(p.A + (size_t)m0 * p.K, (uint32_t)mrows * (uint32_t)p.K * 2u);
+  __amdgpu_buffer_rsrc_t s_src[NW], z_src[NW];
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    const size_t run = (size_t)(NTL - ct_base) * Gall;  // groups from the first column tile on
+    s_src[i] = raw_rsrc(reinterpret_cast<const uint8_t *>(p.scales[i]) + (size_t)ct_base * Gall * 16 * SB,
+                        (uint32_t)min(run * 16 * SB, (size_t)0xFFFFFFFFu));
+    z_src[i] = has_zp ? raw_rsrc(p.zeros[i] + (size_t)ct_base * Gall * 8,
+                                 (uint32_t)min(run * 8, (size_t)0xFFFFFFFFu))
+                      : s_src[i];
+  }
 
   // copies of step j into stage st: the slice's activation tile (a quarter
   // of it per column quarter); when step j opens a metadata block, first
@@ -181,20 +197,19 @@ tile_kernel(const GemmArgs p) {
       uint8_t *blk = mblk_of(j / MBS);
       // k tile of step j + s_step (the lane's own step in the block)
       const int kts = min(ktile(j + s_step), KC - 1), ktz = min(ktile(j + z_step), KC - 1);
+      const uint32_t s_off = s_lane + (uint32_t)kts * (GPC * 16 * SB);
+      const uint32_t z_off = has_zp ? z_lane + (uint32_t)ktz * (GPC * 8) : s_off;
 #pragma unroll
       for (int i = 0; i < NW; ++i) {
-        const uint8_t *sb = reinterpret_cast<const uint8_t *>(p.scales[i]);
-        if (s_on) copy16_to_lds(sb + s_lane + (size_t)kts * GPC * 16 * SB, blk + i * BS);
-        const uint8_t *zb = has_zp ? p.zeros[i] + (size_t)ktz * GPC * 8 + z_lane
-                                   : sb + s_lane + (size_t)kts * GPC * 16 * SB;
-        if (z_on) copy4_to_lds(zb, blk + NW * BS + i * BZ);
+        if (s_on) copy16_to_lds(s_src[i], s_off, 0, blk + i * BS);
+        if (z_on) copy4_to_lds(z_src[i], z_off, 0, blk + NW * BS + i * BZ);
       }
     }
     const int kt = min(ktile(j), KC - 1);
     uint8_t *abuf = abuf_of(st);
-    const uint8_t *abase = a_rows + (size_t)kt * kTileK * 2;
 #pragma unroll
-    for (int qi = 0; qi < AQ; ++qi) copy16_to_lds(abase + aoff[qi], abuf + (wc + NWC * qi) * 1024);
+    for (int qi = 0; qi < AQ; ++qi)
+      copy16_to_lds(a_src, aoff[qi], (uint32_t)kt * kTileK * 2, abuf + (wc + NWC * qi) * 1024);
   };
 
   // the weight tiles of step j, straight into registers
