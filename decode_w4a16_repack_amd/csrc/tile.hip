@@ -103,10 +103,10 @@ tile_kernel(const GemmArgs p) {
   static_assert(MBS >= ST - 1 || NBUF * MBS >= ST, "metadata ring");
   // per step and wavefront at least: activation copies CL, then weight-tile
   // loads WL.  At the top of step j, the loads issued after the copies of
-  // step j are the weights of that step and the copies and weights of the
-  // ST - 2 steps after it; metadata copies (one block every MBS steps) and
-  // the first steps' extra loads only add to that, which makes the wait
-  // stricter, never looser.
+  // step j are the WL weight loads of the step that issued them and the
+  // copies and weight loads of the ST - 2 steps after it; metadata copies
+  // (one block every MBS steps) and the first steps' extra loads only add to
+  // that, which makes the wait stricter, never looser.
   constexpr int CL = kTileABytes / 1024 / NWC;
   constexpr int WL = NW * CT;
   constexpr int AFTER = WL + (ST - 2) * (CL + WL);
@@ -187,12 +187,12 @@ tile_kernel(const GemmArgs p) {
                       : s_src[i];
   }
 
-  // copies of step j into stage st: the slice's activation tile (a quarter
-  // of it per column quarter); when step j opens a metadata block, first
-  // that block's scales and zero-points.  Steps past K re-read the last k
-  // tile; symmetric weights copy scale bytes into the (unread) zero-point
-  // area.
-  auto issue = [&](int j, int st, bool opens_block) __attribute__((always_inline)) {
+  // copies of step j: when step j opens a metadata block, that block's
+  // scales and zero-points (issue_meta), then the slice's activation tile
+  // into stage st, a quarter of it per column quarter, one 1 KiB copy qi at a
+  // time (issue_a).  Steps past K re-read the last k tile; symmetric weights
+  // copy scale bytes into the (unread) zero-point area.
+  auto issue_meta = [&](int j, bool opens_block) __attribute__((always_inline)) {
     if (opens_block) {
       uint8_t *blk = mblk_of(j / MBS);
       // k tile of step j + s_step (the lane's own step in the block)
@@ -205,23 +205,17 @@ tile_kernel(const GemmArgs p) {
         if (z_on) copy4_to_lds(z_src[i], z_off, 0, blk + NW * BS + i * BZ);
       }
     }
+  };
+  auto issue_a = [&](int j, int st, int qi) __attribute__((always_inline)) {
     const int kt = min(ktile(j), KC - 1);
-    uint8_t *abuf = abuf_of(st);
-#pragma unroll
-    for (int qi = 0; qi < AQ; ++qi)
-      copy16_to_lds(a_src, aoff[qi], (uint32_t)kt * kTileK * 2, abuf + (wc + NWC * qi) * 1024);
+    copy16_to_lds(a_src, aoff[qi], (uint32_t)kt * kTileK * 2, abuf_of(st) + (wc + NWC * qi) * 1024);
   };
 
-  // the weight tiles of step j, straight into registers
-  auto load_w = [&](int j, u32x4 (&wv)[NW][CT]) __attribute__((always_inline)) {
+  // weight tile (i, ct) of step j, straight into registers
+  auto load_w1 = [&](int j, int i, int ct, u32x4 (&wv)[NW][CT]) __attribute__((always_inline)) {
     const int kt = min(ktile(j), KC - 1);
-#pragma unroll
-    for (int i = 0; i < NW; ++i)
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct) {
-        const size_t tile = (size_t)min(ctw + ct, NTL - 1) * KC + kt;
-        wv[i][ct] = load_weights<CT == 1>(p.w[i] + tile * kTileBytes, lane);  // CT > 1: several row blocks
-      }
+    const size_t tile = (size_t)min(ctw + ct, NTL - 1) * KC + kt;
+    wv[i][ct] = load_weights<CT == 1>(p.w[i] + tile * kTileBytes, lane);  // CT > 1: several row blocks
   };
 
   f32x4 acc[NW][MT][CT];
@@ -233,7 +227,8 @@ tile_kernel(const GemmArgs p) {
       for (int ct = 0; ct < CT; ++ct) acc[i][mt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int zshift = 4 * (c & 1);
-  auto compute = [&](int j, int st, const u32x4 (&wreg)[NW][CT]) __attribute__((always_inline)) {
+  // (hook(b) runs before block b of 32 k, b = (i * CT + ct) * 4 + d)
+  auto compute = [&](int j, int st, const u32x4 (&wreg)[NW][CT], auto &&hook) __attribute__((always_inline)) {
     // row 16mt + c, chunk 4d + kq sits at slot row * 16 + ((4d + kq) ^ c): the
     // 16 rows of one operand read land in 16 different chunk positions
     const uint8_t *abuf = abuf_of(st) + c * 256;
@@ -272,6 +267,7 @@ tile_kernel(const GemmArgs p) {
           f16x2 zlo, zhi;
 #pragma unroll
           for (int d = 0; d < 4; ++d) {
+            hook((i * CT + ct) * 4 + d);
             if (d % SPG == 0) zconst(d / SPG, zlo, zhi);
             const f16x8 b = unpack8(wv[d], zlo, zhi);
 #pragma unroll
@@ -295,6 +291,7 @@ tile_kernel(const GemmArgs p) {
           const f16x8 zero8 = {};
 #pragma unroll
           for (int d = 0; d < 4; ++d) {
+            hook((i * CT + ct) * 4 + d);
             f16x2 zlo, zhi;
             zconst(2 * d + (kq >> 1), zlo, zhi);
             const f16x8 b = unpack8(wv[d], zlo, zhi);
@@ -324,36 +321,68 @@ tile_kernel(const GemmArgs p) {
   // and computes.
   u32x4 wring[D + 1][NW][CT];
 #pragma unroll
-  for (int u = 0; u < ST - 1; ++u) issue(u, u, u % MBS == 0);
+  for (int u = 0; u < ST - 1; ++u) {
+    issue_meta(u, u % MBS == 0);
 #pragma unroll
-  for (int u = 0; u < D; ++u) load_w(u, wring[u]);
+    for (int qi = 0; qi < AQ; ++qi) issue_a(u, u, qi);
+  }
+#pragma unroll
+  for (int u = 0; u < D; ++u)
+#pragma unroll
+    for (int i = 0; i < NW; ++i)
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) load_w1(u, i, ct, wring[u]);
   int st = 0;
   // Step j = j0 + u (j0 a multiple of D + 1 = 4, so u, the ring slot and
-  // whether a metadata block opens are known at compile time).  Every step
-  // issues the same copies and loads and runs the same contraction (a step
-  // past K with zero scales), so every load has a consumer on every path
-  // and the compiler never has to drain the loads in flight.  Where the
-  // register file allows it (one column tile per wavefront, one weight
-  // stream, groups of 64 or 128) the trip count is padded to a multiple of
-  // 4 and the body has no branch at all; elsewhere the steps past the last
-  // group of 4 are skipped, since the compiler would otherwise interleave
-  // the four steps past what the register file holds.
-  auto step = [&](int j, auto uc) __attribute__((always_inline)) {
+  // whether a metadata block opens are known at compile time).  A step's
+  // activation copies and weight loads (in that order, AQ + NW * CT of them)
+  // are spread over its contraction's NW * CT * 4 blocks of 32 k instead of
+  // being issued together after the barrier: the eight wavefronts' loads
+  // then reach the compute unit's load path one at a time while it also
+  // serves the matrix cores' operands, rather than as one burst that stalls
+  // every wavefront's issue at once (measured: K=5120 N=13824 M=128 29.2 ->
+  // 26.6 us).  Every step issues the same copies and loads, and every step
+  // that runs its contraction runs the same one (a step past K with zero
+  // scales).  Where the register file allows it (one column tile per
+  // wavefront, one weight stream, groups of 64 or 128) the trip count is
+  // padded to a multiple of 4 and the body has no branch at all; elsewhere
+  // the contractions of the steps past the last group of 4 are skipped (the
+  // compiler would otherwise interleave four contractions past what the
+  // register file holds), but not their copies and loads, so that every path
+  // through the loop issues the same loads in the same order and the
+  // compiler's waits for the weight registers stay close to exact.
+  auto step = [&](int j, auto uc, bool live) __attribute__((always_inline)) {
     constexpr int u = decltype(uc)::value;
     wait_vmcnt<AFTER>();  // this wavefront's copies of step j have landed
     lds_only_barrier();   // everyone's have, and step j - 1's reads are done
-    issue(j + ST - 1, st == 0 ? ST - 1 : st - 1, (u + ST - 1) % MBS == 0);
-    load_w(j + D, wring[(u + D) % (D + 1)]);
-    compute(j, st, wring[u]);
+    const int jn = j + ST - 1, stn = st == 0 ? ST - 1 : st - 1;  // stage read in step j - 1
+    issue_meta(jn, (u + ST - 1) % MBS == 0);
+    constexpr int NB = NW * CT * 4, NL = AQ + NW * CT;
+    auto hook = [&](int b) __attribute__((always_inline)) {
+#pragma unroll
+      for (int l = 0; l < NL; ++l)
+        if (l * NB / NL == b) {
+          if (l < AQ)
+            issue_a(jn, stn, l);
+          else
+            load_w1(j + D, (l - AQ) / CT, (l - AQ) % CT, wring[(u + D) % (D + 1)]);
+        }
+    };
+    if (live) {
+      compute(j, st, wring[u], hook);
+    } else {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) hook(b);
+    }
     st = st == ST - 1 ? 0 : st + 1;
   };
   static_assert(D + 1 == 4 && 4 % MBS == 0, "unroll and metadata blocks");
   constexpr bool FLAT = CT == 1 && !GU && (G == 128 || (G == 64 && !SF32));
   for (int j0 = 0; j0 < nsteps; j0 += D + 1) {
-    step(j0, std::integral_constant<int, 0>{});
-    if (FLAT || j0 + 1 < nsteps) step(j0 + 1, std::integral_constant<int, 1>{});
-    if (FLAT || j0 + 2 < nsteps) step(j0 + 2, std::integral_constant<int, 2>{});
-    if (FLAT || j0 + 3 < nsteps) step(j0 + 3, std::integral_constant<int, 3>{});
+    step(j0, std::integral_constant<int, 0>{}, true);
+    step(j0 + 1, std::integral_constant<int, 1>{}, FLAT || j0 + 1 < nsteps);
+    step(j0 + 2, std::integral_constant<int, 2>{}, FLAT || j0 + 2 < nsteps);
+    step(j0 + 3, std::integral_constant<int, 3>{}, FLAT || j0 + 3 < nsteps);
   }
   __syncthreads();  // every step and every copy done: the stages become reduction scratch
 
