@@ -74,11 +74,13 @@ stream_kernel(const GemmArgs p) {
   constexpr int A_EARLY = (PDE - 1) / CPW + 1 < KPW ? (PDE - 1) / CPW + 1 : KPW;
   // (the skip prologue loads the whole slice before the weights: more loads
   // after the copies than counted here, which only makes the wait stricter)
+  // weight tiles issued before the direct-to-LDS copies (LDS-staged rows)
+  constexpr int F0 = ALDS ? (PDE < 2 ? PDE : 2) : 0;
   // loads issued after the direct-to-LDS copies that may still be in
   // flight when the copies are waited for (at least): the register
   // activation fragments of the first k tiles (unless they come through
-  // LDS) and the first PDE tiles
-  constexpr int AFTER_COPIES = (ALDS ? 0 : 4 * A_EARLY) + PDE * NW;
+  // LDS) and the first PDE tiles but the F0 issued before the copies
+  constexpr int AFTER_COPIES = (ALDS ? 0 : 4 * A_EARLY) + (PDE - F0) * NW;
 
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
@@ -115,6 +117,43 @@ stream_kernel(const GemmArgs p) {
   uint8_t *mg = mz + NW * MZ_PAD;         // the slice's gamma, [KPW][128] fp16
   uint8_t *aslots = mg + KPW * kTileK * 2;  // ALDS: KPW * 16 * R slots of 16 bytes
   float *lRms = reinterpret_cast<float *>(smem + p.lds_r);  // [NWK][16]
+
+  // 0. weight tiles: tile f = t * CPW + w (k tile t, column tile w) is issued
+  //    PDE tiles before it is contracted, the activations of k tile t from
+  //    registers just before tile (t, 0) (below: where they come from).
+  //    Tiles past the slice or past N re-read a valid tile.  With the
+  //    activation rows staged in LDS, the first F0 tiles go out before the
+  //    copies of steps 1-2, so that the weight stream starts as early as it
+  //    can (K=5120 N=13824 M=1: 8.05 -> 7.83 us); they then land before the
+  //    copies, which the wait of step 4 covers all the same.
+  const int arow = min(c, mrows - 1);
+  f16x8 a[KPW][4][1];
+  // Without LDS staging the fragments of k tile t are loaded just before the
+  // first weight tile of t: loads complete in issue order, so a slice loaded
+  // up front made the first tile wait for all of it.  The skip prologue (at
+  // most 4 rows) loads the slice and its residual up front and adds them
+  // before the loop: a conditional store of the sum inside the loop would
+  // split it into branches and spill.
+  const f16 *arow_p = p.A + (size_t)(m0 + arow) * p.K + 8 * kq;
+  auto load_a = [&](int t) __attribute__((always_inline)) {
+    const int kc = min(my_kb + min(t, max(my_n - 1, 0)), KC - 1);
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+      a[t][d][0] = *reinterpret_cast<const f16x8 *>(arow_p + kc * kTileK + 32 * d);
+  };
+  constexpr bool A_PROGRESSIVE = !ALDS && !RES;
+  u32x4 wv[NW][NTILE];
+  auto issue_tile = [&](int f) __attribute__((always_inline)) {
+    const int t = f / CPW, w = f % CPW;
+    if (A_PROGRESSIVE && w == 0) load_a(t);
+    const int kc = min(my_kb + min(t, max(my_n - 1, 0)), KC - 1);
+    const size_t tile = (size_t)min(ct0 + w, NTL - 1) * KC + kc;
+#pragma unroll
+    for (int i = 0; i < NW; ++i)
+      wv[i][f] = load_weights(p.w[i] + tile * kTileBytes, lane);
+  };
+#pragma unroll
+  for (int f = 0; f < F0; ++f) issue_tile(f);
 
   // 1. this slice's scales and zero-points of the CPW column tiles: runs of
   //    the packed layout, copied straight into the region (reads clamped to
@@ -174,8 +213,6 @@ stream_kernel(const GemmArgs p) {
   //    tile and are zeroed below, so they add nothing.
   //    ALDS: the slice's rows are first copied into the region in fragment
   //    order (slot ((t*4 + d)*4 + kq)*R + row), unique data only.
-  const int arow = min(c, mrows - 1);
-  f16x8 a[KPW][4][1];
   if constexpr (ALDS) {
     const int lr = __builtin_ctz(R);
     const int n_slots = KPW * 16 * R;
@@ -196,20 +233,6 @@ stream_kernel(const GemmArgs p) {
   auto read_slot = [&](int t, int d) __attribute__((always_inline)) {
     return *reinterpret_cast<const f16x8 *>(aslot_p + (t * 4 + d) * 64 * R);
   };
-  // Otherwise the fragments of k tile t are loaded just before the first
-  // weight tile of t: loads complete in issue order, so a slice loaded up
-  // front made the first tile wait for all of it.  The skip prologue (at most
-  // 4 rows) loads the slice and its residual up front and adds them before
-  // the loop: a conditional store of the sum inside the loop would split it
-  // into branches and spill.
-  const f16 *arow_p = p.A + (size_t)(m0 + arow) * p.K + 8 * kq;
-  auto load_a = [&](int t) __attribute__((always_inline)) {
-    const int kc = min(my_kb + min(t, max(my_n - 1, 0)), KC - 1);
-#pragma unroll
-    for (int d = 0; d < 4; ++d)
-      a[t][d][0] = *reinterpret_cast<const f16x8 *>(arow_p + kc * kTileK + 32 * d);
-  };
-  constexpr bool A_PROGRESSIVE = !ALDS && !RES;
   f16x8 rr[RES ? KPW : 1][4];
   if constexpr (RES) {
     const f16 *rrow_p = p.resid + (size_t)(m0 + arow) * p.K + 8 * kq;
@@ -223,22 +246,9 @@ stream_kernel(const GemmArgs p) {
     }
   }
 
-  // 3. weight tiles; tile f = t * CPW + w (k tile t, column tile w) is issued
-  //    PDE tiles before it is contracted, the activations of k tile t just
-  //    before tile (t, 0).  Tiles past the slice or past N re-read a valid
-  //    tile.
-  u32x4 wv[NW][NTILE];
-  auto issue_tile = [&](int f) __attribute__((always_inline)) {
-    const int t = f / CPW, w = f % CPW;
-    if (A_PROGRESSIVE && w == 0) load_a(t);
-    const int kc = min(my_kb + min(t, max(my_n - 1, 0)), KC - 1);
-    const size_t tile = (size_t)min(ct0 + w, NTL - 1) * KC + kc;
+  // 3. the other weight tiles in flight
 #pragma unroll
-    for (int i = 0; i < NW; ++i)
-      wv[i][f] = load_weights(p.w[i] + tile * kTileBytes, lane);
-  };
-#pragma unroll
-  for (int f = 0; f < PDE; ++f) issue_tile(f);
+  for (int f = F0; f < PDE; ++f) issue_tile(f);
 
   // 4. this wavefront's copies into its region have landed (completion is
   //    in issue order); no other wavefront reads the region before the end
