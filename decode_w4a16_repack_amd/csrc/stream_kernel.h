@@ -74,8 +74,10 @@ stream_kernel(const GemmArgs p) {
   constexpr int A_EARLY = (PDE - 1) / CPW + 1 < KPW ? (PDE - 1) / CPW + 1 : KPW;
   // (the skip prologue loads the whole slice before the weights: more loads
   // after the copies than counted here, which only makes the wait stricter)
-  // weight tiles issued before the direct-to-LDS copies (LDS-staged rows)
-  constexpr int F0 = ALDS ? (PDE < 2 ? PDE : 2) : 0;
+  // weight tiles issued before the direct-to-LDS copies (LDS-staged rows,
+  // several column tiles per wavefront; measured: a single-column
+  // configuration is slower with them, K=4096 N=4096 M=4 5.5 -> 5.8 us)
+  constexpr int F0 = (ALDS && CPW >= 2) ? (PDE < 2 ? PDE : 2) : 0;
   // loads issued after the direct-to-LDS copies that may still be in
   // flight when the copies are waited for (at least): the register
   // activation fragments of the first k tiles (unless they come through
