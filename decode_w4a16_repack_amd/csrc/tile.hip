@@ -384,6 +384,26 @@ tile_kernel(const GemmArgs p) {
     step(j0 + 2, std::integral_constant<int, 2>{}, FLAT || j0 + 2 < nsteps);
     step(j0 + 3, std::integral_constant<int, 3>{}, FLAT || j0 + 3 < nsteps);
   }
+  // The epilogue's own inputs, loaded before the barrier so that their
+  // latency overlaps it: the bias of this lane's columns and the row scales
+  // (staged RMSNorm) of the rows this wavefront finishes, row tiles ks,
+  // ks + NKS, ... of column quarter wc.
+  static_assert(MT % NKS == 0, "row tiles per finishing wavefront");
+  constexpr int MTO = MT / NKS;
+  float bias_v[CT];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct)
+    bias_v[ct] = (!GU && p.epilogue != 0 && ctw + ct < NTL) ? (float)p.bias[(ctw + ct) * kTileN + c] : 0.f;
+  float rsc[MTO][4];
+#pragma unroll
+  for (int o = 0; o < MTO; ++o)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = 16 * (ks + NKS * o) + 4 * kq + e;
+      rsc[o][e] = (p.row_ss != nullptr && row < mrows)
+                      ? 1.0f / sqrtf(p.row_ss[m0 + row] / (float)p.K + p.eps)
+                      : 1.0f;
+    }
   __syncthreads();  // every step and every copy done: the stages become reduction scratch
 
   // slice partial sums -> LDS ([wave][i][mt][ct][lane], 16 bytes per lane)
@@ -397,13 +417,24 @@ tile_kernel(const GemmArgs p) {
         red[((wave * NW + i) * MT + mt) * CT * 64 + ct * 64 + lane] = acc[i][mt][ct];
   __syncthreads();
 
-  // wavefront (wc, ks) finishes row tiles ks, ks + NKS, ... of column quarter wc
+  // Each finishing wavefront sums its tiles over the k slices in slice order
+  // and applies the epilogue; the fp16 results go into a row-major tile of
+  // the workgroup's 64 x WC outputs in LDS (rows padded by 16 bytes against
+  // bank conflicts), after the reduction area where it fits, else over it
+  // once every wavefront has read its partial sums; then each thread stores
+  // whole 16-byte runs of a row (two scattered 2-byte stores per output
+  // element otherwise).
+  constexpr int WC = NWC * CT * kTileN;  // the workgroup's columns
+  constexpr int OSTR = WC + 8;           // tile row stride, halves
+  constexpr int RED_BYTES = kTileNWave * NW * MT * CT * 1024;
+  constexpr bool OSEP = RED_BYTES + 64 * OSTR * 2 <= ST * STAGE;
+  static_assert(64 * OSTR * 2 <= ST * STAGE, "output tile");
+  f16 yv[MTO][CT][4];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    if (mt % NKS != ks) continue;
+  for (int o = 0; o < MTO; ++o) {
+    const int mt = ks + NKS * o;
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
-      if (ctw + ct >= NTL) continue;
       f32x4 fin[NW];
 #pragma unroll
       for (int i = 0; i < NW; ++i) {
@@ -412,25 +443,40 @@ tile_kernel(const GemmArgs p) {
           v += red[(((s2 * NWC + wc) * NW + i) * MT + mt) * CT * 64 + ct * 64 + lane];
         fin[i] = v;
       }
-      const int ncol = (ctw + ct) * kTileN + c;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int row = 16 * mt + 4 * kq + e;
-        if (row < mrows) {
-          float rsc = 1.0f;
-          if (p.row_ss != nullptr) rsc = 1.0f / sqrtf(p.row_ss[m0 + row] / (float)p.K + p.eps);
-          float y;
-          if constexpr (GU) {
-            y = silu(fin[0][e] * rsc) * (fin[1][e] * rsc);
-          } else {
-            y = fin[0][e] * rsc;
-            if (p.epilogue != 0) y += (float)p.bias[ncol];
-            if (p.epilogue == 2) y = y > 0.f ? y : 0.f;
-          }
-          p.out[(size_t)(m0 + row) * p.N + ncol] = (f16)y;
+        float y;
+        if constexpr (GU) {
+          y = silu(fin[0][e] * rsc[o][e]) * (fin[1][e] * rsc[o][e]);
+        } else {
+          y = fin[0][e] * rsc[o][e];
+          if (p.epilogue != 0) y += bias_v[ct];
+          if (p.epilogue == 2) y = y > 0.f ? y : 0.f;
         }
+        yv[o][ct][e] = (f16)y;
       }
     }
+  }
+  if constexpr (!OSEP) __syncthreads();  // the partial sums are read before the tile overwrites them
+  f16 *otile = reinterpret_cast<f16 *>(smem + (OSEP ? RED_BYTES : 0));
+#pragma unroll
+  for (int o = 0; o < MTO; ++o)
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        otile[(16 * (ks + NKS * o) + 4 * kq + e) * OSTR + (wc * CT + ct) * kTileN + c] = yv[o][ct][e];
+  __syncthreads();
+  const int col0 = blockIdx.x * WC;
+  constexpr int RUNS = WC / 8;  // 16-byte runs per row
+  static_assert(64 * RUNS % (64 * kTileNWave) == 0, "whole store rounds");
+#pragma unroll
+  for (int q = 0; q < 64 * RUNS / (64 * kTileNWave); ++q) {
+    const int idx = q * 64 * kTileNWave + tid;
+    const int row = idx / RUNS, run = idx % RUNS;
+    if (row < mrows && col0 + run * 8 < p.N)
+      *reinterpret_cast<u32x4 *>(p.out + (size_t)(m0 + row) * p.N + col0 + run * 8) =
+          *reinterpret_cast<const u32x4 *>(otile + row * OSTR + run * 8);
   }
 }
 
