@@ -739,7 +739,9 @@ def cu_probes():
     held in L2 (216 workgroups, the tile kernel's grid at M=128, 160 steps
     of 32 KiB each), both per compute unit (256 CUs for the first: 1024
     workgroups spread over all of them; 216 for the second, one workgroup
-    each).  Medians of 5 timed launches with HIP events."""
+    each).  And the issue probe: how far independent VALU work overlaps the
+    matrix cores (``w4a16_probe_mfma_valu``).  Medians of 5 timed launches
+    with HIP events."""
     import torch
     import decode_w4a16_repack_amd as w4
     sink = torch.zeros(1024 * 512, dtype=torch.int32, device="cuda")
@@ -762,13 +764,26 @@ def cu_probes():
     read_bytes = 1024 * 512 * 2000 * 256
     t_copy = timed(lambda: w4.probe_lds_copy(rows, 216, 160, sink))
     copy_bytes = 216 * 161 * 32 * 1024
+    # issue probe: ns per round of 8 MFMAs + X fp32 FMAs per wavefront, one
+    # workgroup per compute unit, 1 or 2 wavefronts per SIMD
+    fsink = torch.zeros(256 * 512, dtype=torch.float32, device="cuda")
+    iters = 20000
+    issue = {}
+    for waves in (1, 2):
+        issue[f"{waves}_wave_per_simd"] = {
+            str(x): timed(lambda x=x: w4.probe_mfma_valu(x, waves, 256, iters, fsink)) / iters * 1e9
+            for x in (0, 8, 16, 32, 48, 64)}
     return {"lds_read_GBps_per_cu": read_bytes / t_read / 1e9 / 256,
             "lds_read_seconds": t_read,
             "l2_to_lds_copy_GBps_per_cu": copy_bytes / t_copy / 1e9 / 216,
             "l2_to_lds_copy_seconds": t_copy,
+            "mfma_valu_ns_per_round": issue,
             "what": "LDS read: 1024 workgroups x 512 threads, 2000 x 16 KiB per wavefront; "
                     "L2 -> LDS copy: 216 workgroups, 161 x 32 KiB each of a 640 KiB fp16 "
-                    "matrix, two steps in flight, one barrier per step"}
+                    "matrix, two steps in flight, one barrier per step; issue: 256 workgroups "
+                    "of 256 or 512 threads, 20000 rounds of 8 independent-accumulator "
+                    "v_mfma_f32_16x16x32_f16 and X (key) independent fp32 FMAs per wavefront, "
+                    "ns per round"}
 
 
 def tile_read_probe(steps=480, warmup=2000):
@@ -1145,6 +1160,9 @@ def main():
         f"{trp['even_256']['us_per_call']:.2f} us")
     log(f"[bench] compute-unit probes: LDS read {cu['lds_read_GBps_per_cu']:.0f} GB/s per CU, "
         f"L2 -> LDS copy {cu['l2_to_lds_copy_GBps_per_cu']:.0f} GB/s per CU")
+    for k, v in cu["mfma_valu_ns_per_round"].items():
+        log(f"[bench] issue probe, {k.replace('_', ' ')}: ns per round of 8 MFMAs + X FMAs: "
+            + " ".join(f"X={x}:{t:.1f}" for x, t in v.items()))
     cpu = None if args.no_cpu else cpu_baseline(gpu_out)
     if cpu:
         log(f"[bench] cpu oracle: {cpu['value']:.3f} GB/s on {cpu['cores']} threads"

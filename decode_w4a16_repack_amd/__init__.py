@@ -25,7 +25,8 @@ from ._lib import W4A16Error
 __all__ = [
     "PackedWeight", "repack", "gemm", "gemm_gate_up", "packed_bytes",
     "workspace_bytes", "layout_version", "add_bias", "relu", "rmsnorm",
-    "probe_read", "probe_copy", "probe_lds_read", "probe_lds_copy", "probe_read_tiles", "Workspace", "plan", "Plan", "W4A16Error",
+    "probe_read", "probe_copy", "probe_lds_read", "probe_lds_copy", "probe_read_tiles",
+    "probe_mfma_valu", "Workspace", "plan", "Plan", "W4A16Error",
     "mlp", "mlp_workspace_bytes", "gemm_noalloc",
 ]
 
@@ -463,6 +464,21 @@ def probe_lds_copy(buf: torch.Tensor, workgroups: int, steps: int, sink: torch.T
     _lib.check(_lib.lib().w4a16_probe_lds_copy(_ptr(buf), buf.numel() * buf.element_size(),
                                                int(workgroups), int(steps), _ptr(sink), _stream()),
                "w4a16_probe_lds_copy")
+
+
+def probe_mfma_valu(valu_per_8_mfma: int, waves_per_simd: int, workgroups: int, iters: int,
+                    sink: torch.Tensor) -> None:
+    """w4a16_probe_mfma_valu: every wavefront runs iters rounds of 8 MFMAs and
+    valu_per_8_mfma independent fp32 FMAs; workgroups of 256 * waves_per_simd
+    threads; sink (device, >= workgroups * threads fp32) gets one value per
+    thread."""
+    _need_gpu(sink, "sink")
+    if sink.numel() * sink.element_size() < workgroups * 256 * waves_per_simd * 4:
+        raise ValueError("sink needs workgroups * 256 * waves_per_simd * 4 bytes")
+    _lib.check(_lib.lib().w4a16_probe_mfma_valu(int(valu_per_8_mfma), int(waves_per_simd),
+                                                int(workgroups), int(iters), _ptr(sink),
+                                                sink.numel() * sink.element_size(), _stream()),
+               "w4a16_probe_mfma_valu")
 
 
 def probe_read_tiles(w: PackedWeight, mode: int, workgroups: int, sink: torch.Tensor) -> None:

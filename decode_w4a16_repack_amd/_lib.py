@@ -47,6 +47,7 @@ EXPORTS = [
     "w4a16_gemm_gate_up", "w4a16_status_string", "w4a16_layout_version",
     "w4a16_add_bias", "w4a16_relu", "w4a16_rmsnorm", "w4a16_probe_read",
     "w4a16_probe_copy", "w4a16_probe_lds_read", "w4a16_probe_lds_copy", "w4a16_probe_read_tiles",
+    "w4a16_probe_mfma_valu",
     "w4a16_plan", "w4a16_gemm_split", "w4a16_gemm_gate_up_split",
     "w4a16_gemm_skip_rmsnorm", "w4a16_gemm_gate_up_skip_rmsnorm",
     "w4a16_mlp_workspace_bytes", "w4a16_mlp", "w4a16_gemm_noalloc",
@@ -97,6 +98,7 @@ def lib() -> ctypes.CDLL:
         "w4a16_probe_lds_read": (I, [I, I, P, P]),
         "w4a16_probe_lds_copy": (I, [P, Z, I, I, P, P]),
         "w4a16_probe_read_tiles": (I, [P, I, I, I, I, P, Z, P]),
+        "w4a16_probe_mfma_valu": (I, [I, I, I, I, P, Z, P]),
         "w4a16_plan": (I, [I, I, I, I, I, I, I, ctypes.POINTER(PlanInfo)]),
         "w4a16_gemm_split": (I, [P, I, I, I, I, I, I, P, I, P, P, F, P, P, Z, I, P]),
         "w4a16_gemm_gate_up_split": (I, [P, I, I, I, I, I, I, P, P, P, F, P, P, Z, I, P]),

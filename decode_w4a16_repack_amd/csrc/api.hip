@@ -547,6 +547,21 @@ int w4a16_probe_lds_read(int workgroups, int iters, void *sink, w4a16_stream str
                                         static_cast<hipStream_t>(stream)));
 }
 
+int w4a16_probe_mfma_valu(int valu_per_8_mfma, int waves_per_simd, int workgroups, int iters,
+                          void *sink, size_t sink_bytes, w4a16_stream stream) {
+  if (sink == nullptr) return W4A16_ERR_NULL;
+  const int v = valu_per_8_mfma;
+  if ((v != 0 && v != 8 && v != 16 && v != 32 && v != 48 && v != 64) ||
+      (waves_per_simd != 1 && waves_per_simd != 2) || workgroups < 1 || workgroups > 65535 ||
+      iters < 1 || iters > (1 << 20))
+    return W4A16_ERR_SHAPE;
+  const int threads = 256 * waves_per_simd;
+  if ((size_t)workgroups * threads * 4 > sink_bytes) return W4A16_ERR_SHAPE;
+  if (!aligned16(sink)) return W4A16_ERR_ALIGN;
+  return launched(launch_probe_mfma_valu(v, threads, workgroups, iters, static_cast<float *>(sink),
+                                         static_cast<hipStream_t>(stream)));
+}
+
 int w4a16_probe_lds_copy(const void *buf, size_t bytes, int workgroups, int steps, void *sink,
                          w4a16_stream stream) {
   if (buf == nullptr || sink == nullptr) return W4A16_ERR_NULL;

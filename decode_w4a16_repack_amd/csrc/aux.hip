@@ -129,6 +129,35 @@ __global__ void __launch_bounds__(512) probe_lds_read_kernel(int iters, uint32_t
   sink[(size_t)blockIdx.x * 512 + t] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
 }
 
+// Issue probe: how far independent VALU work overlaps the matrix cores.
+// Every wavefront runs iters rounds of 8 v_mfma_f32_16x16x32_f16 (four
+// accumulators, two MFMAs each) and X independent fp32 FMAs (sixteen
+// registers; X / 8 after each MFMA), then folds its registers into one value
+// per thread in sink.  The time per round against X, at one and at two
+// wavefronts per SIMD, gives the MFMA time alone and what each VALU
+// instruction adds to it.
+template <int X>
+__global__ void __launch_bounds__(512) probe_mfma_valu_kernel(int iters, float s, float *sink) {
+  f32x4 acc[4] = {};
+  const f16x8 a = {(f16)((float)threadIdx.x * 0.001f)};
+  const f16x8 b = {(f16)1.0f};
+  float v[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) v[i] = (float)(threadIdx.x + i);
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      acc[m & 3] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[m & 3], 0, 0, 0);
+#pragma unroll
+      for (int x = 0; x < X / 8; ++x) v[(m * 7 + x) & 15] = __builtin_fmaf(v[(m * 7 + x) & 15], s, 1.0f);
+    }
+  }
+  float r = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) r += v[i];
+  sink[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = r + acc[0][0] + acc[1][1] + acc[2][2] + acc[3][3];
+}
+
 // Global-to-LDS copy rate of activation-like rows held in L2: buf is a
 // 64-row fp16 matrix of K = bytes / 128 columns.  Per step, wavefront
 // (wc, ks) of a 512-thread workgroup copies a quarter (four 1 KiB copies of
@@ -289,6 +318,21 @@ hipError_t launch_probe_lds_copy(const void *buf, size_t bytes, int workgroups, 
                                  uint32_t *sink, hipStream_t stream) {
   hipLaunchKernelGGL(probe_lds_copy_kernel, dim3(workgroups), dim3(512), 0, stream,
                      static_cast<const uint8_t *>(buf), (int)(bytes / 16384), steps, sink);
+  return hipGetLastError();
+}
+
+hipError_t launch_probe_mfma_valu(int valu, int threads, int workgroups, int iters, float *sink,
+                                  hipStream_t stream) {
+  const float s = 0.999f;
+  switch (valu) {
+    case 0: hipLaunchKernelGGL(probe_mfma_valu_kernel<0>, dim3(workgroups), dim3(threads), 0, stream, iters, s, sink); break;
+    case 8: hipLaunchKernelGGL(probe_mfma_valu_kernel<8>, dim3(workgroups), dim3(threads), 0, stream, iters, s, sink); break;
+    case 16: hipLaunchKernelGGL(probe_mfma_valu_kernel<16>, dim3(workgroups), dim3(threads), 0, stream, iters, s, sink); break;
+    case 32: hipLaunchKernelGGL(probe_mfma_valu_kernel<32>, dim3(workgroups), dim3(threads), 0, stream, iters, s, sink); break;
+    case 48: hipLaunchKernelGGL(probe_mfma_valu_kernel<48>, dim3(workgroups), dim3(threads), 0, stream, iters, s, sink); break;
+    case 64: hipLaunchKernelGGL(probe_mfma_valu_kernel<64>, dim3(workgroups), dim3(threads), 0, stream, iters, s, sink); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

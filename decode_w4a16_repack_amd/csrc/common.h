@@ -182,6 +182,8 @@ hipError_t launch_probe_read(const void *buf, size_t bytes, uint32_t *sink,
 hipError_t launch_probe_copy(const void *src, void *dst, size_t bytes,
                              hipStream_t stream);
 hipError_t launch_probe_lds_read(int workgroups, int iters, uint32_t *sink, hipStream_t stream);
+hipError_t launch_probe_mfma_valu(int valu, int threads, int workgroups, int iters, float *sink,
+                                  hipStream_t stream);
 hipError_t launch_probe_lds_copy(const void *buf, size_t bytes, int workgroups, int steps,
                                  uint32_t *sink, hipStream_t stream);
 unsigned probe_tiles_grid(int N, int mode, int workgroups);

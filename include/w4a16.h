@@ -348,6 +348,21 @@ int w4a16_probe_lds_read(int workgroups, int iters, void *sink, w4a16_stream str
 int w4a16_probe_lds_copy(const void *buf, size_t bytes, int workgroups, int steps, void *sink,
                          w4a16_stream stream);
 
+/*
+ * Issue probe: how far independent VALU work overlaps the matrix cores, the
+ * limit of the MFMA-tile kernel, which unpacks every weight word and scales
+ * every group's partial sums with VALU instructions next to its MFMAs.
+ * `workgroups` workgroups of 256 * waves_per_simd threads (1 or 2 wavefronts
+ * per SIMD when each compute unit holds one workgroup); every wavefront runs
+ * iters rounds of 8 independent-accumulator v_mfma_f32_16x16x32_f16 and
+ * valu_per_8_mfma (0, 8, 16, 32, 48 or 64) independent fp32 FMAs, and writes
+ * one fp32 value per thread to sink (at least workgroups * threads * 4 bytes,
+ * sink_bytes).  W4A16_ERR_SHAPE for another FMA count or wavefront count,
+ * workgroups outside 1..65535, iters outside 1..2^20, or a sink too small.
+ */
+int w4a16_probe_mfma_valu(int valu_per_8_mfma, int waves_per_simd, int workgroups, int iters,
+                          void *sink, size_t sink_bytes, w4a16_stream stream);
+
 
 /*
  * Probe of how the streaming kernel's tiles are spread over the chip: plain

@@ -134,6 +134,14 @@ def test_aux_validation(L):
     assert L.w4a16_probe_lds_copy(FAKE, 16384, 70000, 10, FAKE, None) == _lib.ERR_SHAPE
     assert L.w4a16_probe_lds_copy(FAKE, 16384, 4, 0, FAKE, None) == _lib.ERR_SHAPE
     assert L.w4a16_probe_lds_copy(FAKE + 4, 16384, 4, 10, FAKE, None) == _lib.ERR_ALIGN
+    sb = 256 * 512 * 4
+    assert L.w4a16_probe_mfma_valu(16, 2, 256, 100, None, sb, None) == _lib.ERR_NULL
+    assert L.w4a16_probe_mfma_valu(12, 2, 256, 100, FAKE, sb, None) == _lib.ERR_SHAPE
+    assert L.w4a16_probe_mfma_valu(16, 3, 256, 100, FAKE, sb, None) == _lib.ERR_SHAPE
+    assert L.w4a16_probe_mfma_valu(16, 2, 0, 100, FAKE, sb, None) == _lib.ERR_SHAPE
+    assert L.w4a16_probe_mfma_valu(16, 2, 256, 0, FAKE, sb, None) == _lib.ERR_SHAPE
+    assert L.w4a16_probe_mfma_valu(16, 2, 256, 100, FAKE, sb - 4, None) == _lib.ERR_SHAPE
+    assert L.w4a16_probe_mfma_valu(16, 2, 256, 100, FAKE + 4, sb, None) == _lib.ERR_ALIGN
     big = 1 << 30
     assert L.w4a16_probe_read_tiles(None, 5120, 13824, 0, 0, FAKE, big, None) == _lib.ERR_NULL
     assert L.w4a16_probe_read_tiles(FAKE, 5000, 13824, 0, 0, FAKE, big, None) == _lib.ERR_SHAPE

@@ -484,6 +484,17 @@ def test_probes():
     rows = torch.randn(64, 1024, device="cuda").half()
     w4.probe_lds_copy(rows, 8, 5, sink2)
     torch.cuda.synchronize()
+    # the issue probe: every FMA count and wavefront count runs, and the
+    # folded registers are finite and the same from run to run
+    fs = torch.zeros(8 * 512, dtype=torch.float32, device="cuda")
+    for waves in (1, 2):
+        for x in (0, 8, 16, 32, 48, 64):
+            w4.probe_mfma_valu(x, waves, 8, 3, fs)
+            first = fs.clone()
+            w4.probe_mfma_valu(x, waves, 8, 3, fs)
+            torch.cuda.synchronize()
+            assert torch.isfinite(first[: 8 * 256 * waves]).all()
+            assert torch.equal(first, fs)
 
 
 
