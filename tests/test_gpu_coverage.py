@@ -213,3 +213,20 @@ def test_tile_ragged_last_block_sampled(M, N):
     got = run(p)
     cols = np.unique(np.concatenate([np.arange(N - 128, N), sample_cols(N, 128, seed=M)]))
     check_close(got[:, cols], ref(p, cols=cols), f"tile ragged M={M} N={N}")
+
+
+@pytest.mark.parametrize("M,g,epi,rms", [(128, 128, "bias_relu", False), (100, 32, "bias", False),
+                                         (128, 64, "none", True), (70, 16, "bias", True)])
+def test_tile_epilogue_wide_ragged_sampled(M, g, epi, rms):
+    """The tile kernel's epilogue with two 64-row blocks (two column tiles per
+    wavefront), a ragged last column block and a ragged last row block: bias
+    and ReLU, the staged RMSNorm row scales, every group size's path; the
+    last block's columns and a sample of the rest against the oracle."""
+    N = 13808
+    pl = w4.plan(M, 1024, N, g)
+    assert pl.kernel == "tile" and pl.grid[2] == 2 and (N // 16) % pl.col_tiles != 0
+    p = synth.make_problem(M, 1024, N, g, seed=M + g, gamma=rms, bias=epi != "none")
+    got = run(p, epilogue=epi, rms=rms)
+    cols = np.unique(np.concatenate([np.arange(N - 160, N), sample_cols(N, 128, seed=M + g)]))
+    check_close(got[:, cols], ref(p, epilogue=epi, rms=rms, cols=cols),
+                f"tile epilogue M={M} g={g} {epi} rms={rms}")
