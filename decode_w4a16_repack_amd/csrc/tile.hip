@@ -17,22 +17,24 @@
 //    weight fragment feeds 4 MFMAs and each activation fragment CT, and the
 //    activation tile of a step is shared by the four column quarters;
 //  * the slice's 64 x 128 activation tile goes straight from global memory
-//    (L2) into an LDS stage with direct global-to-LDS loads (whole row
-//    segments; all four column quarters read it), its 16-byte chunks
-//    XOR-swizzled by row so an MFMA operand read is conflict-free; ST
-//    stages, so the copies of step j + ST - 1 are issued while step j
-//    computes; each wavefront's scales and zero-points go the same way into
-//    its own LDS blocks, several steps per copy (every copy costs issue time
-//    in the memory pipeline, whatever its size);
+//    (L2) into an LDS stage with buffer loads to LDS (whole row segments;
+//    all four column quarters read it), its 16-byte chunks XOR-swizzled by
+//    row so an MFMA operand read is conflict-free; ST stages, so the copies
+//    of step j + ST - 1 are issued while step j computes; each wavefront's
+//    scales and zero-points go the same way into its own LDS blocks, several
+//    steps per copy (every copy costs issue time in the memory pipeline,
+//    whatever its size);
 //  * the weight tiles (the HBM stream: one 16-byte load per lane per 1 KiB
 //    tile) go straight into registers D = 3 steps ahead (a ring of four,
 //    the step loop unrolled by four);
+//  * a step's copies and weight loads go out one per 32-k block of its
+//    contraction, not as one burst after the barrier;
 //  * the number of copies and loads per step is fixed (tail steps re-read
 //    the last tile), which keeps the one wait per step exact;
 //  * one barrier per step; after the last step, the slices' partial sums
 //    meet in LDS and wavefront (wc, ks) finishes row tiles ks, ks + 2 of its
-//    column quarter in slice order: the RMSNorm row scale (rows staged by
-//    stage.hip), epilogue, one fp16 write.
+//    column quarter in slice order (the RMSNorm row scale of rows staged by
+//    stage.hip, the epilogue), through an LDS tile to 16-byte fp16 stores.
 #include <type_traits>
 
 #include "device.h"
