@@ -35,6 +35,22 @@ def test_exports_every_header_function(L):
     assert set(names) == set(_lib.EXPORTS)
 
 
+def test_header_is_plain_c_and_cxx(tmp_path):
+    """The header compiles as strict C99 and as C++17 with no warning: a C
+    caller needs nothing from C++ or from HIP's headers."""
+    import shutil
+    import subprocess
+    src = tmp_path / "use.c"
+    src.write_text('#include "w4a16.h"\nint main(void) { return w4a16_layout_version() > 0 ? 0 : 1; }\n')
+    inc = os.path.join(ROOT, "include")
+    for cc, std, lang in (("gcc", "-std=c99", "c"), ("g++", "-std=c++17", "c++")):
+        if shutil.which(cc) is None:
+            pytest.skip(f"{cc} not found")
+        r = subprocess.run([cc, std, "-Wall", "-Wextra", "-pedantic", "-Werror", "-fsyntax-only",
+                            "-x", lang, "-I", inc, str(src)], capture_output=True, text=True)
+        assert r.returncode == 0, (cc, r.stderr)
+
+
 def test_header_enums_match_binding():
     text = open(HEADER).read()
     for name, val in [("W4A16_ERR_NULL", -1), ("W4A16_ERR_SHAPE", -2),
